@@ -1,0 +1,145 @@
+/*
+ * mxfp8_partial.h -- C ABI of libmxfp8partial.so: MXFP8 partial amax, amax MAX-combine,
+ * E8M0 scale update and partial E4M3 cast for a contiguous fragment of a flattened 2-D
+ * master weight, on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the distributed master-weight writeback of "Support row-only MXFP8
+ * distributed master-weight casts" (TransformerEngine PR 3488): each rank holds a contiguous
+ * fragment [start, start + len) of the row-major flattening of a rows x cols weight
+ * (section Changes; the kernel documentation in the review threads describes the input as a
+ * contiguous piece of the flattened tensor), computes per-block amax for the directions that
+ * exist, the amax of all fragments is MAX-combined in a single packed reduction, scales are
+ * updated for the present directions, and the fragment is cast in place to E4M3 row-wise
+ * data and, only when that output is present, column-wise data (flow diagram of the Greptile
+ * summary).  The block shape (1x32 row-wise, 32x1 column-wise) and
+ * the numeric rules below follow the OCP Microscaling (MX) v1.0 and OFP8 specifications.
+ *
+ * Conventions shared by every entry point
+ *  - All buffer pointers are DEVICE pointers unless stated otherwise.  The caller owns every
+ *    buffer; the library allocates nothing, keeps no pointer after a call returns, and never
+ *    synchronizes: work is enqueued on `hip_stream` (a hipStream_t; NULL = the null stream).
+ *  - An absent direction or output is an empty handle: ptr == NULL.  There is no shape
+ *    sentinel (the pages drop the empty-shape convention in favour of empty handles).
+ *  - Element (r, c) of the weight is flat index i = r * cols + c.  Fragment element k is
+ *    input[k] = x[start + k].  Row-wise block (r, j) covers columns [32 j, min(32 j + 32, cols))
+ *    of row r; column-wise block (b, c) covers rows [32 b, min(32 b + 32, rows)) of column c.
+ *  - amax arrays hold the input dtype (FP32 or BF16 bit patterns; the review threads show a
+ *    check that the amax dtype equals the input dtype): amax_row is [rows][ld >= ceil(cols/32)], amax_col is
+ *    [ceil(rows/32)][ld >= cols].  Scale arrays are uint8 E8M0 with the same shapes.
+ *    Entries beyond the logical width (padding) are never read or written.
+ *  - data_row / data_col are uint8 E4M3 and FRAGMENT-RELATIVE: byte k belongs to element
+ *    start + k, in the weight's row-major order for both directions (column-wise data is not
+ *    transposed).  In-place writes into a full-size MXFP8 tensor pass base + start; a
+ *    fragment-sized output buffer passes its own pointer.
+ *  - Errors: every check runs on the host before anything is enqueued; a call returns a
+ *    status code and never aborts or throws.  mxfp8_last_error() gives a message for the
+ *    calling thread's last non-OK status.  A HIP launch failure returns MXFP8_ERR_HIP; pieces
+ *    enqueued before the failing one stay enqueued.
+ *  - len == 0 (an empty master shard on a participating rank) is a valid no-op; input and
+ *    outputs may then be NULL.
+ *  - Precondition, not checked (device data): inputs are finite, and pre-rounding (below)
+ *    does not overflow BF16; amax entries are non-negative; scale bytes are at most 254.
+ */
+#ifndef MXFP8_PARTIAL_H
+#define MXFP8_PARTIAL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP8_OK = 0,
+  MXFP8_ERR_ARG = 1,     /* n < 0, pieces == NULL with n > 0, rows/cols < 1, k < 1, NULL input */
+  MXFP8_ERR_RANGE = 2,   /* [start, start + len) not inside [0, rows * cols]                     */
+  MXFP8_ERR_DTYPE = 3,   /* unknown dtype, or pre-rounding requested for a BF16 input            */
+  MXFP8_ERR_LAYOUT = 4,  /* leading dimension below the logical width, misaligned element
+                            pointer, or an input overlapping an output                            */
+  MXFP8_ERR_MISSING = 5, /* a required buffer is absent (row-wise outputs are always required;
+                            column-wise scales are required when column-wise work is requested) */
+  MXFP8_ERR_HIP = 6      /* a kernel launch failed                                                */
+} mxfp8_status;
+
+typedef enum { MXFP8_FP32 = 0, MXFP8_BF16 = 1 } mxfp8_dtype;
+
+/* A device buffer and its leading dimension in elements; ptr == NULL means absent. */
+typedef struct {
+  void* ptr;
+  int64_t ld;
+} mxfp8_buf;
+
+/* One fragment of one weight.  Which fields an entry point reads is stated at that entry
+ * point; the others are ignored. */
+typedef struct {
+  int64_t rows, cols;       /* logical shape of the whole 2-D weight                          */
+  int64_t start, len;       /* fragment [start, start + len) of its row-major flattening      */
+  int32_t in_dtype;         /* MXFP8_FP32 or MXFP8_BF16                                       */
+  int32_t preround_bf16;    /* 1: round FP32 master values to BF16 (nearest, ties to even)
+                               before amax and cast (the rounding through the model dtype
+                               of section Changes); FP32 input only                           */
+  const void* input;        /* len elements of in_dtype, aligned to the element size          */
+  mxfp8_buf amax_row;       /* in_dtype entries, [rows][ld]                                   */
+  mxfp8_buf amax_col;       /* in_dtype entries, [ceil(rows/32)][ld]; NULL = row-only         */
+  mxfp8_buf scale_row;      /* uint8 E8M0, [rows][ld]                                         */
+  mxfp8_buf scale_col;      /* uint8 E8M0, [ceil(rows/32)][ld]                                */
+  void* data_row;           /* uint8 E4M3, len bytes, fragment-relative                       */
+  void* data_col;           /* uint8 E4M3, len bytes, fragment-relative; NULL = row-only      */
+} mxfp8_piece;
+
+/* Step 1 -- partial amax (first step of the flow diagram; the kernel documentation in the
+ * review threads marks both amax outputs as in/out).
+ * For each of the n pieces (a host array) and every block the fragment touches in a present
+ * direction: amax[block] = max(amax[block], max |w| over the fragment's elements in the
+ * block), w being the input value (pre-rounded to BF16 if requested).  Blocks the fragment
+ * does not touch keep their entry; blocks cut by a fragment boundary are MAX-merged, so
+ * pieces of one weight may share amax buffers within a call or across calls, and zero-filled
+ * buffers accumulate the amax of all pieces.  The column-wise direction is computed iff
+ * amax_col.ptr != NULL.  Reads: rows, cols, start, len, in_dtype, preround_bf16, input,
+ * amax_row (required), amax_col. */
+int mxfp8_partial_amax(const mxfp8_piece* pieces, int n, void* hip_stream);
+
+/* Step 2 -- MAX-combine (section Changes keeps a single MAX all-reduce over the packed amax;
+ * on one GPU the partials of several fragments are combined on the device instead).
+ * dst[e] = max over j < k of srcs[j][e], for e < count entries of amax_dtype.  srcs is a HOST
+ * array of k device pointers; dst may equal srcs[0] (in place) but must not partly overlap
+ * any source.  Pack the amax of every present direction of a batch into one buffer and call
+ * this once per batch. */
+int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
+                       int32_t amax_dtype, void* hip_stream);
+
+/* Step 3 -- E8M0 scales for the present directions (flow diagram; section Changes skips the
+ * update of absent column-wise scales).  For every block the piece's
+ * fragment touches: scale = clamp(floor(log2 amax) - 8 + 127, 0, 254), and 0 for amax == 0
+ * (OCP MX, emax of E4M3 = 8).  Other scale bytes are left as they are.  The column-wise
+ * direction is computed iff amax_col.ptr != NULL, and then scale_col is required.  Reads:
+ * rows, cols, start, len, in_dtype (the amax dtype), amax_row, amax_col, scale_row
+ * (required), scale_col.  Pieces whose fragments share a cut block write the same byte. */
+int mxfp8_compute_scales(const mxfp8_piece* pieces, int n, void* hip_stream);
+
+/* Step 4 -- partial cast, in place (last steps of the flow diagram: row-wise output always;
+ * column-wise output only when present, in which case its scales are required, otherwise its
+ * reads and writes are skipped).
+ * data_row[k] = E4M3(w * 2^(127 - s)) with s the row-wise block's scale byte, rounded to
+ * nearest even and saturated to +-448 (the sign of zero is kept); data_col[k] likewise with
+ * the column-wise block's scale, only when data_col != NULL, which then requires scale_col.
+ * When data_col is NULL, scale_col is ignored even if set.  Row-wise outputs (data_row,
+ * scale_row) are always required.  Reads: rows, cols, start, len, in_dtype, preround_bf16,
+ * input, scale_row, scale_col, data_row, data_col. */
+int mxfp8_partial_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
+
+/* Message for the calling thread's last non-OK status (static storage, thread-local). */
+const char* mxfp8_last_error(void);
+
+/* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast:
+ * 1 = the vectorized path (16-byte loads of 32-aligned row segments; needs cols % 32 == 0,
+ * input - start aligned to 16 bytes, and for the cast fragment-relative outputs aligned to
+ * the chunk's byte count), 0 = the element-wise path for any other layout, negative = the
+ * piece fails validation (the status code, negated).  Host-only; launches nothing. */
+int mxfp8_query_path(const mxfp8_piece* piece, int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_PARTIAL_H */

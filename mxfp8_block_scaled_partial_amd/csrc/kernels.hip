@@ -1,0 +1,784 @@
+// HIP kernels for gfx950 (CDNA4): MXFP8 partial amax, amax MAX-combine, E8M0 scales and the
+// partial E4M3 cast of a contiguous fragment of a flattened 2-D weight.
+//
+// What is computed follows "Support row-only MXFP8 distributed master-weight casts"
+// (TransformerEngine PR 3488, sections Changes and the flow diagram of the Greptile summary)
+// with the OCP MX / OFP8 rules for blocks, scales and E4M3; the public contract is in
+// include/mxfp8_partial.h.
+//
+// Design (MI355X first; no matrix cores, since nothing here is a contraction):
+//  * A wave owns a tile of one 32-row band (the height of a column-wise block) and 64 * E
+//    columns, E = elements per 16-byte chunk (8 for BF16, 4 for FP32).  Each lane streams one
+//    16-byte chunk per row down the band, so every load instruction of the wave covers 1 KiB
+//    of contiguous HBM.  Column-wise maxima stay in the lane's registers for the whole band;
+//    row-wise maxima are reduced over the 32/E lanes that share a 32-value block with DPP
+//    (quad_perm, row_half_mirror), no LDS round trip.  One read of the input feeds both
+//    directions.
+//  * amax is handled as unsigned integers on |x|'s bit pattern (exact, independent of the
+//    floating-point mode); BF16 pairs use v_pk_max_u16.
+//  * The cast scales with v_ldexp_f32 (exact, denormals preserved), saturates with v_med3_f32
+//    and converts pairs with v_cvt_pk_fp8_f32 (OCP E4M3, round to nearest even on gfx950).
+//  * The column-wise direction and BF16 pre-rounding are compile-time template booleans, so
+//    a row-only call carries no column-wise code (the runtime-guard version measured on the
+//    pages cost amax 21-35%).
+//  * Tiles wholly inside the fragment run branch-free; tiles the fragment boundary cuts take
+//    an element-masked path.  Amax entries of blocks wholly inside a piece are read-max-written
+//    by their single owner; blocks a boundary cuts use an atomic max, so pieces sharing one
+//    amax buffer merge correctly in any order.
+//  * Workgroup ids are remapped so consecutive tiles (one band's amax entries) land on the
+//    same XCD's L2.
+//  * Layouts the vector path cannot take (cols % 32 != 0, input - start not 16-byte aligned,
+//    unaligned fragment-relative outputs) run an element-wise kernel: one lane per column,
+//    same band tiling, same results.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "mxfp8_internal.h"
+
+namespace mxfp8 {
+namespace {
+
+constexpr int kBlockLen = 32;     // MX block length
+constexpr int kWaveSize = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWaveSize * kWavesPerGroup;
+constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+struct TileArgs {
+  int64_t rows, cols, start, end;
+  const void* input;
+  void* amax_row;
+  int64_t ld_ar;
+  void* amax_col;
+  int64_t ld_ac;
+  const uint8_t* scale_row;
+  int64_t ld_sr;
+  const uint8_t* scale_col;
+  int64_t ld_sc;
+  uint8_t* data_row;
+  uint8_t* data_col;
+  int64_t band0;   // first 32-row band the fragment touches
+  int64_t ntc;     // tiles per band
+  int64_t ntiles;  // bands * ntc
+  int32_t col_vec; // amax_col rows are 16-byte aligned: column entries move as 16-byte vectors
+};
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ small device helpers
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, kCtrl, 0xF, 0xF, false);
+}
+
+// Max over aligned groups of kLanes lanes (4 or 8); every lane of the group gets the result.
+template <int kLanes>
+__device__ __forceinline__ uint32_t group_max(uint32_t v) {
+  v = umax(v, dpp<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+  v = umax(v, dpp<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (kLanes >= 8) v = umax(v, dpp<0x141>(v));  // row_half_mirror: other quad
+  static_assert(kLanes == 4 || kLanes == 8, "group of 4 or 8 lanes");
+  return v;
+}
+
+// Max over each 32-lane half of the wave (one row-wise block per half in the element path).
+__device__ __forceinline__ uint32_t half_wave_max(uint32_t v) {
+  v = umax(v, dpp<0xB1>(v));
+  v = umax(v, dpp<0x4E>(v));
+  v = umax(v, dpp<0x141>(v));
+  v = umax(v, dpp<0x140>(v));   // row_mirror: the other 8 lanes of the 16-lane row
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 16));
+  return v;
+}
+
+// FP32 bit pattern rounded to the nearest BF16 value (ties to even), as an FP32 bit pattern.
+// Integer arithmetic: exact for normal and subnormal inputs alike.
+__device__ __forceinline__ uint32_t round_bf16_bits(uint32_t u) {
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+}
+
+// Dispatch round-robins consecutive workgroup ids over the XCDs; renumber them so that each
+// XCD works through one contiguous range of tiles.
+__device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t nwg) {
+  const int64_t per = nwg / kNumXcd, rem = nwg % kNumXcd;
+  const int64_t xcd = wg % kNumXcd, idx = wg / kNumXcd;
+  const int64_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return base + idx;
+}
+
+// ------------------------------------------------------------------ amax entries
+
+__device__ __forceinline__ void merge_plain(uint16_t* p, uint32_t v) {
+  const uint32_t old = *p;
+  *p = (uint16_t)umax(old, v);
+}
+__device__ __forceinline__ void merge_plain(uint32_t* p, uint32_t v) { *p = umax(*p, v); }
+
+__device__ __forceinline__ void merge_atomic(uint32_t* p, uint32_t v) { atomicMax(p, v); }
+
+// 16-bit atomic max through a compare-and-swap on the aligned 32-bit word holding the entry.
+// Amax values are non-negative, so unsigned order on the bits is float order.
+__device__ __forceinline__ void merge_atomic(uint16_t* p, uint32_t v) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  uint32_t* w = reinterpret_cast<uint32_t*>(a & ~uintptr_t(3));
+  const int sh = (a & 2) ? 16 : 0;
+  uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (((old >> sh) & 0xFFFFu) < v) {
+    const uint32_t nw = (old & ~(0xFFFFu << sh)) | (v << sh);
+    const uint32_t prev = atomicCAS(w, old, nw);
+    if (prev == old) break;
+    old = prev;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void merge_entry(void* base, int64_t idx, uint32_t v, bool full) {
+  T* p = static_cast<T*>(base) + idx;
+  if (full)
+    merge_plain(p, v);
+  else
+    merge_atomic(p, v);
+}
+
+// ------------------------------------------------------------------ per-element working values
+
+// |w| as the amax bit pattern, for one element given by its raw input bits.
+template <typename T, bool kPre>
+__device__ __forceinline__ uint32_t abs_bits(uint32_t raw) {
+  if constexpr (sizeof(T) == 2) {
+    return raw & 0x7FFFu;
+  } else {
+    return (kPre ? round_bf16_bits(raw) : raw) & 0x7FFFFFFFu;
+  }
+}
+
+template <typename T, bool kPre>
+__device__ __forceinline__ float work_value(uint32_t raw) {
+  if constexpr (sizeof(T) == 2) {
+    return __uint_as_float(raw << 16);
+  } else {
+    return __uint_as_float(kPre ? round_bf16_bits(raw) : raw);
+  }
+}
+
+// Two working values -> two E4M3 bytes in the low or high half of `old`.
+template <bool kHigh>
+__device__ __forceinline__ uint32_t cvt2(float a, float b, int exp_shift_a, int exp_shift_b,
+                                         uint32_t old) {
+  float ya = __builtin_amdgcn_fmed3f(__builtin_ldexpf(a, exp_shift_a), -448.0f, 448.0f);
+  float yb = __builtin_amdgcn_fmed3f(__builtin_ldexpf(b, exp_shift_b), -448.0f, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ya, yb, (int)old, kHigh);
+}
+
+__device__ __forceinline__ uint8_t cvt1(float a, int exp_shift) {
+  float y = __builtin_amdgcn_fmed3f(__builtin_ldexpf(a, exp_shift), -448.0f, 448.0f);
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+}
+
+__device__ __forceinline__ uint32_t load_raw(const void* input, int64_t k, int esize) {
+  return esize == 2 ? (uint32_t)static_cast<const uint16_t*>(input)[k]
+                    : static_cast<const uint32_t*>(input)[k];
+}
+
+// ------------------------------------------------------------------ chunk helpers (vector path)
+
+template <typename T>
+struct Chunk {
+  static constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
+};
+
+// Raw bits of element e of a chunk held as 4 dwords.
+template <typename T>
+__device__ __forceinline__ uint32_t chunk_elem(const uint32_t (&d)[4], int e) {
+  if constexpr (sizeof(T) == 2)
+    return (d[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+  else
+    return d[e];
+}
+
+// Fold a chunk into the lane's column-wise maxima and return the chunk's own max |w|.
+// BF16: col[j] packs columns 2j (low half) and 2j+1 (high half), the entries' memory order.
+template <typename T, bool kCol, bool kPre>
+__device__ __forceinline__ uint32_t chunk_absmax(const uint32_t (&d)[4], uint32_t (&col)[4]) {
+  uint32_t a[4];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = d[j] & 0x7FFF7FFFu;
+      if constexpr (kCol) col[j] = pk_max_u16(col[j], a[j]);
+    }
+    const uint32_t m = pk_max_u16(pk_max_u16(a[0], a[1]), pk_max_u16(a[2], a[3]));
+    return umax(m & 0xFFFFu, m >> 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      a[j] = (kPre ? round_bf16_bits(d[j]) : d[j]) & 0x7FFFFFFFu;
+      if constexpr (kCol) col[j] = umax(col[j], a[j]);
+    }
+    return umax(umax(a[0], a[1]), umax(a[2], a[3]));
+  }
+}
+
+// Column-wise amax of column e of the chunk from the packed maxima.
+template <typename T>
+__device__ __forceinline__ uint32_t col_entry(const uint32_t (&col)[4], int e) {
+  if constexpr (sizeof(T) == 2)
+    return (col[e >> 1] >> ((e & 1) * 16)) & 0xFFFFu;
+  else
+    return col[e];
+}
+
+__device__ __forceinline__ void load16(const void* p, uint32_t (&d)[4]) {
+  const uint4 v = *static_cast<const uint4*>(p);
+  d[0] = v.x;
+  d[1] = v.y;
+  d[2] = v.z;
+  d[3] = v.w;
+}
+
+// Chunk whose elements straddle a fragment boundary: load only the fragment's elements.
+template <typename T>
+__device__ __forceinline__ uint32_t load_masked(const TileArgs& p, int64_t g, uint32_t (&d)[4]) {
+  constexpr int E = Chunk<T>::E;
+  uint32_t mask = 0;
+  d[0] = d[1] = d[2] = d[3] = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int64_t i = g + e;
+    if (i >= p.start && i < p.end) {
+      const uint32_t raw = load_raw(p.input, i - p.start, (int)sizeof(T));
+      if constexpr (sizeof(T) == 2)
+        d[e >> 1] |= raw << ((e & 1) * 16);
+      else
+        d[e] = raw;
+      mask |= 1u << e;
+    }
+  }
+  return mask;
+}
+
+// ------------------------------------------------------------------ partial amax, vector path
+
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block
+  constexpr int WC = kWaveSize * E;     // columns per wave tile
+  constexpr int NK = kBlockLen / LB;    // row maxima each lane keeps
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + (threadIdx.x >> 6);
+  if (tile >= p.ntiles) return;
+  const int64_t band = p.band0 + tile / p.ntc;
+  const int64_t c0 = (tile % p.ntc) * WC;
+  const int64_t c = c0 + lane * E;
+  const int64_t r0 = band * kBlockLen;
+  const bool cvalid = c < p.cols;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int64_t tile_first = r0 * p.cols + c0;
+  const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
+  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+
+  uint32_t col[4] = {0, 0, 0, 0};
+  const T* src = static_cast<const T*>(p.input) + (r0 * p.cols + c - p.start);
+
+  if (interior) {
+    uint32_t keep[NK];
+#pragma unroll
+    for (int i = 0; i < kBlockLen; ++i) {
+      uint32_t d[4] = {0, 0, 0, 0};
+      if (cvalid) load16(src + i * p.cols, d);
+      uint32_t m = chunk_absmax<T, kCol, kPre>(d, col);
+      m = group_max<LB>(m);
+      if ((i % LB) == (lane % LB)) keep[i / LB] = m;
+    }
+    if (!cvalid) return;
+    // lane t of a block group writes rows t, t + LB, ... of the block's column of amax_row
+    T* ar = static_cast<T*>(p.amax_row) + (r0 + lane % LB) * p.ld_ar + (c >> 5);
+    uint32_t old[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) old[k] = ar[(int64_t)k * LB * p.ld_ar];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)umax(old[k], keep[k]);
+    if constexpr (kCol) {
+      T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
+      if (p.col_vec) {
+        uint32_t o[4];
+        load16(ac, o);
+        uint4 w;
+        if constexpr (sizeof(T) == 2) {
+          w = make_uint4(pk_max_u16(o[0], col[0]), pk_max_u16(o[1], col[1]),
+                         pk_max_u16(o[2], col[2]), pk_max_u16(o[3], col[3]));
+        } else {
+          w = make_uint4(umax(o[0], col[0]), umax(o[1], col[1]), umax(o[2], col[2]),
+                         umax(o[3], col[3]));
+        }
+        *reinterpret_cast<uint4*>(ac) = w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) merge_plain(ac + e, col_entry<T>(col, e));
+      }
+    }
+    return;
+  }
+
+  // Edge tile: the fragment boundary (or the last, short band) cuts it.
+  uint32_t touched = 0;  // bit e: column c + e has an element inside the fragment
+  for (int i = 0; i < nrows; ++i) {
+    const int64_t r = r0 + i;
+    const int64_t g = r * p.cols + c;
+    uint32_t d[4] = {0, 0, 0, 0};
+    if (cvalid) {
+      if (g >= p.start && g + E <= p.end) {
+        load16(src + i * p.cols, d);
+        touched = (1u << E) - 1;
+      } else if (g + E > p.start && g < p.end) {
+        touched |= load_masked<T>(p, g, d);
+      }
+    }
+    uint32_t m = chunk_absmax<T, kCol, kPre>(d, col);
+    m = group_max<LB>(m);
+    if (cvalid && (lane % LB) == 0) {
+      const int64_t gb = r * p.cols + (c & ~int64_t(kBlockLen - 1));
+      const int64_t ge = gb + kBlockLen;
+      if (gb < p.end && ge > p.start)
+        merge_entry<T>(p.amax_row, r * p.ld_ar + (c >> 5), m, gb >= p.start && ge <= p.end);
+    }
+  }
+  if constexpr (kCol) {
+    if (cvalid) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (!((touched >> e) & 1u)) continue;
+        const int64_t first = r0 * p.cols + c + e;
+        const int64_t last = (r0 + nrows - 1) * p.cols + c + e;
+        merge_entry<T>(p.amax_col, band * p.ld_ac + c + e, col_entry<T>(col, e),
+                       first >= p.start && last < p.end);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ partial cast, vector path
+
+// E4M3 bytes of one chunk with one exponent shift for all elements (row-wise) or one per
+// element (column-wise), packed little-endian into E/4 dwords.
+template <typename T, bool kPre>
+__device__ __forceinline__ void quantize_chunk(const uint32_t (&d)[4], const int* shift,
+                                               bool per_elem, uint32_t* out) {
+  constexpr int E = Chunk<T>::E;
+#pragma unroll
+  for (int q = 0; q < E / 4; ++q) {
+    float x[4];
+    int s[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[t] = work_value<T, kPre>(chunk_elem<T>(d, 4 * q + t));
+      s[t] = per_elem ? shift[4 * q + t] : shift[0];
+    }
+    uint32_t w = cvt2<false>(x[0], x[1], s[0], s[1], 0);
+    out[q] = cvt2<true>(x[2], x[3], s[2], s[3], w);
+  }
+}
+
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads) void cast_vec_kernel(TileArgs p) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int WC = kWaveSize * E;
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + (threadIdx.x >> 6);
+  if (tile >= p.ntiles) return;
+  const int64_t band = p.band0 + tile / p.ntc;
+  const int64_t c0 = (tile % p.ntc) * WC;
+  const int64_t c = c0 + lane * E;
+  const int64_t r0 = band * kBlockLen;
+  if (c >= p.cols) return;  // no cross-lane work in the cast
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int64_t tile_first = r0 * p.cols + c0;
+  const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
+  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+
+  int cshift[E];
+  if constexpr (kCol) {
+    const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+#pragma unroll
+    for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+  }
+  const T* src = static_cast<const T*>(p.input) + (r0 * p.cols + c - p.start);
+  const uint8_t* srow = p.scale_row + r0 * p.ld_sr + (c >> 5);
+  const int64_t o0 = r0 * p.cols + c - p.start;  // fragment-relative output offset, row 0
+
+  if (interior) {
+#pragma unroll 4
+    for (int i = 0; i < kBlockLen; ++i) {
+      uint32_t d[4];
+      load16(src + i * p.cols, d);
+      const int rshift = 127 - (int)srow[i * p.ld_sr];
+      const int64_t o = o0 + i * p.cols;
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d, &rshift, false, q);
+      if constexpr (E == 8)
+        *reinterpret_cast<uint2*>(p.data_row + o) = make_uint2(q[0], q[1]);
+      else
+        *reinterpret_cast<uint32_t*>(p.data_row + o) = q[0];
+      if constexpr (kCol) {
+        quantize_chunk<T, kPre>(d, cshift, true, q);
+        if constexpr (E == 8)
+          *reinterpret_cast<uint2*>(p.data_col + o) = make_uint2(q[0], q[1]);
+        else
+          *reinterpret_cast<uint32_t*>(p.data_col + o) = q[0];
+      }
+    }
+    return;
+  }
+
+  for (int i = 0; i < nrows; ++i) {
+    const int64_t g = (r0 + i) * p.cols + c;
+    if (g + E <= p.start || g >= p.end) continue;
+    uint32_t d[4];
+    const uint32_t mask = load_masked<T>(p, g, d);
+    const int rshift = 127 - (int)srow[i * p.ld_sr];
+    uint32_t qr[E / 4], qc[E / 4];
+    quantize_chunk<T, kPre>(d, &rshift, false, qr);
+    if constexpr (kCol) quantize_chunk<T, kPre>(d, cshift, true, qc);
+    const int64_t o = o0 + i * p.cols;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (!((mask >> e) & 1u)) continue;
+      p.data_row[o + e] = (uint8_t)(qr[e >> 2] >> ((e & 3) * 8));
+      if constexpr (kCol) p.data_col[o + e] = (uint8_t)(qc[e >> 2] >> ((e & 3) * 8));
+    }
+  }
+}
+
+// ------------------------------------------------------------------ element-wise path (any layout)
+
+constexpr int kElemTileCols = kWaveSize;  // one lane per column
+
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads) void amax_elem_kernel(TileArgs p) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t tile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  if (tile >= p.ntiles) return;
+  const int64_t band = p.band0 + tile / p.ntc;
+  const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
+  const int64_t r0 = band * kBlockLen;
+  const bool cvalid = c < p.cols;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  uint32_t cmax = 0;
+  bool ctouched = false, cfull = true;
+  const int half = lane & 32;
+  for (int i = 0; i < nrows; ++i) {
+    const int64_t r = r0 + i;
+    const int64_t g = r * p.cols + c;
+    const bool inside = cvalid && g >= p.start && g < p.end;
+    uint32_t a = 0;
+    if (inside) a = abs_bits<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
+    if constexpr (kCol) {
+      cmax = umax(cmax, a);
+      ctouched |= inside;
+      cfull &= inside || !cvalid;
+    }
+    const uint32_t m = half_wave_max(a);
+    const uint32_t in_h = (uint32_t)(__ballot(inside) >> half);
+    const uint32_t val_h = (uint32_t)(__ballot(cvalid) >> half);
+    if ((lane & 31) == 0 && in_h != 0)
+      merge_entry<T>(p.amax_row, r * p.ld_ar + (c >> 5), m, in_h == val_h);
+  }
+  if constexpr (kCol) {
+    if (cvalid && ctouched) merge_entry<T>(p.amax_col, band * p.ld_ac + c, cmax, cfull);
+  }
+}
+
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads) void cast_elem_kernel(TileArgs p) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t tile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  if (tile >= p.ntiles) return;
+  const int64_t band = p.band0 + tile / p.ntc;
+  const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
+  if (c >= p.cols) return;
+  const int64_t r0 = band * kBlockLen;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  int cshift = 0;
+  if constexpr (kCol) cshift = 127 - (int)p.scale_col[band * p.ld_sc + c];
+  for (int i = 0; i < nrows; ++i) {
+    const int64_t r = r0 + i;
+    const int64_t g = r * p.cols + c;
+    if (g < p.start || g >= p.end) continue;
+    const float w = work_value<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
+    p.data_row[g - p.start] = cvt1(w, 127 - (int)p.scale_row[r * p.ld_sr + (c >> 5)]);
+    if constexpr (kCol) p.data_col[g - p.start] = cvt1(w, cshift);
+  }
+}
+
+// ------------------------------------------------------------------ E8M0 scales
+
+struct ScaleArgs {
+  int64_t rows, cols, start, end;
+  const void* amax_row;
+  int64_t ld_ar;
+  const void* amax_col;
+  int64_t ld_ac;
+  uint8_t* scale_row;
+  int64_t ld_sr;
+  uint8_t* scale_col;
+  int64_t ld_sc;
+  int64_t r_first, r_last;  // rows the fragment touches
+  int64_t b_first, b_last;  // bands the fragment touches
+};
+
+// Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
+// values, so the biased MX exponent is field - 8, clamped at 0 (subnormal and zero amax
+// included); the field is at most 254 for finite amax, so the upper clamp never applies.
+template <typename T>
+__device__ __forceinline__ uint8_t e8m0_of(uint32_t bits) {
+  const int field = sizeof(T) == 2 ? (int)((bits >> 7) & 0xFF) : (int)((bits >> 23) & 0xFF);
+  return (uint8_t)(field > 8 ? field - 8 : 0);
+}
+
+// Whether column-wise block (b, c) holds an element of [start, end).
+__device__ __forceinline__ bool col_block_touched(const ScaleArgs& p, int64_t b, int64_t c) {
+  const int64_t r0 = b * kBlockLen;
+  const int64_t r1 = min<int64_t>(r0 + kBlockLen, p.rows) - 1;
+  const int64_t need = p.start - c;  // smallest row r with r * cols + c >= start
+  int64_t rmin = need <= 0 ? 0 : (need + p.cols - 1) / p.cols;
+  if (rmin < r0) rmin = r0;
+  return rmin <= r1 && rmin * p.cols + c < p.end;
+}
+
+// grid: x over entries of one row (or band), y over rows (or bands), z = direction.
+template <typename T>
+__global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (blockIdx.z == 0) {
+    const int64_t nb = (p.cols + kBlockLen - 1) / kBlockLen;
+    if (x >= nb) return;
+    for (int64_t r = p.r_first + blockIdx.y; r <= p.r_last; r += gridDim.y) {
+      const int64_t gb = r * p.cols + x * kBlockLen;
+      const int64_t ge = min<int64_t>(gb + kBlockLen, (r + 1) * p.cols);
+      if (gb < p.end && ge > p.start)
+        p.scale_row[r * p.ld_sr + x] =
+            e8m0_of<T>(static_cast<const T*>(p.amax_row)[r * p.ld_ar + x]);
+    }
+  } else {
+    if (x >= p.cols) return;
+    for (int64_t b = p.b_first + blockIdx.y; b <= p.b_last; b += gridDim.y) {
+      const bool edge = b == p.b_first || b == p.b_last;
+      if (!edge || col_block_touched(p, b, x))
+        p.scale_col[b * p.ld_sc + x] =
+            e8m0_of<T>(static_cast<const T*>(p.amax_col)[b * p.ld_ac + x]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MAX-combine
+
+constexpr int kMaxSrcs = 8;
+
+struct CombineArgs {
+  const void* src[kMaxSrcs];
+  int k;
+  void* dst;
+  int64_t count;   // entries
+  int32_t vec;     // every pointer 16-byte aligned
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  constexpr int E = 16 / sizeof(T);
+  int64_t done = 0;
+  if (a.vec) {
+    const int64_t n16 = a.count / E;
+    for (int64_t i = tid; i < n16; i += stride) {
+      uint32_t m[4];
+      load16(static_cast<const uint4*>(a.src[0]) + i, m);
+      for (int j = 1; j < a.k; ++j) {
+        uint32_t v[4];
+        load16(static_cast<const uint4*>(a.src[j]) + i, v);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) m[t] = sizeof(T) == 2 ? pk_max_u16(m[t], v[t]) : umax(m[t], v[t]);
+      }
+      static_cast<uint4*>(a.dst)[i] = make_uint4(m[0], m[1], m[2], m[3]);
+    }
+    done = n16 * E;
+  }
+  for (int64_t i = done + tid; i < a.count; i += stride) {
+    uint32_t m = static_cast<const T*>(a.src[0])[i];
+    for (int j = 1; j < a.k; ++j) m = umax(m, static_cast<const T*>(a.src[j])[i]);
+    static_cast<T*>(a.dst)[i] = (T)m;
+  }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+TileArgs tile_args(const Piece& p, int64_t tile_cols) {
+  TileArgs a{};
+  a.rows = p.rows;
+  a.cols = p.cols;
+  a.start = p.start;
+  a.end = p.start + p.len;
+  a.input = p.input;
+  a.amax_row = p.amax_row;
+  a.ld_ar = p.ld_ar;
+  a.amax_col = p.amax_col;
+  a.ld_ac = p.ld_ac;
+  a.scale_row = p.scale_row;
+  a.ld_sr = p.ld_sr;
+  a.scale_col = p.scale_col;
+  a.ld_sc = p.ld_sc;
+  a.data_row = p.data_row;
+  a.data_col = p.data_col;
+  const int64_t b0 = (p.start / p.cols) / kBlockLen;
+  const int64_t b1 = ((a.end - 1) / p.cols) / kBlockLen;
+  a.band0 = b0;
+  a.ntc = cdiv(p.cols, tile_cols);
+  a.ntiles = (b1 - b0 + 1) * a.ntc;
+  const int64_t esz = elem_size(p.dtype);
+  a.col_vec = p.amax_col && (reinterpret_cast<uintptr_t>(p.amax_col) % 16 == 0) &&
+              ((p.ld_ac * esz) % 16 == 0);
+  return a;
+}
+
+template <typename K>
+hipError_t launch_tiles(K kernel, const TileArgs& a, hipStream_t s) {
+  const int64_t groups = cdiv(a.ntiles, kWavesPerGroup);
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, bool kCol, bool kPre>
+hipError_t amax_dispatch(const Piece& p, bool vec, hipStream_t s) {
+  if (vec)
+    return launch_tiles(amax_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), s);
+  return launch_tiles(amax_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols), s);
+}
+
+template <typename T, bool kCol, bool kPre>
+hipError_t cast_dispatch(const Piece& p, bool vec, hipStream_t s) {
+  if (vec)
+    return launch_tiles(cast_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), s);
+  return launch_tiles(cast_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols), s);
+}
+
+bool vec_common_ok(const Piece& p) {
+  const int64_t esz = elem_size(p.dtype);
+  const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
+  return p.cols % kBlockLen == 0 && virt % 16 == 0;
+}
+
+}  // namespace
+
+bool amax_fast_ok(const Piece& p) { return vec_common_ok(p); }
+
+bool cast_fast_ok(const Piece& p) {
+  if (!vec_common_ok(p)) return false;
+  const uintptr_t e = (uintptr_t)(16 / elem_size(p.dtype));  // output bytes per chunk
+  auto ok = [&](const uint8_t* d) {
+    return d == nullptr || (reinterpret_cast<uintptr_t>(d) - (uintptr_t)p.start) % e == 0;
+  };
+  return ok(p.data_row) && ok(p.data_col);
+}
+
+hipError_t launch_partial_amax(const Piece& p, hipStream_t s) {
+  const bool vec = amax_fast_ok(p);
+  const bool col = p.amax_col != nullptr;
+  if (p.dtype == kBF16)
+    return col ? amax_dispatch<uint16_t, true, false>(p, vec, s)
+               : amax_dispatch<uint16_t, false, false>(p, vec, s);
+  if (p.preround)
+    return col ? amax_dispatch<uint32_t, true, true>(p, vec, s)
+               : amax_dispatch<uint32_t, false, true>(p, vec, s);
+  return col ? amax_dispatch<uint32_t, true, false>(p, vec, s)
+             : amax_dispatch<uint32_t, false, false>(p, vec, s);
+}
+
+hipError_t launch_partial_cast(const Piece& p, hipStream_t s) {
+  const bool vec = cast_fast_ok(p);
+  const bool col = p.data_col != nullptr;
+  if (p.dtype == kBF16)
+    return col ? cast_dispatch<uint16_t, true, false>(p, vec, s)
+               : cast_dispatch<uint16_t, false, false>(p, vec, s);
+  if (p.preround)
+    return col ? cast_dispatch<uint32_t, true, true>(p, vec, s)
+               : cast_dispatch<uint32_t, false, true>(p, vec, s);
+  return col ? cast_dispatch<uint32_t, true, false>(p, vec, s)
+             : cast_dispatch<uint32_t, false, false>(p, vec, s);
+}
+
+hipError_t launch_compute_scales(const Piece& p, hipStream_t s) {
+  ScaleArgs a{};
+  a.rows = p.rows;
+  a.cols = p.cols;
+  a.start = p.start;
+  a.end = p.start + p.len;
+  a.amax_row = p.amax_row;
+  a.ld_ar = p.ld_ar;
+  a.amax_col = p.amax_col;
+  a.ld_ac = p.ld_ac;
+  a.scale_row = p.scale_row;
+  a.ld_sr = p.ld_sr;
+  a.scale_col = p.scale_col;
+  a.ld_sc = p.ld_sc;
+  a.r_first = p.start / p.cols;
+  a.r_last = (a.end - 1) / p.cols;
+  a.b_first = a.r_first / kBlockLen;
+  a.b_last = a.r_last / kBlockLen;
+  const int64_t nb = cdiv(p.cols, kBlockLen);
+  const bool col = p.amax_col != nullptr;
+  const int64_t width = col ? std::max<int64_t>(nb, p.cols) : nb;
+  const int64_t height = col ? std::max<int64_t>(a.r_last - a.r_first + 1, a.b_last - a.b_first + 1)
+                             : a.r_last - a.r_first + 1;
+  dim3 grid((unsigned)cdiv(width, 256), (unsigned)std::min<int64_t>(height, 65535), col ? 2 : 1);
+  if (p.dtype == kBF16)
+    hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(scales_kernel<uint32_t>, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,
+                          hipStream_t s) {
+  const int64_t esz = elem_size(dtype);
+  // More than kMaxSrcs sources: fold them into dst kMaxSrcs - 1 at a time after the first pass.
+  int done = 0;
+  while (done < k) {
+    CombineArgs a{};
+    int n = 0;
+    if (done > 0) a.src[n++] = dst;
+    while (n < kMaxSrcs && done < k) a.src[n++] = srcs[done++];
+    a.k = n;
+    a.dst = dst;
+    a.count = count;
+    bool vec = reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+    for (int j = 0; j < n; ++j) vec = vec && reinterpret_cast<uintptr_t>(a.src[j]) % 16 == 0;
+    a.vec = vec;
+    const int64_t work = vec ? cdiv(count * esz, 16) : count;
+    const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(cdiv(work, 256), 256 * 16));
+    if (dtype == kBF16)
+      hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)groups), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(combine_kernel<uint32_t>, dim3((unsigned)groups), dim3(256), 0, s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace mxfp8

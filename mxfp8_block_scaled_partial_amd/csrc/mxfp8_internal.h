@@ -1,0 +1,42 @@
+// Internal interface between the C-ABI host layer (abi.cpp) and the HIP kernels
+// (kernels.hip).  Not installed; the public interface is include/mxfp8_partial.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp8 {
+
+enum Dtype : int { kFP32 = 0, kBF16 = 1 };
+
+// A validated piece.  Absent directions / outputs are nullptr.
+struct Piece {
+  int64_t rows, cols, start, len;
+  int dtype;
+  bool preround;
+  const void* input;
+  void* amax_row;
+  int64_t ld_ar;
+  void* amax_col;
+  int64_t ld_ac;
+  uint8_t* scale_row;
+  int64_t ld_sr;
+  uint8_t* scale_col;
+  int64_t ld_sc;
+  uint8_t* data_row;
+  uint8_t* data_col;
+};
+
+inline int64_t elem_size(int dtype) { return dtype == kBF16 ? 2 : 4; }
+
+// Whether the vectorized kernels apply (see mxfp8_query_path in the public header).
+bool amax_fast_ok(const Piece& p);
+bool cast_fast_ok(const Piece& p);
+
+hipError_t launch_partial_amax(const Piece& p, hipStream_t s);
+hipError_t launch_partial_cast(const Piece& p, hipStream_t s);
+hipError_t launch_compute_scales(const Piece& p, hipStream_t s);
+hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,
+                          hipStream_t s);
+
+}  // namespace mxfp8

@@ -1,0 +1,229 @@
+"""CPU tests of the C ABI boundary: the library loads and exports every function that
+include/mxfp8_partial.h declares, the ctypes layout matches the header, and host-side
+validation returns the documented status codes.  Nothing here launches a kernel: every call
+either fails validation, is an empty fragment (a no-op), or is the host-only path query."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from mxfp8_block_scaled_partial_amd import binding as B
+from mxfp8_block_scaled_partial_amd import writeback as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+# fake device addresses: validation compares them but never dereferences them
+BASE = 0x7F0000000000
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mxfp8_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == set(B.EXPORTS)
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_piece_layout_matches_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stddef.h>\n#include <stdio.h>\n#include "mxfp8_partial.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(mxfp8_piece),"
+        " offsetof(mxfp8_piece,input), offsetof(mxfp8_piece,amax_row),"
+        " offsetof(mxfp8_piece,amax_col), offsetof(mxfp8_piece,scale_row),"
+        " offsetof(mxfp8_piece,scale_col), offsetof(mxfp8_piece,data_row),"
+        " offsetof(mxfp8_piece,data_col), sizeof(mxfp8_buf));return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", f"-I{ROOT}/include", str(src), "-o", str(exe)])
+    got = [int(v) for v in subprocess.check_output([str(exe)]).split()]
+    P = B.Piece
+    want = [ctypes.sizeof(P), P.input.offset, P.amax_row.offset, P.amax_col.offset,
+            P.scale_row.offset, P.scale_col.offset, P.data_row.offset, P.data_col.offset,
+            ctypes.sizeof(B.Buf)]
+    assert got == want
+
+
+def raw_piece(rows=64, cols=64, start=0, length=None, dtype=B.BF16, pre=0, **bufs):
+    n = rows * cols if length is None else length
+    esz = 2 if dtype == B.BF16 else 4
+    nb, nbands = (cols + 31) // 32, (rows + 31) // 32
+    default = {
+        "input": BASE,
+        "amax_row": B.Buf(BASE + 0x10000000, nb), "amax_col": B.Buf(BASE + 0x20000000, cols),
+        "scale_row": B.Buf(BASE + 0x30000000, nb), "scale_col": B.Buf(BASE + 0x40000000, cols),
+        "data_row": BASE + 0x50000000, "data_col": BASE + 0x60000000}
+    default.update(bufs)
+    del esz, nbands
+    return B.Piece(rows, cols, start, n, dtype, pre, default["input"], default["amax_row"],
+                   default["amax_col"], default["scale_row"], default["scale_col"],
+                   default["data_row"], default["data_col"])
+
+
+def call(fn, *pieces):
+    arr = (B.Piece * len(pieces))(*pieces)
+    return getattr(B.lib(), fn)(arr, len(pieces), None)
+
+
+AMAX, SCALES, CAST = "mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast"
+
+
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST])
+def test_shape_range_dtype_errors(fn):
+    assert call(fn, raw_piece(rows=0)) == B.ERR_ARG
+    assert call(fn, raw_piece(cols=-3)) == B.ERR_ARG
+    assert call(fn, raw_piece(start=1)) == B.ERR_RANGE           # runs one past the end
+    assert call(fn, raw_piece(start=-1, length=4)) == B.ERR_RANGE
+    assert call(fn, raw_piece(start=4096, length=1)) == B.ERR_RANGE
+    assert call(fn, raw_piece(dtype=7)) == B.ERR_DTYPE
+    assert "piece 0" in B.mxfp8_last_error()
+    assert B.lib()[fn](None, -1, None) == B.ERR_ARG
+    assert B.lib()[fn](None, 1, None) == B.ERR_ARG
+
+
+def test_preround_needs_fp32():
+    assert call(AMAX, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
+    assert call(CAST, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
+    assert call(AMAX, raw_piece(dtype=B.BF16, pre=2)) == B.ERR_ARG
+
+
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST])
+def test_empty_fragment_is_a_no_op_even_with_null_buffers(fn):
+    p = B.Piece(64, 64, 17, 0, B.BF16, 0, None, B.Buf(None, 0), B.Buf(None, 0), B.Buf(None, 0),
+                B.Buf(None, 0), None, None)
+    assert call(fn, p) == B.OK
+    assert call(fn) == B.OK  # n == 0
+
+
+def test_required_buffers():
+    assert call(AMAX, raw_piece(amax_row=B.Buf(None, 0))) == B.ERR_MISSING
+    assert call(AMAX, raw_piece(input=None)) == B.ERR_ARG
+    assert call(SCALES, raw_piece(scale_row=B.Buf(None, 0))) == B.ERR_MISSING
+    # column-wise amax present -> column-wise scales required
+    assert call(SCALES, raw_piece(scale_col=B.Buf(None, 0))) == B.ERR_MISSING
+    assert call(CAST, raw_piece(data_row=None)) == B.ERR_MISSING
+    assert call(CAST, raw_piece(scale_row=B.Buf(None, 0))) == B.ERR_MISSING
+    # requested column-wise output needs its scales
+    assert call(CAST, raw_piece(scale_col=B.Buf(None, 0))) == B.ERR_MISSING
+    assert "scale_col" in B.mxfp8_last_error()
+
+
+def test_omitted_columnwise_output_ignores_its_scales():
+    # data_col absent: a scale_col with an invalid leading dimension is ignored
+    p = raw_piece(data_col=None, scale_col=B.Buf(BASE + 0x40000000, 1))
+    assert B.mxfp8_query_path(p, 1) >= 0
+    # with data_col present the same scale_col is rejected
+    p = raw_piece(scale_col=B.Buf(BASE + 0x40000000, 1))
+    assert B.mxfp8_query_path(p, 1) == -B.ERR_LAYOUT
+    # amax without the column direction ignores nothing it needs: row-only is valid
+    p = raw_piece(amax_col=B.Buf(None, 0))
+    assert B.mxfp8_query_path(p, 0) >= 0
+
+
+def test_layout_errors():
+    assert call(AMAX, raw_piece(amax_row=B.Buf(BASE + 0x10000000, 1))) == B.ERR_LAYOUT  # ld < 2
+    assert call(AMAX, raw_piece(amax_col=B.Buf(BASE + 0x20000000, 63))) == B.ERR_LAYOUT
+    assert call(AMAX, raw_piece(input=BASE + 1)) == B.ERR_LAYOUT          # misaligned BF16
+    assert call(AMAX, raw_piece(dtype=B.FP32, input=BASE + 2)) == B.ERR_LAYOUT
+    assert call(AMAX, raw_piece(amax_row=B.Buf(BASE + 1, 2))) == B.ERR_LAYOUT
+    assert call(SCALES, raw_piece(scale_row=B.Buf(BASE + 0x30000000, 1))) == B.ERR_LAYOUT
+
+
+def test_overlap_errors():
+    # input overlapping the row-wise data it is cast into
+    assert call(CAST, raw_piece(data_row=BASE + 100)) == B.ERR_LAYOUT
+    assert "overlaps" in B.mxfp8_last_error()
+    assert call(CAST, raw_piece(data_col=BASE + 0x50000000 + 10)) == B.ERR_LAYOUT
+    assert call(AMAX, raw_piece(amax_col=B.Buf(BASE + 0x10000000 + 8, 64))) == B.ERR_LAYOUT
+    assert call(SCALES, raw_piece(scale_row=B.Buf(BASE + 0x10000000, 2))) == B.ERR_LAYOUT
+
+
+def test_combine_validation():
+    L = B.lib()
+    srcs = (ctypes.c_void_p * 3)(BASE, BASE + 0x1000000, BASE + 0x2000000)
+    assert L.mxfp8_combine_amax(BASE + 0x3000000, srcs, 0, 16, B.FP32, None) == B.ERR_ARG
+    assert L.mxfp8_combine_amax(BASE + 0x3000000, srcs, 3, -1, B.FP32, None) == B.ERR_ARG
+    assert L.mxfp8_combine_amax(BASE + 0x3000000, srcs, 3, 16, 9, None) == B.ERR_DTYPE
+    assert L.mxfp8_combine_amax(BASE + 0x3000000, srcs, 3, 0, B.FP32, None) == B.OK
+    assert L.mxfp8_combine_amax(None, srcs, 3, 16, B.FP32, None) == B.ERR_MISSING
+    assert L.mxfp8_combine_amax(BASE + 0x3000002, srcs, 3, 16, B.FP32, None) == B.ERR_LAYOUT
+    # dst may alias srcs[0] only; partial overlap of a later source is rejected
+    assert L.mxfp8_combine_amax(BASE + 0x1000000 + 4, srcs, 3, 16, B.FP32, None) == B.ERR_LAYOUT
+    nul = (ctypes.c_void_p * 2)(BASE, None)
+    assert L.mxfp8_combine_amax(BASE + 0x3000000, nul, 2, 16, B.BF16, None) == B.ERR_MISSING
+
+
+def test_query_path_selects_vector_kernel_only_for_aligned_layouts():
+    q = B.mxfp8_query_path
+    assert q(raw_piece(), 0) == 1 and q(raw_piece(), 1) == 1
+    # start 17 with input = base + 17 elements: virtual base aligned -> vector path
+    assert q(raw_piece(start=17, length=100, input=BASE + 34,
+                       data_row=BASE + 0x50000000 + 17, data_col=BASE + 0x60000000 + 17), 1) == 1
+    # a fragment held in its own (aligned) buffer: shifted by 17 elements -> element path
+    assert q(raw_piece(start=17, length=100), 0) == 0
+    # ragged width -> element path
+    assert q(raw_piece(rows=40, cols=40), 0) == 0
+    # fragment-relative outputs misaligned for the cast only
+    p = raw_piece(start=32, length=64, input=BASE + 64, data_row=BASE + 0x50000000 + 3)
+    assert q(p, 0) == 1 and q(p, 1) == 0
+    assert q(raw_piece(rows=0), 0) == -B.ERR_ARG
+    assert q(raw_piece(), 5) == -B.ERR_ARG
+
+
+# ------------------------------------------------------------------ binding marshalling
+
+
+def test_binding_maps_zero_element_tensors_to_empty_handles():
+    # zero-element views that still have storage become NULL, before any device check
+    storage = torch.zeros(64, dtype=torch.uint8)
+    empty_view = storage[10:10]
+    assert empty_view.numel() == 0 and empty_view.untyped_storage().nbytes() == 64
+    p = B.make_piece(4, 32, 0, None, length=0, in_dtype=torch.float32, data_row=empty_view,
+                     scale_col=torch.zeros(0, 0, dtype=torch.uint8))
+    assert p.data_row is None and p.scale_col.ptr is None and p.input is None
+
+
+def test_binding_rejects_host_tensors_and_bad_dtypes():
+    x = torch.zeros(64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        B.make_piece(2, 32, 0, x)
+    with pytest.raises(ValueError):
+        B.make_piece(2, 32, 0, torch.zeros(64, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        B.make_piece(2, 32, 0, None, length=64, in_dtype=torch.float32,
+                     amax_row=torch.zeros(2, 1, dtype=torch.bfloat16))
+
+
+# ------------------------------------------------------------------ batch helper host logic
+
+
+def test_split_fragment_pieces():
+    specs = [W.WeightSpec(4, 32, True), W.WeightSpec(2, 32, False), W.WeightSpec(3, 64, True)]
+    # sizes 128, 64, 192 -> offsets 0, 128, 192
+    assert W.split_fragment(specs, 100, 200) == [(0, 100, 28, 0), (1, 0, 64, 28),
+                                                 (2, 0, 108, 92)]
+    assert W.split_fragment(specs, 128, 0) == []
+    assert W.split_fragment(specs, 0, 384) == [(0, 0, 128, 0), (1, 0, 64, 128), (2, 0, 192, 192)]
+
+
+def test_packed_amax_layout():
+    specs = [W.WeightSpec(40, 96, True), W.WeightSpec(33, 64, False)]
+    p = W.PackedAmax(specs, torch.bfloat16, "cpu")
+    assert p.numel == 40 * 3 + 2 * 96 + 33 * 2
+    r0, c0 = p.views(0)
+    r1, c1 = p.views(1)
+    assert r0.shape == (40, 3) and c0.shape == (2, 96) and r1.shape == (33, 2) and c1 is None
+    assert c0.data_ptr() - r0.data_ptr() == 40 * 3 * 2
+    assert r1.data_ptr() - r0.data_ptr() == (40 * 3 + 2 * 96) * 2

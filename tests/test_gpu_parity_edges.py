@@ -1,0 +1,402 @@
+"""GPU parity on edge cases and per-kernel contracts, byte for byte against the oracle:
+ragged shapes, short last bands, tiny fragments, padded leading dimensions, the MAX-merge
+into non-zero amax entries, every BF16 code at every scale byte through the cast, scales for
+every non-negative BF16 amax, K-way combines, omitted column-wise outputs, untouched bytes
+outside the fragment, consecutive updates with stable pointers, determinism, and many
+pieces of one weight merging in a single call."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp8_block_scaled_partial_amd import binding as B
+from mxfp8_block_scaled_partial_amd import workloads as wl
+from mxfp8_block_scaled_partial_amd import writeback as W
+
+from gpu_util import (DEV, assert_same, bits, first_mismatch, require_gpu, run_matrix, to_dev,
+                      to_np, torch_dtype)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def splits(n, k, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cuts = np.sort(g.integers(0, n + 1, k - 1))
+    cuts = np.concatenate([[0], cuts, [n]])
+    return [(int(a), int(b - a)) for a, b in zip(cuts[:-1], cuts[1:])]
+
+
+# ------------------------------------------------------------------ shapes and fragments
+
+SHAPES = [(37, 45), (33, 40), (1, 70), (70, 1), (96, 33), (65, 96), (100, 64), (31, 4128),
+          (64, 64), (2, 32)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_shapes_full_and_split(rows, cols, dtype):
+    x = wl.random_matrix(rows, cols, dtype, seed=rows * 7 + cols, kind="mixed")
+    n = rows * cols
+    for frags in ([(0, n)], splits(n, 3, rows + cols), splits(n, 5, rows * cols)):
+        for colwise in (True, False):
+            want = oracle.writeback(x, rows, cols, frags, colwise)
+            for inputs in ("views", "own"):
+                for shared in (True, False):
+                    got = run_matrix(x, rows, cols, frags, colwise, inputs=inputs, shared=shared)
+                    assert_same(got, want, rows, cols,
+                                f"{frags} colwise={colwise} {inputs} shared={shared}: ")
+
+
+@pytest.mark.parametrize("kind", ["tiny", "huge", "normal"])
+@pytest.mark.parametrize("pre", [False, True])
+def test_value_ranges_fp32(kind, pre):
+    rows, cols = 96, 160
+    x = wl.random_matrix(rows, cols, "fp32", seed=5, kind=kind)
+    for frags in ([(0, rows * cols)], [(17, 5000), (5017, rows * cols - 5017)]):
+        want = oracle.writeback(x, rows, cols, frags, True, pre)
+        for inputs in ("views", "own"):
+            got = run_matrix(x, rows, cols, frags, True, pre, inputs=inputs)
+            assert_same(got, want, rows, cols, f"{kind} pre={pre} {frags} {inputs}: ")
+
+
+@pytest.mark.parametrize("start,length", [(0, 1), (5, 1), (31, 1), (0, 31), (1, 31), (16, 32),
+                                          (31, 2), (95, 66), (160 * 33 - 7, 40),
+                                          (160 * 95, 160), (160 * 96 - 1, 1)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_tiny_fragments(start, length, dtype):
+    rows, cols = 96, 160
+    x = wl.random_matrix(rows, cols, dtype, seed=start + length, kind="mixed")
+    frags = [(start, length)]
+    want = oracle.writeback(x, rows, cols, frags, True)
+    for inputs in ("views", "own"):
+        got = run_matrix(x, rows, cols, frags, True, inputs=inputs)
+        assert_same(got, want, rows, cols, f"{inputs}: ")
+
+
+def test_vector_and_element_paths_are_both_exercised():
+    x = torch.zeros(64 * 64, dtype=torch.bfloat16, device=DEV)
+    ar = torch.zeros(64, 2, dtype=torch.bfloat16, device=DEV)
+    p_view = B.make_piece(64, 64, 17, x[17:117], amax_row=ar)
+    p_own = B.make_piece(64, 64, 17, x[17:117].clone(), amax_row=ar)
+    assert B.mxfp8_query_path(p_view, 0) == 1
+    assert B.mxfp8_query_path(p_own, 0) == 0
+
+
+# ------------------------------------------------------------------ padded leading dimensions
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_padded_leading_dimensions_and_padding_untouched(dtype):
+    rows, cols = 70, 96
+    x = wl.random_matrix(rows, cols, dtype, seed=3, kind="mixed")
+    nb, nbands = 3, 3
+    tdt = torch_dtype(x)
+    xd = to_dev(x)
+    frag = (40, rows * cols - 100)
+    xs = xd[frag[0]:frag[0] + frag[1]]
+    # padded arrays: padding holds a sentinel the library must never touch
+    ar = torch.full((rows, nb + 5), 3.0, dtype=tdt, device=DEV)
+    ac = torch.full((nbands, cols + 7), 3.0, dtype=tdt, device=DEV)
+    ar[:, :nb] = 0
+    ac[:, :cols] = 0
+    sr = torch.full((rows, nb + 2), 0xEE, dtype=torch.uint8, device=DEV)
+    sc = torch.full((nbands, cols + 9), 0xEE, dtype=torch.uint8, device=DEV)
+    dr = torch.full((rows * cols,), 0xCD, dtype=torch.uint8, device=DEV)
+    dc = torch.full((rows * cols,), 0xCD, dtype=torch.uint8, device=DEV)
+    s, l = frag
+    B.mxfp8_partial_amax(B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac))
+    B.mxfp8_compute_scales(B.make_piece(rows, cols, s, None, length=l, in_dtype=tdt,
+                                        amax_row=ar, amax_col=ac, scale_row=sr, scale_col=sc))
+    B.mxfp8_partial_cast(B.make_piece(rows, cols, s, xs, scale_row=sr, scale_col=sc,
+                                      data_row=dr[s:s + l], data_col=dc[s:s + l]))
+    torch.cuda.synchronize()
+    o = oracle.new_buffers(rows, cols, oracle.dtype_of(x), True)
+    oracle.partial_amax(x[s:s + l], rows, cols, s, o["amax_row"], o["amax_col"])
+    osr = np.full((rows, nb), 0xEE, np.uint8)
+    osc = np.full((nbands, cols), 0xEE, np.uint8)
+    oracle.compute_scales(rows, cols, s, l, o["amax_row"], osr, o["amax_col"], osc)
+    odr = np.full(rows * cols, 0xCD, np.uint8)
+    odc = np.full(rows * cols, 0xCD, np.uint8)
+    oracle.partial_cast(x[s:s + l], rows, cols, s, osr, odr[s:s + l], osc, odc[s:s + l])
+    assert_same({"amax_row": to_np(ar)[:, :nb], "amax_col": to_np(ac)[:, :cols],
+                 "scale_row": to_np(sr)[:, :nb], "scale_col": to_np(sc)[:, :cols],
+                 "data_row": to_np(dr), "data_col": to_np(dc)},
+                {"amax_row": o["amax_row"], "amax_col": o["amax_col"], "scale_row": osr,
+                 "scale_col": osc, "data_row": odr, "data_col": odc}, rows, cols)
+    sentinel = bits(to_np(torch.full((1,), 3.0, dtype=tdt)))[0]
+    assert (bits(to_np(ar)[:, nb:]) == sentinel).all()
+    assert (bits(to_np(ac)[:, cols:]) == sentinel).all()
+    assert (to_np(sr)[:, nb:] == 0xEE).all() and (to_np(sc)[:, cols:] == 0xEE).all()
+
+
+# ------------------------------------------------------------------ per-kernel contracts
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("inputs", ["views", "own"])
+def test_amax_merges_into_existing_entries(dtype, inputs):
+    rows, cols = 96, 128
+    x = wl.random_matrix(rows, cols, dtype, seed=9, kind="normal")
+    g = np.random.Generator(np.random.PCG64(1))
+    init = np.abs(g.standard_normal((rows, 4)) * 1.5).astype(np.float32)
+    initc = np.abs(g.standard_normal((3, cols)) * 1.5).astype(np.float32)
+    if dtype == "bf16":
+        init, initc = wl.to_dtype(init, "bf16").reshape(rows, 4), wl.to_dtype(initc, "bf16").reshape(3, cols)
+    s, l = 1000, 6000
+    ar, ac = to_dev(init.ravel()).view(rows, 4), to_dev(initc.ravel()).view(3, cols)
+    xd = to_dev(x)
+    xs = xd[s:s + l] if inputs == "views" else xd[s:s + l].clone()
+    B.mxfp8_partial_amax(B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac))
+    torch.cuda.synchronize()
+    war, wac = init.copy(), initc.copy()
+    oracle.partial_amax(x[s:s + l], rows, cols, s, war, wac)
+    assert not first_mismatch(bits(to_np(ar)), bits(war))
+    assert not first_mismatch(bits(to_np(ac)), bits(wac))
+
+
+def test_scales_for_every_nonnegative_bf16_amax():
+    codes = np.arange(0, 0x7F80, dtype=np.uint16)  # +0 .. largest finite, subnormals included
+    codes = np.concatenate([codes, np.zeros((-codes.size) % 64, np.uint16)])
+    rows, cols = codes.size // 64, 64 * 32  # every row: 64 row-wise blocks
+    ar = to_dev(codes).view(rows, 64)
+    sr = torch.zeros(rows, 64, dtype=torch.uint8, device=DEV)
+    B.mxfp8_compute_scales(B.make_piece(rows, cols, 0, None, length=rows * cols,
+                                        in_dtype=torch.bfloat16, amax_row=ar, scale_row=sr))
+    want = np.zeros((rows, 64), np.uint8)
+    oracle.compute_scales(rows, cols, 0, rows * cols, codes.reshape(rows, 64), want)
+    assert not first_mismatch(to_np(sr), want)
+
+
+def test_scales_fp32_binade_edges():
+    vals = []
+    for k in range(-149, 128):
+        p = np.float32(2.0 ** k)
+        vals += [p, np.nextafter(p, np.float32(0)), np.nextafter(p, np.float32(np.inf))]
+    vals += [np.float32(0), np.finfo(np.float32).max]
+    v = np.array(vals, np.float32)
+    v = np.concatenate([v, np.zeros((-v.size) % 32, np.float32)])
+    rows, nb = v.size // 32, 32
+    ar = to_dev(v).view(rows, nb)
+    sr = torch.zeros(rows, nb, dtype=torch.uint8, device=DEV)
+    B.mxfp8_compute_scales(B.make_piece(rows, nb * 32, 0, None, length=rows * nb * 32,
+                                        in_dtype=torch.float32, amax_row=ar, scale_row=sr))
+    want = np.zeros((rows, nb), np.uint8)
+    oracle.compute_scales(rows, nb * 32, 0, rows * nb * 32, v.reshape(rows, nb), want)
+    assert not first_mismatch(to_np(sr), want)
+
+
+@pytest.mark.parametrize("k", [1, 2, 8, 9, 17])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_combine_k_buffers(k, dtype, offset):
+    count = 100003
+    g = np.random.Generator(np.random.PCG64(k))
+    srcs_np = [np.abs(g.standard_normal(count + offset)).astype(np.float32) for _ in range(k)]
+    if dtype == "bf16":
+        srcs_np = [wl.to_dtype(s, "bf16") for s in srcs_np]
+    srcs = [to_dev(s)[offset:] for s in srcs_np]  # offset 1: misaligned -> scalar path
+    dst = torch.empty_like(srcs[0])
+    B.mxfp8_combine_amax(dst, srcs)
+    want = oracle.combine_amax([s[offset:] for s in srcs_np])
+    assert not first_mismatch(bits(to_np(dst)), bits(want))
+    # in place on the first source
+    B.mxfp8_combine_amax(srcs[0], srcs)
+    assert not first_mismatch(bits(to_np(srcs[0])), bits(want))
+
+
+def _probe_matrix():
+    bits16 = np.arange(0x10000, dtype=np.uint32)
+    finite = ((bits16 >> 7) & 0xFF) != 0xFF
+    codes = bits16[finite].astype(np.uint16)      # 65024 values, a multiple of 32
+    scales = np.arange(255, dtype=np.uint8)
+    return codes, scales
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("inputs", ["views", "own"])
+def test_cast_every_bf16_value_at_every_scale_byte(dtype, inputs):
+    """Pins the hardware conversion (v_ldexp_f32, v_med3_f32, v_cvt_pk_fp8_f32): every finite
+    BF16 value (as BF16, or widened to FP32) at every scale byte 0..254, both directions."""
+    codes, scales = _probe_matrix()
+    cols, rows = codes.size, scales.size
+    x = np.tile(codes, rows)
+    if dtype == "fp32":
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    scale_row = np.repeat(scales[:, None], cols // 32, axis=1).copy()
+    nbands = (rows + 31) // 32
+    scale_col = np.zeros((nbands, cols), np.uint8)  # column blocks: a cycle of scale bytes
+    scale_col[:] = (np.arange(cols) % 255).astype(np.uint8)[None, :]
+    scale_col = (scale_col + np.arange(nbands, dtype=np.uint8)[:, None] * 37) % 255
+    scale_col = scale_col.astype(np.uint8)
+    s = 3 if inputs == "own" else 0   # a fragment in its own buffer: element-wise kernel
+    n = rows * cols - s
+    xd = to_dev(x)
+    xs = xd[s:] if inputs == "views" else xd[s:].clone()
+    dr = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    dc = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    B.mxfp8_partial_cast(B.make_piece(rows, cols, s, xs, scale_row=to_dev_u8(scale_row),
+                                      scale_col=to_dev_u8(scale_col), data_row=dr, data_col=dc))
+    torch.cuda.synchronize()
+    wr = np.zeros(n, np.uint8)
+    wc = np.zeros(n, np.uint8)
+    oracle.partial_cast(x[s:], rows, cols, s, scale_row, wr, scale_col, wc)
+    assert not first_mismatch(to_np(dr), wr, (rows, cols))
+    assert not first_mismatch(to_np(dc), wc, (rows, cols))
+
+
+def to_dev_u8(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def test_fp32_specific_values_through_the_cast():
+    """FP32 values BF16 cannot hold: E4M3 midpoints and their neighbours, subnormals, ties
+    of the BF16 pre-rounding, at unit and extreme scales."""
+    mids = []
+    for c in range(0x7E):
+        a = (c >> 3, c & 7)
+        va = (a[1] / 8) * 2.0 ** -6 if a[0] == 0 else (1 + a[1] / 8) * 2.0 ** (a[0] - 7)
+        b = ((c + 1) >> 3, (c + 1) & 7)
+        vb = (b[1] / 8) * 2.0 ** -6 if b[0] == 0 else (1 + b[1] / 8) * 2.0 ** (b[0] - 7)
+        m = np.float32((va + vb) / 2)
+        mids += [m, np.nextafter(m, np.float32(0)), np.nextafter(m, np.float32(1e9))]
+    g = np.random.Generator(np.random.PCG64(2))
+    sub = (g.integers(1, 1 << 23, 2000).astype(np.uint32)).view(np.float32)
+    # exact ties of the BF16 pre-rounding; high halves stay below BF16's overflow threshold
+    ties = ((g.integers(1, 0x7F7E, 2000).astype(np.uint32) << 16) | 0x8000).view(np.float32)
+    v = np.concatenate([np.array(mids, np.float32), sub, ties])
+    v = np.concatenate([v, -v])
+    v = np.concatenate([v, np.zeros((-v.size) % 32, np.float32)])
+    cols = v.size
+    for scale in (127, 0, 100, 200, 254):
+        for pre in (False, True):
+            scale_row = np.full((1, cols // 32), scale, np.uint8)
+            d = torch.zeros(cols, dtype=torch.uint8, device=DEV)
+            B.mxfp8_partial_cast(B.make_piece(1, cols, 0, to_dev(v), scale_row=to_dev_u8(scale_row),
+                                              data_row=d, preround=pre))
+            want = np.zeros(cols, np.uint8)
+            oracle.partial_cast(v, 1, cols, 0, scale_row, want, preround=pre)
+            assert not first_mismatch(to_np(d), want), (scale, pre)
+
+
+# ------------------------------------------------------------------ direction selection, sentinels
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_omitted_columnwise_output_skips_its_work_and_ignores_its_scales(dtype):
+    rows, cols = 64, 96
+    x = wl.random_matrix(rows, cols, dtype, seed=4, kind="mixed")
+    xd = to_dev(x)
+    o = oracle.writeback(x, rows, cols, [(0, rows * cols)], colwise=False)
+    sr = to_dev_u8(o["scale_row"])
+    garbage_sc = torch.full((2, cols), 0xFF, dtype=torch.uint8, device=DEV)  # would be invalid
+    dr = torch.zeros(rows * cols, dtype=torch.uint8, device=DEV)
+    B.mxfp8_partial_cast(B.make_piece(rows, cols, 0, xd, scale_row=sr, scale_col=garbage_sc,
+                                      data_row=dr, data_col=None))
+    torch.cuda.synchronize()
+    assert not first_mismatch(to_np(dr), o["data_row"])
+    # a requested column-wise output without scales is an error, and nothing is written
+    dc = torch.full((rows * cols,), 0x5A, dtype=torch.uint8, device=DEV)
+    with pytest.raises(B.Mxfp8Error) as e:
+        B.mxfp8_partial_cast(B.make_piece(rows, cols, 0, xd, scale_row=sr, data_row=dr,
+                                          data_col=dc))
+    assert e.value.status == B.ERR_MISSING
+    assert (to_np(dc) == 0x5A).all()
+
+
+@pytest.mark.parametrize("inputs", ["views", "own"])
+def test_bytes_outside_the_fragment_are_untouched(inputs):
+    rows, cols = 96, 160
+    x = wl.random_matrix(rows, cols, "bf16", seed=12, kind="mixed")
+    s, l = 1000 + 17, 7000
+    o = oracle.writeback(x, rows, cols, [(s, l)])
+    xd = to_dev(x)
+    xs = xd[s:s + l] if inputs == "views" else xd[s:s + l].clone()
+    dr = torch.full((rows * cols,), 0xAB, dtype=torch.uint8, device=DEV)
+    dc = torch.full((rows * cols,), 0xAB, dtype=torch.uint8, device=DEV)
+    B.mxfp8_partial_cast(B.make_piece(rows, cols, s, xs, scale_row=to_dev_u8(o["scale_row"]),
+                                      scale_col=to_dev_u8(o["scale_col"]), data_row=dr[s:s + l],
+                                      data_col=dc[s:s + l]))
+    torch.cuda.synchronize()
+    gr, gc = to_np(dr), to_np(dc)
+    assert (gr[:s] == 0xAB).all() and (gr[s + l:] == 0xAB).all()
+    assert (gc[:s] == 0xAB).all() and (gc[s + l:] == 0xAB).all()
+    assert not first_mismatch(gr[s:s + l], o["data_row"][s:s + l])
+    assert not first_mismatch(gc[s:s + l], o["data_col"][s:s + l])
+
+
+def test_fragment_sized_outputs():
+    """FSDP-style outputs: the data buffers hold only the fragment (misaligned relative to
+    the block grid), written through the element-wise cast."""
+    rows, cols = 64, 128
+    x = wl.random_matrix(rows, cols, "fp32", seed=13, kind="mixed")
+    s, l = 17, 5000
+    o = oracle.writeback(x, rows, cols, [(s, l)])
+    xd = to_dev(x)
+    dr = torch.zeros(l, dtype=torch.uint8, device=DEV)
+    dc = torch.zeros(l, dtype=torch.uint8, device=DEV)
+    p = B.make_piece(rows, cols, s, xd[s:s + l], scale_row=to_dev_u8(o["scale_row"]),
+                     scale_col=to_dev_u8(o["scale_col"]), data_row=dr, data_col=dc)
+    assert B.mxfp8_query_path(p, 1) == 0
+    B.mxfp8_partial_cast(p)
+    torch.cuda.synchronize()
+    assert not first_mismatch(to_np(dr), o["data_row"][s:s + l])
+    assert not first_mismatch(to_np(dc), o["data_col"][s:s + l])
+
+
+# ------------------------------------------------------------------ updates, pointers, determinism
+
+
+def test_consecutive_updates_keep_pointers_and_give_second_update_bytes():
+    rows, cols = 128, 256
+    frags = [(0, 10000 + 17), (10017, 12000), (22017, rows * cols - 22017)]
+    x1 = wl.random_matrix(rows, cols, "fp32", seed=1, kind="mixed")
+    x2 = wl.random_matrix(rows, cols, "fp32", seed=2, kind="normal")
+    wb = W.Writeback([W.WeightSpec(rows, cols, True)], torch.float32, DEV, frags, shared=False)
+    st = wb.storage[0]
+    ptrs = (st.data_row.data_ptr(), st.data_col.data_ptr(), st.scale_row.data_ptr(),
+            st.scale_col.data_ptr())
+    for x in (x1, x2):
+        xd = to_dev(x)
+        wb([xd[s:s + l] for s, l in frags])
+    torch.cuda.synchronize()
+    assert ptrs == (st.data_row.data_ptr(), st.data_col.data_ptr(), st.scale_row.data_ptr(),
+                    st.scale_col.data_ptr())
+    want = oracle.writeback(x2, rows, cols, frags)
+    ar, ac = wb.combined.views(0)
+    got = {"amax_row": to_np(ar), "amax_col": to_np(ac), "scale_row": to_np(st.scale_row),
+           "scale_col": to_np(st.scale_col), "data_row": to_np(st.data_row),
+           "data_col": to_np(st.data_col)}
+    assert_same(got, want, rows, cols)
+
+
+def test_repeated_runs_are_bitwise_identical():
+    rows, cols = 256, 512
+    x = wl.random_matrix(rows, cols, "bf16", seed=8, kind="mixed")
+    frags = splits(rows * cols, 7, 3)
+    outs = [run_matrix(x, rows, cols, frags, True, inputs="own", shared=True) for _ in range(3)]
+    for o in outs[1:]:
+        assert_same(o, outs[0], rows, cols)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_many_pieces_of_one_weight_in_one_call_share_an_amax_buffer(dtype):
+    rows, cols = 256, 512
+    x = wl.random_matrix(rows, cols, dtype, seed=21, kind="mixed")
+    frags = splits(rows * cols, 16, 5)
+    xd = to_dev(x)
+    tdt = torch_dtype(x)
+    ar = torch.zeros(rows, cols // 32, dtype=tdt, device=DEV)
+    ac = torch.zeros(rows // 32, cols, dtype=tdt, device=DEV)
+    pieces = [B.make_piece(rows, cols, s, xd[s:s + l] if i % 2 else xd[s:s + l].clone(),
+                           amax_row=ar, amax_col=ac) for i, (s, l) in enumerate(frags)]
+    B.mxfp8_partial_amax(pieces)
+    torch.cuda.synchronize()
+    want = oracle.new_buffers(rows, cols, oracle.dtype_of(x), True)
+    oracle.partial_amax(x, rows, cols, 0, want["amax_row"], want["amax_col"])
+    assert not first_mismatch(bits(to_np(ar)), bits(want["amax_row"]))
+    assert not first_mismatch(bits(to_np(ac)), bits(want["amax_col"]))
