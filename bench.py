@@ -1,0 +1,328 @@
+"""Benchmark of the MXFP8 master-weight writeback on one MI355X.
+
+One step is the whole path over a 16384x6144 master weight (BF16 by default) held as four
+contiguous fragments whose boundaries fall inside 32-value blocks (cuts at N/4+17, N/2+17,
+3N/4+17), as four ranks would hold it: zero-fill of one packed amax buffer per fragment,
+partial amax of every fragment, MAX-combine of the four buffers, E8M0 scales for the whole
+weight, and the in-place partial cast of every fragment to E4M3 row-wise and column-wise
+data.  Inputs are resident in HBM before timing; each step uses the next of several
+distinct input/output sets (>= 1.2 GB in all), so no step reads what the previous one left
+in the 256 MB Infinity Cache.
+
+Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
+``roofline`` is for the dominant kernel (the partial cast), from HIP events recorded on the
+launch stream around every cast call of the timed steps; ``kernels`` is the per-call table
+(full input and the quarter fragment at offset 17, BF16 and FP32); ``cpu_baseline`` times
+the oracle on the host over a band-aligned sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "µs/call and achieved HBM GB/s (% of peak) for partial amax + cast"
+KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_partial_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cast_bf16_16384x6144_counters.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dtype", choices=["bf16", "fp32"], default="bf16")
+    ap.add_argument("--min-footprint-gb", type=float, default=1.2,
+                    help="distinct input/output sets rotate until this many GB are in use")
+    ap.add_argument("--kernel-table", dest="kernel_table", action="store_true", default=True)
+    ap.add_argument("--no-kernel-table", dest="kernel_table", action="store_false")
+    ap.add_argument("--kernel-calls", type=int, default=30)
+    ap.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
+    ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
+    ap.add_argument("--cpu-rows", type=int, default=8192,
+                    help="rows of the weight (a band-aligned sample) the oracle processes")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain device copy (the counter calibration kernel)")
+    return ap.parse_args()
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_counters(alg_bytes_per_launch):
+    """HBM bytes per cast launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; None otherwise."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_sha256_16") != kernel_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build runs the writeback on a single MI355X "
+              "(the cross-rank MAX all-reduce is replaced by an on-device combine); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import binding as B
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
+    from mxfp8_block_scaled_partial_amd import workloads as wl
+    from mxfp8_block_scaled_partial_amd import writeback as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.lib()
+    dev = torch.device("cuda:0")
+    rows, cols = 16384, 6144
+    n = rows * cols
+    tdt = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    s_in = 2 if args.dtype == "bf16" else 4
+
+    log(f"generating {rows}x{cols} {args.dtype} input")
+    m = wl.matrix_large(args.dtype)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x0 = to_dev(m.data)
+    cuts = [0, n // 4 + 17, n // 2 + 17, 3 * n // 4 + 17, n]
+    frags = [(cuts[i], cuts[i + 1] - cuts[i]) for i in range(4)]
+    spec = W.WeightSpec(rows, cols, True)
+
+    set_bytes = n * s_in + 2 * n + 4 * (spec.amax_row_entries + spec.amax_col_entries) * s_in
+    n_sets = max(2, int(np.ceil(args.min_footprint_gb * 1e9 / set_bytes)))
+    log(f"{n_sets} buffer sets of {set_bytes / 1e6:.0f} MB")
+    sets = []
+    for i in range(n_sets):
+        x = x0 if i == 0 else x0.clone()
+        wb = W.Writeback([spec], tdt, dev, frags, shared=False)
+        plan = wb.plan([x[s:s + l] for s, l in frags])
+        sets.append((x, wb, plan))
+    for p in sets[0][2].amax:
+        assert B.mxfp8_query_path(p, 0) == 1
+    for p in sets[0][2].cast:
+        assert B.mxfp8_query_path(p, 1) == 1
+
+    # algorithmic bytes of one step
+    per = [BM.piece_bytes(rows, cols, s, l, s_in, True) for s, l in frags]
+    packed = spec.amax_row_entries + spec.amax_col_entries
+    stage_bytes = {
+        "zero": BM.zero_bytes(4, packed, s_in),
+        "amax": sum(p["amax"] for p in per),
+        "combine": BM.combine_bytes(4, packed, s_in),
+        "scales": BM.piece_bytes(rows, cols, 0, n, s_in, True)["scales"],
+        "cast": sum(p["cast"] for p in per),
+    }
+    step_bytes = sum(stage_bytes.values())
+
+    stage_names = [name for name, _ in sets[0][2].stages()]
+    stages = [s[2].stages() for s in sets]
+
+    def step(i, ev=None):
+        for j, (_, fn) in enumerate(stages[i % n_sets]):
+            if ev is not None:
+                ev[j].record()
+            fn()
+        if ev is not None:
+            ev[-1].record()
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    stage_ms = {name: statistics.median(e[j].elapsed_time(e[j + 1]) for e in evs)
+                for j, name in enumerate(stage_names)}
+    stage_ms_mean = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
+                     for j, name in enumerate(stage_names)}
+
+    # dominant kernel: the partial cast, 4 launches (one per fragment) per call
+    n_cast = sets[0][2].n_cast
+    cast_launch_us = stage_ms_mean["cast"] * 1e3 / n_cast
+    cast_bytes_launch = stage_bytes["cast"] / n_cast
+    achieved = cast_bytes_launch / (cast_launch_us * 1e-6) / 1e9
+    traffic = traffic_from_counters(cast_bytes_launch)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": f"cast_vec_kernel<{args.dtype}, colwise>",
+                "launch_us": round(cast_launch_us, 2),
+                "alg_bytes_per_launch": int(cast_bytes_launch)}
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": f"{rows}x{cols} {args.dtype} master weight as 4 contiguous "
+                               "fragments (cuts at N/4+17, N/2+17, 3N/4+17), bidirectional "
+                               "MXFP8 writeback: zero, partial amax, combine K=4, scales, "
+                               "partial cast",
+                   "rows": rows, "cols": cols, "fragments": frags, "buffer_sets": n_sets,
+                   "step_alg_bytes": step_bytes},
+        "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
+        "stage_alg_GBps": {k: round(stage_bytes[k] / (stage_ms[k] * 1e-3) / 1e9, 1)
+                           for k in stage_names},
+        "roofline": roofline,
+    }
+
+    if args.copy_probe:
+        nb = 1 << 30
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 10
+        out["copy_probe"] = {"bytes_per_launch": 2 * nb, "us": round(us, 2),
+                             "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
+        del a, b
+
+    if args.kernel_table:
+        out["kernels"] = kernel_table(args, sets if args.dtype == "bf16" else None, m, dev, tdt)
+
+    if args.cpu:
+        out["cpu_baseline"] = cpu_baseline(m, args.cpu_rows, s_in)
+
+    print(json.dumps(out), flush=True)
+
+
+def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
+    """Per-call µs and GB/s of partial amax and partial cast, the pages' table: full input and
+    the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Each call is
+    timed alone with HIP events, rotating over distinct buffer sets; median over calls."""
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import binding as B
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
+    from mxfp8_block_scaled_partial_amd import workloads as wl
+
+    rows, cols = 16384, 6144
+    n = rows * cols
+    table = {}
+    for dtype in ("bf16", "fp32"):
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        s_in = 2 if dtype == "bf16" else 4
+        if dtype == args.dtype:
+            m = m_default
+        else:
+            log(f"generating {rows}x{cols} {dtype} input for the kernel table")
+            m = wl.matrix_large(dtype)
+        host = m.data
+        x0 = (torch.from_numpy(host.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+              else torch.from_numpy(host)).to(dev)
+        per_set = n * s_in + 2 * n + 2 * n // 32 * s_in
+        n_sets = max(2, int(np.ceil(args.min_footprint_gb * 1e9 / per_set)))
+        bufs = []
+        for i in range(n_sets):
+            x = x0 if i == 0 else x0.clone()
+            ar = torch.zeros(rows, cols // 32, dtype=tdt, device=dev)
+            ac = torch.zeros(rows // 32, cols, dtype=tdt, device=dev)
+            sr = torch.full((rows, cols // 32), 120, dtype=torch.uint8, device=dev)
+            sc = torch.full((rows // 32, cols), 120, dtype=torch.uint8, device=dev)
+            dr = torch.empty(n, dtype=torch.uint8, device=dev)
+            dc = torch.empty(n, dtype=torch.uint8, device=dev)
+            bufs.append((x, ar, ac, sr, sc, dr, dc))
+        for run, (s, l) in (("full", (0, n)), ("partial", (17, n // 4))):
+            amax_p, cast_p = [], []
+            for (x, ar, ac, sr, sc, dr, dc) in bufs:
+                amax_p.append(B.make_piece(rows, cols, s, x[s:s + l], amax_row=ar, amax_col=ac))
+                cast_p.append(B.make_piece(rows, cols, s, x[s:s + l], scale_row=sr,
+                                           scale_col=sc, data_row=dr[s:s + l],
+                                           data_col=dc[s:s + l]))
+            pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
+            for kname, pieces, fn in (("amax", amax_p, B.mxfp8_partial_amax),
+                                      ("cast", cast_p, B.mxfp8_partial_cast)):
+                for i in range(3):
+                    fn(pieces[i % n_sets])
+                torch.cuda.synchronize()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(args.kernel_calls)]
+                for i, (e0, e1) in enumerate(ev):
+                    e0.record()
+                    fn(pieces[i % n_sets])
+                    e1.record()
+                torch.cuda.synchronize()
+                us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+                gbs = pb[kname] / (us * 1e-6) / 1e9
+                table[f"{kname}_{dtype}_{run}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
+                                                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                                                   "alg_bytes": pb[kname]}
+        del bufs, x0
+        torch.cuda.empty_cache()
+    return table
+
+
+def cpu_baseline(m, cpu_rows, s_in):
+    """The oracle (plain C, one thread) over the first ``cpu_rows`` rows of the same weight,
+    cut into 4 fragments like the GPU step, through the whole path."""
+    import oracle
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
+
+    rows, cols = cpu_rows, m.cols
+    n = rows * cols
+    cuts = [0, n // 4 + 17, n // 2 + 17, 3 * n // 4 + 17, n]
+    frags = [(cuts[i], cuts[i + 1] - cuts[i]) for i in range(4)]
+    x = m.data[:n]
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.writeback(x, rows, cols, frags, colwise=True)
+    dt = time.perf_counter() - t0
+    packed = rows * ((cols + 31) // 32) + ((rows + 31) // 32) * cols
+    per = [BM.piece_bytes(rows, cols, s, l, s_in, True) for s, l in frags]
+    total = (BM.zero_bytes(4, packed, s_in) + sum(p["amax"] + p["cast"] for p in per)
+             + BM.combine_bytes(4, packed, s_in)
+             + BM.piece_bytes(rows, cols, 0, n, s_in, True)["scales"])
+    return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {rows} of 16384 rows ({rows}x{cols}, {n} elements), 4 fragments, "
+                      "whole path (amax, combine, scales, cast), single-threaded C oracle",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -154,7 +154,8 @@ def make_piece(rows: int, cols: int, start: int, input=None, *, length: int | No
     ``input`` is the fragment's values (contiguous, float32 or bfloat16); ``length`` defaults
     to ``input.numel()``.  amax/scale arguments are 2-D tensors (row stride = leading
     dimension); data arguments are fragment-relative byte tensors.  Zero-element tensors and
-    None are empty handles."""
+    None are empty handles.  The piece holds raw device pointers: the tensors must stay alive
+    until the call that uses the piece has been enqueued."""
     if length is None:
         length = 0 if input is None else input.numel()
     if in_dtype is None:

@@ -269,73 +269,95 @@ __device__ __forceinline__ uint32_t load_masked(const TileArgs& p, int64_t g, ui
 
 // ------------------------------------------------------------------ partial amax, vector path
 
+constexpr int kRowsPerWave = kBlockLen / kWavesPerGroup;  // 8 rows of the band per wave
+
+// A workgroup owns one tile: a 32-row band x 64*E columns.  Wave w streams rows 8w .. 8w+7
+// with all eight 16-byte loads in flight; the four waves' column-wise maxima meet in LDS.
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
   constexpr int E = Chunk<T>::E;
-  constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block
-  constexpr int WC = kWaveSize * E;     // columns per wave tile
-  constexpr int NK = kBlockLen / LB;    // row maxima each lane keeps
+  constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block (4 BF16, 8 FP32)
+  constexpr int WC = kWaveSize * E;     // tile width in columns
+  constexpr int RW = kRowsPerWave;
+  constexpr int NK = RW / LB;           // row maxima each lane keeps (2 BF16, 1 FP32)
+  __shared__ uint4 s_col[kWavesPerGroup][kWaveSize];
+  __shared__ uint32_t s_touch[kWavesPerGroup][kWaveSize];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + (threadIdx.x >> 6);
-  if (tile >= p.ntiles) return;
+  const int wave = threadIdx.x >> 6;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  if (tile >= p.ntiles) return;  // uniform over the workgroup
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * WC;
   const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen;
   const bool cvalid = c < p.cols;
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int i0 = wave * RW;  // this wave's first row within the band
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
 
   uint32_t col[4] = {0, 0, 0, 0};
-  const T* src = static_cast<const T*>(p.input) + (r0 * p.cols + c - p.start);
+  const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
 
   if (interior) {
-    uint32_t keep[NK];
+    uint32_t d[RW][4];
 #pragma unroll
-    for (int i = 0; i < kBlockLen; ++i) {
-      uint32_t d[4] = {0, 0, 0, 0};
-      if (cvalid) load16(src + i * p.cols, d);
-      uint32_t m = chunk_absmax<T, kCol, kPre>(d, col);
+    for (int i = 0; i < RW; ++i) {
+      d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+      if (cvalid) load16(src + i * p.cols, d[i]);
+    }
+    // lane t of a block group owns rows i0 + t + k*LB of the block's amax_row column
+    T* ar = static_cast<T*>(p.amax_row) + (r0 + i0 + lane % LB) * p.ld_ar + (c >> 5);
+    uint32_t old[NK], keep[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) old[k] = cvalid ? (uint32_t)ar[(int64_t)k * LB * p.ld_ar] : 0u;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      uint32_t m = chunk_absmax<T, kCol, kPre>(d[i], col);
       m = group_max<LB>(m);
       if ((i % LB) == (lane % LB)) keep[i / LB] = m;
     }
-    if (!cvalid) return;
-    // lane t of a block group writes rows t, t + LB, ... of the block's column of amax_row
-    T* ar = static_cast<T*>(p.amax_row) + (r0 + lane % LB) * p.ld_ar + (c >> 5);
-    uint32_t old[NK];
+    if (cvalid) {
 #pragma unroll
-    for (int k = 0; k < NK; ++k) old[k] = ar[(int64_t)k * LB * p.ld_ar];
-#pragma unroll
-    for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)umax(old[k], keep[k]);
+      for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)umax(old[k], keep[k]);
+    }
     if constexpr (kCol) {
-      T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
-      if (p.col_vec) {
-        uint32_t o[4];
-        load16(ac, o);
-        uint4 w;
-        if constexpr (sizeof(T) == 2) {
-          w = make_uint4(pk_max_u16(o[0], col[0]), pk_max_u16(o[1], col[1]),
-                         pk_max_u16(o[2], col[2]), pk_max_u16(o[3], col[3]));
-        } else {
-          w = make_uint4(umax(o[0], col[0]), umax(o[1], col[1]), umax(o[2], col[2]),
-                         umax(o[3], col[3]));
-        }
-        *reinterpret_cast<uint4*>(ac) = w;
-      } else {
+      s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+      __syncthreads();
+      if (wave == 0 && cvalid) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) merge_plain(ac + e, col_entry<T>(col, e));
+        for (int w = 1; w < kWavesPerGroup; ++w) {
+          const uint4 o = s_col[w][lane];
+          const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            col[j] = sizeof(T) == 2 ? pk_max_u16(col[j], ov[j]) : umax(col[j], ov[j]);
+        }
+        T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
+        if (p.col_vec) {
+          uint32_t o[4];
+          load16(ac, o);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            o[j] = sizeof(T) == 2 ? pk_max_u16(o[j], col[j]) : umax(o[j], col[j]);
+          *reinterpret_cast<uint4*>(ac) = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) merge_plain(ac + e, col_entry<T>(col, e));
+        }
       }
     }
     return;
   }
 
-  // Edge tile: the fragment boundary (or the last, short band) cuts it.
-  uint32_t touched = 0;  // bit e: column c + e has an element inside the fragment
-  for (int i = 0; i < nrows; ++i) {
-    const int64_t r = r0 + i;
+  // Edge tile: a fragment boundary, or the short last band, cuts it.
+  uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
+  for (int i = 0; i < RW; ++i) {
+    const int ii = i0 + i;
+    if (ii >= nrows) break;  // uniform over the wave
+    const int64_t r = r0 + ii;
     const int64_t g = r * p.cols + c;
     uint32_t d[4] = {0, 0, 0, 0};
     if (cvalid) {
@@ -356,7 +378,19 @@ __global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
     }
   }
   if constexpr (kCol) {
-    if (cvalid) {
+    s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    s_touch[wave][lane] = touched;
+    __syncthreads();
+    if (wave == 0 && cvalid) {
+#pragma unroll
+      for (int w = 1; w < kWavesPerGroup; ++w) {
+        const uint4 o = s_col[w][lane];
+        const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          col[j] = sizeof(T) == 2 ? pk_max_u16(col[j], ov[j]) : umax(col[j], ov[j]);
+        touched |= s_touch[w][lane];
+      }
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         if (!((touched >> e) & 1u)) continue;
@@ -391,20 +425,33 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t (&d)[4], const int
   }
 }
 
+template <int E>
+__device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q) {
+  if constexpr (E == 8)
+    *reinterpret_cast<uint2*>(p) = make_uint2(q[0], q[1]);
+  else
+    *reinterpret_cast<uint32_t*>(p) = q[0];
+}
+
+// Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
+// with all loads in flight.  No cross-lane work.
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void cast_vec_kernel(TileArgs p) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
+  constexpr int RW = kRowsPerWave;
 
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * WC;
   const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen;
-  if (c >= p.cols) return;  // no cross-lane work in the cast
+  if (c >= p.cols) return;
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int i0 = wave * RW;
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
@@ -415,36 +462,36 @@ __global__ __launch_bounds__(kThreads) void cast_vec_kernel(TileArgs p) {
 #pragma unroll
     for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
   }
-  const T* src = static_cast<const T*>(p.input) + (r0 * p.cols + c - p.start);
-  const uint8_t* srow = p.scale_row + r0 * p.ld_sr + (c >> 5);
-  const int64_t o0 = r0 * p.cols + c - p.start;  // fragment-relative output offset, row 0
+  const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
+  const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
+  const int64_t o0 = (r0 + i0) * p.cols + c - p.start;  // fragment-relative output offset
 
   if (interior) {
-#pragma unroll 4
-    for (int i = 0; i < kBlockLen; ++i) {
-      uint32_t d[4];
-      load16(src + i * p.cols, d);
-      const int rshift = 127 - (int)srow[i * p.ld_sr];
+    uint32_t d[RW][4];
+    int rshift[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      load16(src + i * p.cols, d[i]);
+      rshift[i] = 127 - (int)srow[i * p.ld_sr];
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
       const int64_t o = o0 + i * p.cols;
       uint32_t q[E / 4];
-      quantize_chunk<T, kPre>(d, &rshift, false, q);
-      if constexpr (E == 8)
-        *reinterpret_cast<uint2*>(p.data_row + o) = make_uint2(q[0], q[1]);
-      else
-        *reinterpret_cast<uint32_t*>(p.data_row + o) = q[0];
+      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+      store_bytes<E>(p.data_row + o, q);
       if constexpr (kCol) {
-        quantize_chunk<T, kPre>(d, cshift, true, q);
-        if constexpr (E == 8)
-          *reinterpret_cast<uint2*>(p.data_col + o) = make_uint2(q[0], q[1]);
-        else
-          *reinterpret_cast<uint32_t*>(p.data_col + o) = q[0];
+        quantize_chunk<T, kPre>(d[i], cshift, true, q);
+        store_bytes<E>(p.data_col + o, q);
       }
     }
     return;
   }
 
-  for (int i = 0; i < nrows; ++i) {
-    const int64_t g = (r0 + i) * p.cols + c;
+  for (int i = 0; i < RW; ++i) {
+    const int ii = i0 + i;
+    if (ii >= nrows) break;
+    const int64_t g = (r0 + ii) * p.cols + c;
     if (g + E <= p.start || g >= p.end) continue;
     uint32_t d[4];
     const uint32_t mask = load_masked<T>(p, g, d);
@@ -537,6 +584,8 @@ struct ScaleArgs {
   int64_t ld_sc;
   int64_t r_first, r_last;  // rows the fragment touches
   int64_t b_first, b_last;  // bands the fragment touches
+  int64_t groups_row;       // workgroups of the row-wise part (4 rows each)
+  int64_t col_chunks;       // 256-column chunks per band in the column-wise part
 };
 
 // Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
@@ -558,28 +607,34 @@ __device__ __forceinline__ bool col_block_touched(const ScaleArgs& p, int64_t b,
   return rmin <= r1 && rmin * p.cols + c < p.end;
 }
 
-// grid: x over entries of one row (or band), y over rows (or bands), z = direction.
+// Workgroups [0, groups_row): 4 rows each, one wave per row, lanes across the row's blocks.
+// Workgroups after that: one (band, 256-column chunk) each.  Only the first and last row /
+// band can hold untouched blocks, so only they test block membership.
 template <typename T>
 __global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
-  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (blockIdx.z == 0) {
+  const int64_t w = blockIdx.x;
+  if (w < p.groups_row) {
+    const int64_t r = p.r_first + w * 4 + (threadIdx.x >> 6);
+    if (r > p.r_last) return;
     const int64_t nb = (p.cols + kBlockLen - 1) / kBlockLen;
-    if (x >= nb) return;
-    for (int64_t r = p.r_first + blockIdx.y; r <= p.r_last; r += gridDim.y) {
-      const int64_t gb = r * p.cols + x * kBlockLen;
-      const int64_t ge = min<int64_t>(gb + kBlockLen, (r + 1) * p.cols);
-      if (gb < p.end && ge > p.start)
-        p.scale_row[r * p.ld_sr + x] =
-            e8m0_of<T>(static_cast<const T*>(p.amax_row)[r * p.ld_ar + x]);
+    const bool edge = r == p.r_first || r == p.r_last;
+    const T* a = static_cast<const T*>(p.amax_row) + r * p.ld_ar;
+    uint8_t* s = p.scale_row + r * p.ld_sr;
+    for (int64_t x = threadIdx.x & 63; x < nb; x += 64) {
+      if (edge) {
+        const int64_t gb = r * p.cols + x * kBlockLen;
+        const int64_t ge = min<int64_t>(gb + kBlockLen, (r + 1) * p.cols);
+        if (gb >= p.end || ge <= p.start) continue;
+      }
+      s[x] = e8m0_of<T>(a[x]);
     }
   } else {
-    if (x >= p.cols) return;
-    for (int64_t b = p.b_first + blockIdx.y; b <= p.b_last; b += gridDim.y) {
-      const bool edge = b == p.b_first || b == p.b_last;
-      if (!edge || col_block_touched(p, b, x))
-        p.scale_col[b * p.ld_sc + x] =
-            e8m0_of<T>(static_cast<const T*>(p.amax_col)[b * p.ld_ac + x]);
-    }
+    const int64_t u = w - p.groups_row;
+    const int64_t b = p.b_first + u / p.col_chunks;
+    const int64_t c = (u % p.col_chunks) * 256 + threadIdx.x;
+    if (c >= p.cols) return;
+    if ((b == p.b_first || b == p.b_last) && !col_block_touched(p, b, c)) return;
+    p.scale_col[b * p.ld_sc + c] = e8m0_of<T>(static_cast<const T*>(p.amax_col)[b * p.ld_ac + c]);
   }
 }
 
@@ -655,9 +710,11 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   return a;
 }
 
+// tiles_per_group: 1 for the vector kernels (a workgroup per tile), kWavesPerGroup for the
+// element-wise kernels (a wave per tile).
 template <typename K>
-hipError_t launch_tiles(K kernel, const TileArgs& a, hipStream_t s) {
-  const int64_t groups = cdiv(a.ntiles, kWavesPerGroup);
+hipError_t launch_tiles(K kernel, const TileArgs& a, int tiles_per_group, hipStream_t s) {
+  const int64_t groups = cdiv(a.ntiles, tiles_per_group);
   if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
   return hipGetLastError();
@@ -666,15 +723,19 @@ hipError_t launch_tiles(K kernel, const TileArgs& a, hipStream_t s) {
 template <typename T, bool kCol, bool kPre>
 hipError_t amax_dispatch(const Piece& p, bool vec, hipStream_t s) {
   if (vec)
-    return launch_tiles(amax_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), s);
-  return launch_tiles(amax_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols), s);
+    return launch_tiles(amax_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), 1,
+                        s);
+  return launch_tiles(amax_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols),
+                      kWavesPerGroup, s);
 }
 
 template <typename T, bool kCol, bool kPre>
 hipError_t cast_dispatch(const Piece& p, bool vec, hipStream_t s) {
   if (vec)
-    return launch_tiles(cast_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), s);
-  return launch_tiles(cast_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols), s);
+    return launch_tiles(cast_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), 1,
+                        s);
+  return launch_tiles(cast_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols),
+                      kWavesPerGroup, s);
 }
 
 bool vec_common_ok(const Piece& p) {
@@ -740,12 +801,12 @@ hipError_t launch_compute_scales(const Piece& p, hipStream_t s) {
   a.r_last = (a.end - 1) / p.cols;
   a.b_first = a.r_first / kBlockLen;
   a.b_last = a.r_last / kBlockLen;
-  const int64_t nb = cdiv(p.cols, kBlockLen);
   const bool col = p.amax_col != nullptr;
-  const int64_t width = col ? std::max<int64_t>(nb, p.cols) : nb;
-  const int64_t height = col ? std::max<int64_t>(a.r_last - a.r_first + 1, a.b_last - a.b_first + 1)
-                             : a.r_last - a.r_first + 1;
-  dim3 grid((unsigned)cdiv(width, 256), (unsigned)std::min<int64_t>(height, 65535), col ? 2 : 1);
+  a.groups_row = cdiv(a.r_last - a.r_first + 1, 4);
+  a.col_chunks = cdiv(p.cols, 256);
+  const int64_t groups = a.groups_row + (col ? (a.b_last - a.b_first + 1) * a.col_chunks : 0);
+  if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)groups);
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else

@@ -128,18 +128,39 @@ class Plan:
         self.cast = (B.Piece * len(cast_pieces))(*cast_pieces)
         self.n_amax, self.n_cast = len(amax_pieces), len(cast_pieces)
 
-    def run(self, stream=None):
+    def stages(self, stream=None):
+        """The writeback as (name, callable) stages, in order: zero-fill of the packed amax,
+        partial amax, MAX-combine (only with one packed buffer per fragment), scales, cast."""
         wb = self.wb
         lib = B.lib()
         sp = B._stream(stream)
-        for p in (wb.packed if not wb.shared else wb.packed[:1]):
-            p.buffer.zero_()
-        B._check(lib.mxfp8_partial_amax(self.amax, self.n_amax, sp))
-        if not wb.shared and len(wb.packed) > 1:
+        bufs = wb.packed if not wb.shared else wb.packed[:1]
+
+        def zero():
+            for p in bufs:
+                p.buffer.zero_()
+
+        def amax():
+            B._check(lib.mxfp8_partial_amax(self.amax, self.n_amax, sp))
+
+        def combine():
             B._check(lib.mxfp8_combine_amax(wb.combine_dst, wb.combine_srcs, len(wb.packed),
                                             wb.combined.numel, B.dtype_code(wb.dtype), sp))
-        B._check(lib.mxfp8_compute_scales(wb.scale_pieces, wb.n_scale, sp))
-        B._check(lib.mxfp8_partial_cast(self.cast, self.n_cast, sp))
+
+        def scales():
+            B._check(lib.mxfp8_compute_scales(wb.scale_pieces, wb.n_scale, sp))
+
+        def cast():
+            B._check(lib.mxfp8_partial_cast(self.cast, self.n_cast, sp))
+
+        out = [("zero", zero), ("amax", amax)]
+        if not wb.shared and len(wb.packed) > 1:
+            out.append(("combine", combine))
+        return out + [("scales", scales), ("cast", cast)]
+
+    def run(self, stream=None):
+        for _, fn in self.stages(stream):
+            fn()
 
 
 class Writeback:

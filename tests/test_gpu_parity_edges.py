@@ -392,8 +392,11 @@ def test_many_pieces_of_one_weight_in_one_call_share_an_amax_buffer(dtype):
     tdt = torch_dtype(x)
     ar = torch.zeros(rows, cols // 32, dtype=tdt, device=DEV)
     ac = torch.zeros(rows // 32, cols, dtype=tdt, device=DEV)
-    pieces = [B.make_piece(rows, cols, s, xd[s:s + l] if i % 2 else xd[s:s + l].clone(),
-                           amax_row=ar, amax_col=ac) for i, (s, l) in enumerate(frags)]
+    # odd pieces read views of one buffer, even pieces their own copies (kept alive: a piece
+    # holds raw pointers)
+    inputs = [xd[s:s + l] if i % 2 else xd[s:s + l].clone() for i, (s, l) in enumerate(frags)]
+    pieces = [B.make_piece(rows, cols, s, xi, amax_row=ar, amax_col=ac)
+              for (s, l), xi in zip(frags, inputs)]
     B.mxfp8_partial_amax(pieces)
     torch.cuda.synchronize()
     want = oracle.new_buffers(rows, cols, oracle.dtype_of(x), True)
