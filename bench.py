@@ -5,9 +5,10 @@ contiguous fragments whose boundaries fall inside 32-value blocks (cuts at N/4+1
 3N/4+17), as four ranks would hold it: zero-fill of one packed amax buffer per fragment,
 partial amax of every fragment, MAX-combine of the four buffers, E8M0 scales for the whole
 weight, and the in-place partial cast of every fragment to E4M3 row-wise and column-wise
-data.  Inputs are resident in HBM before timing; each step uses the next of several
-distinct input/output sets (>= 1.2 GB in all), so no step reads what the previous one left
-in the 256 MB Infinity Cache.
+data.  Inputs are resident in HBM before timing.  Steps walk over several distinct weights
+(buffer sets, >= 1.2 GB in all) like a writeback over a model: step i runs the amax side on
+weight i and the cast of weight i - 1, so no kernel reads an input another kernel has just
+left in the 256 MB Infinity Cache.
 
 Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
 ``roofline`` is for the dominant kernel (the partial cast), from HIP events recorded on the
@@ -142,11 +143,16 @@ def main():
     }
     step_bytes = sum(stage_bytes.values())
 
+    # Step i runs zero / amax / combine / scales on buffer set i and the cast of set i - 1,
+    # the weight before it: as in a writeback over many weights, a fragment's cast never
+    # directly follows its own amax, so the cast reads its input from HBM and not from the
+    # Infinity Cache the amax just filled.  Every step still runs every stage once.
     stage_names = [name for name, _ in sets[0][2].stages()]
     stages = [s[2].stages() for s in sets]
 
     def step(i, ev=None):
-        for j, (_, fn) in enumerate(stages[i % n_sets]):
+        seq = stages[i % n_sets][:-1] + [stages[(i - 1) % n_sets][-1]]
+        for j, (_, fn) in enumerate(seq):
             if ev is not None:
                 ev[j].record()
             fn()

@@ -45,6 +45,9 @@ constexpr int kWaveSize = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWaveSize * kWavesPerGroup;
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
+// The vector kernels ask the register allocator for at least 6 resident waves per SIMD
+// (<= 80 VGPRs): the edge-tile path would otherwise inflate every wave's register budget.
+#define MXFP8_OCCUPANCY __attribute__((amdgpu_waves_per_eu(6)))
 
 struct TileArgs {
   int64_t rows, cols, start, end;
@@ -124,30 +127,65 @@ __device__ __forceinline__ void merge_plain(uint16_t* p, uint32_t v) {
 }
 __device__ __forceinline__ void merge_plain(uint32_t* p, uint32_t v) { *p = umax(*p, v); }
 
-__device__ __forceinline__ void merge_atomic(uint32_t* p, uint32_t v) { atomicMax(p, v); }
+// Atomic max into N amax entries at once; bit i of `active` selects entry i.  Amax values are
+// non-negative, so unsigned order on the bit patterns is float order.  FP32 entries use the
+// hardware's unsigned atomic max, which returns nothing to wait for.
+template <int N>
+__device__ __forceinline__ void atomic_max_entries(uint32_t* const (&p)[N],
+                                                   const uint32_t (&v)[N], uint32_t active) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if ((active >> i) & 1u) atomicMax(p[i], v[i]);
+}
 
-// 16-bit atomic max through a compare-and-swap on the aligned 32-bit word holding the entry.
-// Amax values are non-negative, so unsigned order on the bits is float order.
-__device__ __forceinline__ void merge_atomic(uint16_t* p, uint32_t v) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  uint32_t* w = reinterpret_cast<uint32_t*>(a & ~uintptr_t(3));
-  const int sh = (a & 2) ? 16 : 0;
-  uint32_t old = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (((old >> sh) & 0xFFFFu) < v) {
-    const uint32_t nw = (old & ~(0xFFFFu << sh)) | (v << sh);
-    const uint32_t prev = atomicCAS(w, old, nw);
-    if (prev == old) break;
-    old = prev;
+// BF16 entries have no 16-bit atomic max: each goes through a compare-and-swap on the aligned
+// 32-bit word holding it.  All words are read first and all swaps issued together; only swaps
+// that lost a race are retried, with the value they observed.
+template <int N>
+__device__ __forceinline__ void atomic_max_entries(uint16_t* const (&p)[N],
+                                                   const uint32_t (&v)[N], uint32_t active) {
+  uint32_t* w[N];
+  int sh[N];
+  uint32_t old[N];
+  uint32_t pending = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p[i]);
+    w[i] = reinterpret_cast<uint32_t*>(a & ~uintptr_t(3));
+    sh[i] = (a & 2) ? 16 : 0;
+    old[i] = 0;
+    if ((active >> i) & 1u) old[i] = __hip_atomic_load(w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (((active >> i) & 1u) && ((old[i] >> sh[i]) & 0xFFFFu) < v[i]) pending |= 1u << i;
+  while (pending) {
+    uint32_t prev[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((pending >> i) & 1u)
+        prev[i] = atomicCAS(w[i], old[i], (old[i] & ~(0xFFFFu << sh[i])) | (v[i] << sh[i]));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      if (!((pending >> i) & 1u)) continue;
+      if (prev[i] == old[i] || ((prev[i] >> sh[i]) & 0xFFFFu) >= v[i])
+        pending &= ~(1u << i);
+      else
+        old[i] = prev[i];
+    }
   }
 }
 
 template <typename T>
 __device__ __forceinline__ void merge_entry(void* base, int64_t idx, uint32_t v, bool full) {
   T* p = static_cast<T*>(base) + idx;
-  if (full)
+  if (full) {
     merge_plain(p, v);
-  else
-    merge_atomic(p, v);
+  } else {
+    T* const ps[1] = {p};
+    const uint32_t vs[1] = {v};
+    atomic_max_entries<1>(ps, vs, 1u);
+  }
 }
 
 // ------------------------------------------------------------------ per-element working values
@@ -246,6 +284,19 @@ __device__ __forceinline__ void load16(const void* p, uint32_t (&d)[4]) {
   d[3] = v.w;
 }
 
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+
+// The input is streamed once: non-temporal loads (the "nt" cache policy) keep it from
+// displacing reused lines; on MI355X they also lift a pure read stream from ~5.9 to ~6.7 TB/s.
+__device__ __forceinline__ void load16_stream(const void* p, uint32_t (&d)[4]) {
+  const v4u v = __builtin_nontemporal_load(static_cast<const v4u*>(p));
+  d[0] = v.x;
+  d[1] = v.y;
+  d[2] = v.z;
+  d[3] = v.w;
+}
+
 // Chunk whose elements straddle a fragment boundary: load only the fragment's elements.
 template <typename T>
 __device__ __forceinline__ uint32_t load_masked(const TileArgs& p, int64_t g, uint32_t (&d)[4]) {
@@ -267,21 +318,55 @@ __device__ __forceinline__ uint32_t load_masked(const TileArgs& p, int64_t g, ui
   return mask;
 }
 
+// Rows i < nrows_here of an edge tile: chunk i of the wave's rows, masked to the fragment.
+// Every load is issued before any result is used.  Returns per-row element masks in em.
+template <typename T, int RW>
+__device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
+                                                 int nrows_here, int64_t c, bool cvalid,
+                                                 uint32_t (&d)[RW][4], uint32_t (&em)[RW]) {
+  constexpr int E = Chunk<T>::E;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+    em[i] = 0;
+    if (i < nrows_here && cvalid) {
+      const int64_t g = (rfirst + i) * p.cols + c;
+      if (g >= p.start && g + E <= p.end) {
+        load16_stream(src + i * p.cols, d[i]);
+        em[i] = (1u << E) - 1;
+      } else if (g + E > p.start && g < p.end) {
+        em[i] = load_masked<T>(p, g, d[i]);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ partial amax, vector path
 
 constexpr int kRowsPerWave = kBlockLen / kWavesPerGroup;  // 8 rows of the band per wave
 
+template <typename T>
+__device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
+  const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) col[j] = sizeof(T) == 2 ? pk_max_u16(col[j], ov[j]) : umax(col[j], ov[j]);
+}
+
 // A workgroup owns one tile: a 32-row band x 64*E columns.  Wave w streams rows 8w .. 8w+7
 // with all eight 16-byte loads in flight; the four waves' column-wise maxima meet in LDS.
+// Tiles wholly inside the fragment read-max-write their entries (each has a single owner);
+// edge tiles merge every touched entry atomically, since a neighbouring piece may share it.
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void amax_vec_kernel(TileArgs p) {
   constexpr int E = Chunk<T>::E;
   constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block (4 BF16, 8 FP32)
   constexpr int WC = kWaveSize * E;     // tile width in columns
   constexpr int RW = kRowsPerWave;
   constexpr int NK = RW / LB;           // row maxima each lane keeps (2 BF16, 1 FP32)
+  constexpr int NBLK = WC / kBlockLen;  // row-wise blocks across the tile (16 BF16, 8 FP32)
   __shared__ uint4 s_col[kWavesPerGroup][kWaveSize];
   __shared__ uint32_t s_touch[kWavesPerGroup][kWaveSize];
+  __shared__ uint32_t s_rmax[kBlockLen][NBLK];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
@@ -299,14 +384,14 @@ __global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
 
   uint32_t col[4] = {0, 0, 0, 0};
+  uint32_t d[RW][4];
   const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
 
   if (interior) {
-    uint32_t d[RW][4];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-      if (cvalid) load16(src + i * p.cols, d[i]);
+      if (cvalid) load16_stream(src + i * p.cols, d[i]);
     }
     // lane t of a block group owns rows i0 + t + k*LB of the block's amax_row column
     T* ar = static_cast<T*>(p.amax_row) + (r0 + i0 + lane % LB) * p.ld_ar + (c >> 5);
@@ -328,20 +413,12 @@ __global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
       __syncthreads();
       if (wave == 0 && cvalid) {
 #pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) {
-          const uint4 o = s_col[w][lane];
-          const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            col[j] = sizeof(T) == 2 ? pk_max_u16(col[j], ov[j]) : umax(col[j], ov[j]);
-        }
+        for (int w = 1; w < kWavesPerGroup; ++w) fold_col<T>(col, s_col[w][lane]);
         T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
         if (p.col_vec) {
           uint32_t o[4];
           load16(ac, o);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            o[j] = sizeof(T) == 2 ? pk_max_u16(o[j], col[j]) : umax(o[j], col[j]);
+          fold_col<T>(o, make_uint4(col[0], col[1], col[2], col[3]));
           *reinterpret_cast<uint4*>(ac) = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
 #pragma unroll
@@ -352,54 +429,59 @@ __global__ __launch_bounds__(kThreads) void amax_vec_kernel(TileArgs p) {
     return;
   }
 
-  // Edge tile: a fragment boundary, or the short last band, cuts it.
+  // Edge tile: a fragment boundary, or the short last band, cuts it.  Every wave loads its
+  // rows masked to the fragment; the row-wise and column-wise maxima meet in LDS and all 256
+  // threads then merge the touched entries atomically, at most two of each kind per thread.
+  uint32_t em[RW];
+  load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
+#pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const int ii = i0 + i;
-    if (ii >= nrows) break;  // uniform over the wave
-    const int64_t r = r0 + ii;
-    const int64_t g = r * p.cols + c;
-    uint32_t d[4] = {0, 0, 0, 0};
-    if (cvalid) {
-      if (g >= p.start && g + E <= p.end) {
-        load16(src + i * p.cols, d);
-        touched = (1u << E) - 1;
-      } else if (g + E > p.start && g < p.end) {
-        touched |= load_masked<T>(p, g, d);
-      }
+    const uint32_t m = group_max<LB>(chunk_absmax<T, kCol, kPre>(d[i], col));
+    if ((lane % LB) == 0) s_rmax[i0 + i][lane / LB] = m;
+    touched |= em[i];
+  }
+  s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+  s_touch[wave][lane] = touched;
+  __syncthreads();
+  {
+    constexpr int kPer = kBlockLen * NBLK / kThreads;  // row entries per thread (2 or 1)
+    T* ptr[kPer];
+    uint32_t v[kPer], act = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = threadIdx.x + j * kThreads;
+      const int row = e / NBLK, blk = e % NBLK;
+      const int64_t r = r0 + row;
+      const int64_t gb = r * p.cols + c0 + blk * kBlockLen;
+      ptr[j] = static_cast<T*>(p.amax_row) + r * p.ld_ar + (c0 >> 5) + blk;
+      v[j] = s_rmax[row][blk];
+      if (row < nrows && c0 + blk * kBlockLen < p.cols && gb < p.end && gb + kBlockLen > p.start)
+        act |= 1u << j;
     }
-    uint32_t m = chunk_absmax<T, kCol, kPre>(d, col);
-    m = group_max<LB>(m);
-    if (cvalid && (lane % LB) == 0) {
-      const int64_t gb = r * p.cols + (c & ~int64_t(kBlockLen - 1));
-      const int64_t ge = gb + kBlockLen;
-      if (gb < p.end && ge > p.start)
-        merge_entry<T>(p.amax_row, r * p.ld_ar + (c >> 5), m, gb >= p.start && ge <= p.end);
-    }
+    atomic_max_entries<kPer>(ptr, v, act);
   }
   if constexpr (kCol) {
-    s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
-    s_touch[wave][lane] = touched;
-    __syncthreads();
-    if (wave == 0 && cvalid) {
+    constexpr int kPer = WC / kThreads;  // columns per thread (2 or 1)
+    T* ptr[kPer];
+    uint32_t v[kPer], act = 0;
 #pragma unroll
-      for (int w = 1; w < kWavesPerGroup; ++w) {
-        const uint4 o = s_col[w][lane];
+    for (int j = 0; j < kPer; ++j) {
+      const int cc = threadIdx.x + j * kThreads;  // column within the tile
+      const int ln = cc / E, e = cc % E;
+      uint32_t m = 0, t = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerGroup; ++w) {
+        const uint4 o = s_col[w][ln];
         const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          col[j] = sizeof(T) == 2 ? pk_max_u16(col[j], ov[j]) : umax(col[j], ov[j]);
-        touched |= s_touch[w][lane];
+        m = umax(m, col_entry<T>(ov, e));
+        t |= s_touch[w][ln];
       }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (!((touched >> e) & 1u)) continue;
-        const int64_t first = r0 * p.cols + c + e;
-        const int64_t last = (r0 + nrows - 1) * p.cols + c + e;
-        merge_entry<T>(p.amax_col, band * p.ld_ac + c + e, col_entry<T>(col, e),
-                       first >= p.start && last < p.end);
-      }
+      ptr[j] = static_cast<T*>(p.amax_col) + band * p.ld_ac + c0 + cc;
+      v[j] = m;
+      if (c0 + cc < p.cols && ((t >> e) & 1u)) act |= 1u << j;
     }
+    atomic_max_entries<kPer>(ptr, v, act);
   }
 }
 
@@ -425,21 +507,30 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t (&d)[4], const int
   }
 }
 
+// E output bytes of a chunk, streamed out with a non-temporal store.
 template <int E>
 __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q) {
   if constexpr (E == 8)
-    *reinterpret_cast<uint2*>(p) = make_uint2(q[0], q[1]);
+    __builtin_nontemporal_store(v2u{q[0], q[1]}, reinterpret_cast<v2u*>(p));
   else
-    *reinterpret_cast<uint32_t*>(p) = q[0];
+    __builtin_nontemporal_store(q[0], reinterpret_cast<uint32_t*>(p));
+}
+
+template <int E>
+__device__ __forceinline__ void store_masked(uint8_t* p, const uint32_t* q, uint32_t mask) {
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((mask >> e) & 1u) p[e] = (uint8_t)(q[e >> 2] >> ((e & 3) * 8));
 }
 
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.  No cross-lane work.
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) void cast_vec_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void cast_vec_kernel(TileArgs p) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
+  constexpr uint32_t kFull = (1u << E) - 1;
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
@@ -465,46 +556,37 @@ __global__ __launch_bounds__(kThreads) void cast_vec_kernel(TileArgs p) {
   const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
   const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
   const int64_t o0 = (r0 + i0) * p.cols + c - p.start;  // fragment-relative output offset
+  uint32_t d[RW][4], em[RW];
+  int rshift[RW];
 
   if (interior) {
-    uint32_t d[RW][4];
-    int rshift[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      load16(src + i * p.cols, d[i]);
+      load16_stream(src + i * p.cols, d[i]);
       rshift[i] = 127 - (int)srow[i * p.ld_sr];
+      em[i] = kFull;
     }
+  } else {
+    load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, true, d, em);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int64_t o = o0 + i * p.cols;
-      uint32_t q[E / 4];
-      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-      store_bytes<E>(p.data_row + o, q);
-      if constexpr (kCol) {
-        quantize_chunk<T, kPre>(d[i], cshift, true, q);
-        store_bytes<E>(p.data_col + o, q);
-      }
-    }
-    return;
+    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
   }
-
-  for (int i = 0; i < RW; ++i) {
-    const int ii = i0 + i;
-    if (ii >= nrows) break;
-    const int64_t g = (r0 + ii) * p.cols + c;
-    if (g + E <= p.start || g >= p.end) continue;
-    uint32_t d[4];
-    const uint32_t mask = load_masked<T>(p, g, d);
-    const int rshift = 127 - (int)srow[i * p.ld_sr];
-    uint32_t qr[E / 4], qc[E / 4];
-    quantize_chunk<T, kPre>(d, &rshift, false, qr);
-    if constexpr (kCol) quantize_chunk<T, kPre>(d, cshift, true, qc);
-    const int64_t o = o0 + i * p.cols;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (!((mask >> e) & 1u)) continue;
-      p.data_row[o + e] = (uint8_t)(qr[e >> 2] >> ((e & 3) * 8));
-      if constexpr (kCol) p.data_col[o + e] = (uint8_t)(qc[e >> 2] >> ((e & 3) * 8));
+  for (int i = 0; i < RW; ++i) {
+    if (!interior && !em[i]) continue;
+    const int64_t o = o0 + i * p.cols;
+    uint32_t q[E / 4];
+    quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+    if (interior || em[i] == kFull)
+      store_bytes<E>(p.data_row + o, q);
+    else
+      store_masked<E>(p.data_row + o, q, em[i]);
+    if constexpr (kCol) {
+      quantize_chunk<T, kPre>(d[i], cshift, true, q);
+      if (interior || em[i] == kFull)
+        store_bytes<E>(p.data_col + o, q);
+      else
+        store_masked<E>(p.data_col + o, q, em[i]);
     }
   }
 }

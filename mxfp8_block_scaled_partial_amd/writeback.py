@@ -134,11 +134,9 @@ class Plan:
         wb = self.wb
         lib = B.lib()
         sp = B._stream(stream)
-        bufs = wb.packed if not wb.shared else wb.packed[:1]
 
         def zero():
-            for p in bufs:
-                p.buffer.zero_()
+            wb.packed_storage.zero_()
 
         def amax():
             B._check(lib.mxfp8_partial_amax(self.amax, self.n_amax, sp))
@@ -182,7 +180,15 @@ class Writeback:
                 raise ValueError(f"fragment [{s}, {s + l}) outside the batch of {total}")
         self.storage = [MXFP8Storage(s, device) for s in self.specs]
         n_bufs = 1 if shared else max(1, len(self.fragments))
-        self.packed = [PackedAmax(self.specs, dtype, device) for _ in range(n_bufs)]
+        # all packed buffers in one allocation (one zero-fill per update); each starts on a
+        # 16-byte boundary so the combine can move 16-byte vectors
+        entries = PackedAmax(self.specs, dtype, "meta").numel
+        per = -(-entries * torch.tensor([], dtype=dtype).element_size() // 16) * 16
+        per //= torch.tensor([], dtype=dtype).element_size()
+        self.packed_storage = torch.zeros(n_bufs * per, dtype=dtype, device=device)
+        self.packed = [PackedAmax(self.specs, dtype, device,
+                                  self.packed_storage[i * per:i * per + entries])
+                       for i in range(n_bufs)]
         self.combined = self.packed[0]
         import ctypes
         self.combine_dst = self.combined.buffer.data_ptr()
