@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <limits>
+#include <vector>
 
 #include "../../include/mxfp8_partial.h"
 #include "mxfp8_internal.h"
@@ -196,16 +197,17 @@ int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch
     const int st = check_piece(pieces[i], kind, i, &p, &skip);
     if (st) return st;
   }
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<mxfp8::Piece> todo;
+  todo.reserve(n);
   for (int i = 0; i < n; ++i) {
     mxfp8::Piece p;
     bool skip;
     check_piece(pieces[i], kind, i, &p, &skip);
-    if (skip) continue;
-    const hipError_t e = launch(p, s);
-    if (e != hipSuccess)
-      return fail(MXFP8_ERR_HIP, "%s: piece %d: launch failed: %s", fn, i, hipGetErrorString(e));
+    if (!skip) todo.push_back(p);
   }
+  if (todo.empty()) return MXFP8_OK;
+  const hipError_t e = launch(todo.data(), (int)todo.size(), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MXFP8_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return MXFP8_OK;
 }
 

@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "mxfp8_internal.h"
 
@@ -45,9 +46,14 @@ constexpr int kWaveSize = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWaveSize * kWavesPerGroup;
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
-// The vector kernels ask the register allocator for at least 6 resident waves per SIMD
-// (<= 80 VGPRs): the edge-tile path would otherwise inflate every wave's register budget.
-#define MXFP8_OCCUPANCY __attribute__((amdgpu_waves_per_eu(6)))
+// Resident waves per SIMD the register allocator targets in the vector kernels, per kernel and
+// element type (chosen by measurement on MI355X; without a target the edge-tile path inflates
+// every wave's register budget).
+template <typename T>
+struct Occupancy {
+  static constexpr int kAmax = 4;
+  static constexpr int kCast = sizeof(T) == 2 ? 3 : 2;
+};
 
 struct TileArgs {
   int64_t rows, cols, start, end;
@@ -66,6 +72,15 @@ struct TileArgs {
   int64_t ntc;     // tiles per band
   int64_t ntiles;  // bands * ntc
   int32_t col_vec; // amax_col rows are 16-byte aligned: column entries move as 16-byte vectors
+};
+
+// One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
+// numbered piece after piece, first[k] being the first tile of piece k.
+constexpr int kMaxGroup = 16;
+struct GroupArgs {
+  TileArgs piece[kMaxGroup];
+  int64_t first[kMaxGroup + 1];
+  int32_t n;
 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -117,6 +132,13 @@ __device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t nwg) {
   const int64_t xcd = wg % kNumXcd, idx = wg / kNumXcd;
   const int64_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
   return base + idx;
+}
+
+// Piece of a grouped launch that global tile t belongs to (uniform: a scalar loop).
+__device__ __forceinline__ int piece_of(const GroupArgs& g, int64_t t) {
+  int k = 0;
+  while (k + 1 < g.n && t >= g.first[k + 1]) ++k;
+  return k;
 }
 
 // ------------------------------------------------------------------ amax entries
@@ -357,7 +379,8 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // Tiles wholly inside the fragment read-max-write their entries (each has a single owner);
 // edge tiles merge every touched entry atomically, since a neighbouring piece may share it.
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void amax_vec_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kAmax))) void amax_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block (4 BF16, 8 FP32)
   constexpr int WC = kWaveSize * E;     // tile width in columns
@@ -370,7 +393,10 @@ __global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void amax_vec_kernel(Tile
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;  // uniform over the workgroup
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * WC;
@@ -526,7 +552,8 @@ __device__ __forceinline__ void store_masked(uint8_t* p, const uint32_t* q, uint
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.  No cross-lane work.
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void cast_vec_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
@@ -534,7 +561,10 @@ __global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void cast_vec_kernel(Tile
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * WC;
@@ -596,9 +626,12 @@ __global__ __launch_bounds__(kThreads) MXFP8_OCCUPANCY void cast_vec_kernel(Tile
 constexpr int kElemTileCols = kWaveSize;  // one lane per column
 
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) void amax_elem_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t tile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
@@ -631,9 +664,12 @@ __global__ __launch_bounds__(kThreads) void amax_elem_kernel(TileArgs p) {
 }
 
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads) void cast_elem_kernel(TileArgs p) {
+__global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t tile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
@@ -792,38 +828,62 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   return a;
 }
 
-// tiles_per_group: 1 for the vector kernels (a workgroup per tile), kWavesPerGroup for the
-// element-wise kernels (a wave per tile).
+// Launches `kernel` over the tiles of `ps`, kMaxGroup pieces per launch.  tiles_per_wg is 1
+// for the vector kernels (a workgroup per tile) and kWavesPerGroup for the element-wise ones
+// (a wave per tile).
 template <typename K>
-hipError_t launch_tiles(K kernel, const TileArgs& a, int tiles_per_group, hipStream_t s) {
-  const int64_t groups = cdiv(a.ntiles, tiles_per_group);
-  if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-template <typename T, bool kCol, bool kPre>
-hipError_t amax_dispatch(const Piece& p, bool vec, hipStream_t s) {
-  if (vec)
-    return launch_tiles(amax_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), 1,
-                        s);
-  return launch_tiles(amax_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols),
-                      kWavesPerGroup, s);
-}
-
-template <typename T, bool kCol, bool kPre>
-hipError_t cast_dispatch(const Piece& p, bool vec, hipStream_t s) {
-  if (vec)
-    return launch_tiles(cast_vec_kernel<T, kCol, kPre>, tile_args(p, kWaveSize * Chunk<T>::E), 1,
-                        s);
-  return launch_tiles(cast_elem_kernel<T, kCol, kPre>, tile_args(p, kElemTileCols),
-                      kWavesPerGroup, s);
+hipError_t launch_grouped(K kernel, const std::vector<TileArgs>& ps, int tiles_per_wg,
+                          hipStream_t s) {
+  for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
+    GroupArgs g{};
+    g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
+    int64_t total = 0;
+    for (int k = 0; k < g.n; ++k) {
+      g.piece[k] = ps[i0 + k];
+      g.first[k] = total;
+      // element-wise tiles start on a workgroup boundary so each workgroup has one piece
+      total += cdiv(g.piece[k].ntiles, tiles_per_wg) * tiles_per_wg;
+    }
+    g.first[g.n] = total;
+    const int64_t groups = cdiv(total, tiles_per_wg);
+    if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, g);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 bool vec_common_ok(const Piece& p) {
   const int64_t esz = elem_size(p.dtype);
   const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
   return p.cols % kBlockLen == 0 && virt % 16 == 0;
+}
+
+// Pieces of one call, bucketed by kernel specialization: dtype x column-wise x pre-round x
+// vector path.
+struct Buckets {
+  std::vector<TileArgs> b[2][2][2][2];  // [bf16][col][pre][vec]
+};
+
+template <typename T, bool kCol, bool kPre>
+hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
+                              hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (!vec.empty()) e = launch_grouped(amax_vec_kernel<T, kCol, kPre>, vec, 1, s);
+  if (e == hipSuccess && !elem.empty())
+    e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, elem, kWavesPerGroup, s);
+  return e;
+}
+
+template <typename T, bool kCol, bool kPre>
+hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
+                              hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (!vec.empty()) e = launch_grouped(cast_vec_kernel<T, kCol, kPre>, vec, 1, s);
+  if (e == hipSuccess && !elem.empty())
+    e = launch_grouped(cast_elem_kernel<T, kCol, kPre>, elem, kWavesPerGroup, s);
+  return e;
 }
 
 }  // namespace
@@ -839,33 +899,55 @@ bool cast_fast_ok(const Piece& p) {
   return ok(p.data_row) && ok(p.data_col);
 }
 
-hipError_t launch_partial_amax(const Piece& p, hipStream_t s) {
-  const bool vec = amax_fast_ok(p);
-  const bool col = p.amax_col != nullptr;
-  if (p.dtype == kBF16)
-    return col ? amax_dispatch<uint16_t, true, false>(p, vec, s)
-               : amax_dispatch<uint16_t, false, false>(p, vec, s);
-  if (p.preround)
-    return col ? amax_dispatch<uint32_t, true, true>(p, vec, s)
-               : amax_dispatch<uint32_t, false, true>(p, vec, s);
-  return col ? amax_dispatch<uint32_t, true, false>(p, vec, s)
-             : amax_dispatch<uint32_t, false, false>(p, vec, s);
+hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s);
+
+hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
+  Buckets bk;
+  for (int i = 0; i < n; ++i) {
+    const Piece& p = ps[i];
+    const bool vec = amax_fast_ok(p);
+    const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
+    bk.b[p.dtype == kBF16][p.amax_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
+  }
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  run(launch_amax_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
+  run(launch_amax_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
+  run(launch_amax_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
+  run(launch_amax_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
+  run(launch_amax_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
+  run(launch_amax_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
+  return e;
 }
 
-hipError_t launch_partial_cast(const Piece& p, hipStream_t s) {
-  const bool vec = cast_fast_ok(p);
-  const bool col = p.data_col != nullptr;
-  if (p.dtype == kBF16)
-    return col ? cast_dispatch<uint16_t, true, false>(p, vec, s)
-               : cast_dispatch<uint16_t, false, false>(p, vec, s);
-  if (p.preround)
-    return col ? cast_dispatch<uint32_t, true, true>(p, vec, s)
-               : cast_dispatch<uint32_t, false, true>(p, vec, s);
-  return col ? cast_dispatch<uint32_t, true, false>(p, vec, s)
-             : cast_dispatch<uint32_t, false, false>(p, vec, s);
+hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s) {
+  Buckets bk;
+  for (int i = 0; i < n; ++i) {
+    const Piece& p = ps[i];
+    const bool vec = cast_fast_ok(p);
+    const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
+    bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
+  }
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  run(launch_cast_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
+  run(launch_cast_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
+  run(launch_cast_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
+  run(launch_cast_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
+  run(launch_cast_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
+  run(launch_cast_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
+  return e;
 }
 
-hipError_t launch_compute_scales(const Piece& p, hipStream_t s) {
+hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_compute_scales_one(ps[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
   ScaleArgs a{};
   a.rows = p.rows;
   a.cols = p.cols;

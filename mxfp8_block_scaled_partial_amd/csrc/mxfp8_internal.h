@@ -33,9 +33,10 @@ inline int64_t elem_size(int dtype) { return dtype == kBF16 ? 2 : 4; }
 bool amax_fast_ok(const Piece& p);
 bool cast_fast_ok(const Piece& p);
 
-hipError_t launch_partial_amax(const Piece& p, hipStream_t s);
-hipError_t launch_partial_cast(const Piece& p, hipStream_t s);
-hipError_t launch_compute_scales(const Piece& p, hipStream_t s);
+// Pieces sharing a kernel specialization go out in as few launches as possible.
+hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s);
+hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s);
+hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,
                           hipStream_t s);
 
