@@ -212,22 +212,27 @@ def main():
     }
 
     if args.copy_probe:
-        nb = 1 << 30
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
-        b = torch.empty(nb, dtype=torch.uint8, device=dev)
-        for _ in range(3):
+        # a plain device-to-device copy of known size (256 MiB per launch, rotating over four
+        # buffer pairs so it streams from HBM): the achievable read+write ceiling on this machine,
+        # and the kernel the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are calibrated on
+        nb = 256 << 20
+        pairs = [(torch.empty(nb, dtype=torch.uint8, device=dev),
+                  torch.empty(nb, dtype=torch.uint8, device=dev)) for _ in range(4)]
+        for a, b in pairs:
             b.copy_(a)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
         e0.record()
-        for _ in range(10):
+        for i in range(reps):
+            a, b = pairs[i % 4]
             b.copy_(a)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / 10
-        out["copy_probe"] = {"bytes_per_launch": 2 * nb, "us": round(us, 2),
-                             "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
-        del a, b
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        out["copy_probe"] = {"bytes_per_launch": 2 * nb, "read_bytes": nb, "write_bytes": nb,
+                             "us": round(us, 2), "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
+        del pairs
 
     if args.kernel_table:
         out["kernels"] = kernel_table(args, sets if args.dtype == "bf16" else None, m, dev, tdt)
