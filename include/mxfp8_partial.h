@@ -132,10 +132,12 @@ int mxfp8_partial_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
 const char* mxfp8_last_error(void);
 
 /* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast:
- * 1 = the vectorized path (16-byte loads of 32-aligned row segments; needs cols % 32 == 0,
- * input - start aligned to 16 bytes, and for the cast fragment-relative outputs aligned to
- * the chunk's byte count), 0 = the element-wise path for any other layout, negative = the
- * piece fails validation (the status code, negated).  Host-only; launches nothing. */
+ * 1 = the vectorized path (16-byte loads of row segments of whole 32-value blocks, for any
+ * cols % 32 == 0, whatever the alignment of input and outputs), 0 = the element-wise path
+ * (cols % 32 != 0), negative = the piece fails validation (the status code, negated).
+ * Host-only; launches nothing.  The vectorized path may read, never write, up to 15 bytes
+ * before the first and after the last input element, within the same 16-byte-aligned
+ * granule (the same memory page), and ignores them. */
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel);
 
 #ifdef __cplusplus

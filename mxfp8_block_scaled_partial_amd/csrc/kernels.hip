@@ -72,6 +72,8 @@ struct TileArgs {
   int64_t ntc;     // tiles per band
   int64_t ntiles;  // bands * ntc
   int32_t col_vec; // amax_col rows are 16-byte aligned: column entries move as 16-byte vectors
+  int32_t in_shift2;  // BF16 input with input - start at 2 mod 4 bytes: chunks need a 2-byte shift
+  int32_t mo_row, mo_col;  // (data - start) mod 4 of each output: 0 = chunks store directly
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
@@ -306,8 +308,11 @@ __device__ __forceinline__ void load16(const void* p, uint32_t (&d)[4]) {
   d[3] = v.w;
 }
 
-typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+// Vector types that need only dword alignment: for accesses of a dword or more the hardware
+// ignores the two low address bits, so a 16-byte load from any 4-byte-aligned address is one
+// global_load_dwordx4 (a fragment's chunks are 16-byte aligned only when input - start is).
+typedef unsigned int v4u __attribute__((ext_vector_type(4), aligned(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2), aligned(4)));
 
 // The input is streamed once: non-temporal loads (the "nt" cache policy) keep it from
 // displacing reused lines; on MI355X they also lift a pure read stream from ~5.9 to ~6.7 TB/s.
@@ -317,6 +322,26 @@ __device__ __forceinline__ void load16_stream(const void* p, uint32_t (&d)[4]) {
   d[1] = v.y;
   d[2] = v.z;
   d[3] = v.w;
+}
+
+// The 16 bytes at p, p 2 bytes past a dword boundary (BF16 input whose input - start sits at
+// 2 mod 4): the dword-aligned 16 bytes before it plus the next dword, shifted by 2 bytes.  The
+// extra 2 bytes on each side lie in the same dwords as the chunk's first and last element.
+__device__ __forceinline__ void load16_stream_shift2(const void* p, uint32_t (&d)[4]) {
+  const uint8_t* b = static_cast<const uint8_t*>(p) - 2;
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(b));
+  const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 16));
+  d[0] = __builtin_amdgcn_alignbyte(v.y, v.x, 2);
+  d[1] = __builtin_amdgcn_alignbyte(v.z, v.y, 2);
+  d[2] = __builtin_amdgcn_alignbyte(v.w, v.z, 2);
+  d[3] = __builtin_amdgcn_alignbyte(t, v.w, 2);
+}
+
+__device__ __forceinline__ void load_chunk(const void* p, bool shift2, uint32_t (&d)[4]) {
+  if (shift2)
+    load16_stream_shift2(p, d);
+  else
+    load16_stream(p, d);
 }
 
 // Chunk whose elements straddle a fragment boundary: load only the fragment's elements.
@@ -354,7 +379,7 @@ __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src
     if (i < nrows_here && cvalid) {
       const int64_t g = (rfirst + i) * p.cols + c;
       if (g >= p.start && g + E <= p.end) {
-        load16_stream(src + i * p.cols, d[i]);
+        load_chunk(src + i * p.cols, p.in_shift2, d[i]);
         em[i] = (1u << E) - 1;
       } else if (g + E > p.start && g < p.end) {
         em[i] = load_masked<T>(p, g, d[i]);
@@ -415,9 +440,15 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kAmax))) void amax_vec_kernel(G
 
   if (interior) {
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-      if (cvalid) load16_stream(src + i * p.cols, d[i]);
+    for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+    if (cvalid) {
+      if (p.in_shift2) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
+      }
     }
     // lane t of a block group owns rows i0 + t + k*LB of the block's amax_row column
     T* ar = static_cast<T*>(p.amax_row) + (r0 + i0 + lane % LB) * p.ld_ar + (c >> 5);
@@ -533,7 +564,7 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t (&d)[4], const int
   }
 }
 
-// E output bytes of a chunk, streamed out with a non-temporal store.
+// E output bytes of a chunk, streamed out with a non-temporal store (p 4-byte aligned).
 template <int E>
 __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q) {
   if constexpr (E == 8)
@@ -549,8 +580,41 @@ __device__ __forceinline__ void store_masked(uint8_t* p, const uint32_t* q, uint
     if ((mask >> e) & 1u) p[e] = (uint8_t)(q[e >> 2] >> ((e & 3) * 8));
 }
 
+// Chunk outputs at p, mo = p mod 4 != 0 (fragment-relative outputs not dword aligned).  Each
+// lane writes the dword-aligned window [p - mo, p - mo + E): the last mo bytes of the lane to
+// its left (same row, contiguous in memory) and its own first E - mo bytes.  The first lane of
+// a row segment writes its own first E - mo bytes one by one instead (the window's head belongs
+// to another workgroup), and the last lane adds its trailing mo bytes.  Every lane of the wave
+// must call this (it exchanges registers with __shfl_up).
+template <int E>
+__device__ __forceinline__ void store_window(uint8_t* p, const uint32_t* q, int mo, bool valid,
+                                             bool first, bool last) {
+  uint32_t prev[E / 4];
+#pragma unroll
+  for (int j = 0; j < E / 4; ++j) prev[j] = (uint32_t)__shfl_up((int)q[j], 1);
+  if (!valid) return;
+  const int sh = 8 * mo;
+  if (!first) {
+    uint32_t w[E / 4];
+    // window bytes = bytes [E - mo, 2E - mo) of prev || own, little-endian
+    if constexpr (E == 8) {
+      const uint64_t own = ((uint64_t)q[1] << 32) | q[0];
+      const uint64_t pv = ((uint64_t)prev[1] << 32) | prev[0];
+      const uint64_t win = (own << sh) | (pv >> (64 - sh));
+      w[0] = (uint32_t)win;
+      w[1] = (uint32_t)(win >> 32);
+    } else {
+      w[0] = (q[0] << sh) | (prev[0] >> (32 - sh));
+    }
+    store_bytes<E>(p - mo, w);
+  } else {
+    store_masked<E>(p, q, (1u << (E - mo)) - 1);
+  }
+  if (last) store_masked<E>(p, q, ((1u << E) - 1) & ~((1u << (E - mo)) - 1));
+}
+
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
-// with all loads in flight.  No cross-lane work.
+// with all loads in flight.
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(GroupArgs ga) {
@@ -565,23 +629,30 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(G
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
-  if (tile >= p.ntiles) return;
+  if (tile >= p.ntiles) return;  // uniform over the workgroup
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * WC;
   const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen;
-  if (c >= p.cols) return;
+  const bool cvalid = c < p.cols;
+  const int64_t cend = min<int64_t>(c0 + WC, p.cols);  // one past the tile's last column
+  const bool first = lane == 0, last = c + E == cend;
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
   const int i0 = wave * RW;
   const int64_t tile_first = r0 * p.cols + c0;
-  const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
+  const int64_t tile_end = (r0 + nrows - 1) * p.cols + cend;
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+  const bool aligned_out = p.mo_row == 0 && p.mo_col == 0;
 
   int cshift[E];
   if constexpr (kCol) {
-    const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
 #pragma unroll
-    for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+    for (int e = 0; e < E; ++e) cshift[e] = 0;
+    if (cvalid) {
+      const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+    }
   }
   const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
   const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
@@ -592,28 +663,76 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(G
   if (interior) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      load16_stream(src + i * p.cols, d[i]);
-      rshift[i] = 127 - (int)srow[i * p.ld_sr];
-      em[i] = kFull;
+      d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+      rshift[i] = 0;
+      em[i] = cvalid ? kFull : 0u;
+    }
+    if (cvalid) {
+      if (p.in_shift2) {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
     }
   } else {
-    load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, true, d, em);
+    load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
 #pragma unroll
     for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
   }
+
+  if (interior && aligned_out) {
+    if (!cvalid) return;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int64_t o = o0 + i * p.cols;
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+      store_bytes<E>(p.data_row + o, q);
+      if constexpr (kCol) {
+        quantize_chunk<T, kPre>(d[i], cshift, true, q);
+        store_bytes<E>(p.data_col + o, q);
+      }
+    }
+    return;
+  }
+  if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int64_t o = o0 + i * p.cols;
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+      if (p.mo_row)
+        store_window<E>(p.data_row + o, q, p.mo_row, cvalid, first, last);
+      else if (cvalid)
+        store_bytes<E>(p.data_row + o, q);
+      if constexpr (kCol) {
+        quantize_chunk<T, kPre>(d[i], cshift, true, q);
+        if (p.mo_col)
+          store_window<E>(p.data_col + o, q, p.mo_col, cvalid, first, last);
+        else if (cvalid)
+          store_bytes<E>(p.data_col + o, q);
+      }
+    }
+    return;
+  }
+  // edge tile: full chunks store whole when the outputs are dword aligned, else byte by byte
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    if (!interior && !em[i]) continue;
+    if (!em[i]) continue;
     const int64_t o = o0 + i * p.cols;
     uint32_t q[E / 4];
     quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-    if (interior || em[i] == kFull)
+    if (em[i] == kFull && p.mo_row == 0)
       store_bytes<E>(p.data_row + o, q);
     else
       store_masked<E>(p.data_row + o, q, em[i]);
     if constexpr (kCol) {
       quantize_chunk<T, kPre>(d[i], cshift, true, q);
-      if (interior || em[i] == kFull)
+      if (em[i] == kFull && p.mo_col == 0)
         store_bytes<E>(p.data_col + o, q);
       else
         store_masked<E>(p.data_col + o, q, em[i]);
@@ -702,8 +821,11 @@ struct ScaleArgs {
   int64_t ld_sc;
   int64_t r_first, r_last;  // rows the fragment touches
   int64_t b_first, b_last;  // bands the fragment touches
-  int64_t groups_row;       // workgroups of the row-wise part (4 rows each)
-  int64_t col_chunks;       // 256-column chunks per band in the column-wise part
+  uint32_t items_row;        // 8-entry items per row (row-wise part)
+  uint32_t items_row_total;  // items of the row-wise part
+  uint32_t items_col;        // 8-entry items per band (column-wise part)
+  uint32_t items_col_total;  // items of the column-wise part (0 when absent)
+  int32_t row_vec, col_vec;  // rows of amax / scales aligned for 16-byte / 8-byte vectors
 };
 
 // Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
@@ -725,34 +847,75 @@ __device__ __forceinline__ bool col_block_touched(const ScaleArgs& p, int64_t b,
   return rmin <= r1 && rmin * p.cols + c < p.end;
 }
 
-// Workgroups [0, groups_row): 4 rows each, one wave per row, lanes across the row's blocks.
-// Workgroups after that: one (band, 256-column chunk) each.  Only the first and last row /
-// band can hold untouched blocks, so only they test block membership.
+// One thread per 8 consecutive entries of a row (row-wise part) or of a band (column-wise
+// part).  Rows and bands strictly between the fragment's first and last are wholly touched
+// and, when aligned, move as one 16-byte (BF16) or two 16-byte (FP32) amax loads and one
+// 8-byte scale store; the first and last row / band test each entry's block membership.
+template <typename T>
+__device__ __forceinline__ void scale_segment(const T* a, uint8_t* s, int64_t x0, int64_t width,
+                                              bool vec) {
+  if (vec && x0 + 8 <= width) {
+    uint32_t w[8];
+    if constexpr (sizeof(T) == 2) {
+      uint32_t d[4];
+      load16(a + x0, d);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) w[j] = (d[j >> 1] >> ((j & 1) * 16)) & 0xFFFFu;
+    } else {
+      uint32_t d0[4], d1[4];
+      load16(a + x0, d0);
+      load16(a + x0 + 4, d1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        w[j] = d0[j];
+        w[j + 4] = d1[j];
+      }
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lo |= (uint32_t)e8m0_of<T>(w[j]) << (8 * j);
+      hi |= (uint32_t)e8m0_of<T>(w[j + 4]) << (8 * j);
+    }
+    *reinterpret_cast<uint2*>(s + x0) = make_uint2(lo, hi);
+  } else {
+    for (int64_t x = x0; x < min<int64_t>(x0 + 8, width); ++x) s[x] = e8m0_of<T>(a[x]);
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
-  const int64_t w = blockIdx.x;
-  if (w < p.groups_row) {
-    const int64_t r = p.r_first + w * 4 + (threadIdx.x >> 6);
-    if (r > p.r_last) return;
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < p.items_row_total) {
+    const uint32_t rr = i / p.items_row;
+    const int64_t r = p.r_first + rr;
+    const int64_t x0 = (int64_t)(i - rr * p.items_row) * 8;
     const int64_t nb = (p.cols + kBlockLen - 1) / kBlockLen;
-    const bool edge = r == p.r_first || r == p.r_last;
     const T* a = static_cast<const T*>(p.amax_row) + r * p.ld_ar;
     uint8_t* s = p.scale_row + r * p.ld_sr;
-    for (int64_t x = threadIdx.x & 63; x < nb; x += 64) {
-      if (edge) {
+    if (r == p.r_first || r == p.r_last) {
+      for (int64_t x = x0; x < min<int64_t>(x0 + 8, nb); ++x) {
         const int64_t gb = r * p.cols + x * kBlockLen;
         const int64_t ge = min<int64_t>(gb + kBlockLen, (r + 1) * p.cols);
-        if (gb >= p.end || ge <= p.start) continue;
+        if (gb < p.end && ge > p.start) s[x] = e8m0_of<T>(a[x]);
       }
-      s[x] = e8m0_of<T>(a[x]);
+    } else {
+      scale_segment<T>(a, s, x0, nb, p.row_vec);
     }
+    return;
+  }
+  const uint32_t j = i - p.items_row_total;
+  if (j >= p.items_col_total) return;
+  const uint32_t bb = j / p.items_col;
+  const int64_t b = p.b_first + bb;
+  const int64_t x0 = (int64_t)(j - bb * p.items_col) * 8;
+  const T* a = static_cast<const T*>(p.amax_col) + b * p.ld_ac;
+  uint8_t* s = p.scale_col + b * p.ld_sc;
+  if (b == p.b_first || b == p.b_last) {
+    for (int64_t c = x0; c < min<int64_t>(x0 + 8, p.cols); ++c)
+      if (col_block_touched(p, b, c)) s[c] = e8m0_of<T>(a[c]);
   } else {
-    const int64_t u = w - p.groups_row;
-    const int64_t b = p.b_first + u / p.col_chunks;
-    const int64_t c = (u % p.col_chunks) * 256 + threadIdx.x;
-    if (c >= p.cols) return;
-    if ((b == p.b_first || b == p.b_last) && !col_block_touched(p, b, c)) return;
-    p.scale_col[b * p.ld_sc + c] = e8m0_of<T>(static_cast<const T*>(p.amax_col)[b * p.ld_ac + c]);
+    scale_segment<T>(a, s, x0, p.cols, p.col_vec);
   }
 }
 
@@ -825,6 +988,13 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   const int64_t esz = elem_size(p.dtype);
   a.col_vec = p.amax_col && (reinterpret_cast<uintptr_t>(p.amax_col) % 16 == 0) &&
               ((p.ld_ac * esz) % 16 == 0);
+  const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
+  a.in_shift2 = (virt % 4) == 2;
+  auto mis = [&](const uint8_t* d) {
+    return d ? (int32_t)((reinterpret_cast<uintptr_t>(d) - (uintptr_t)p.start) % 4) : 0;
+  };
+  a.mo_row = mis(p.data_row);
+  a.mo_col = mis(p.data_col);
   return a;
 }
 
@@ -854,11 +1024,10 @@ hipError_t launch_grouped(K kernel, const std::vector<TileArgs>& ps, int tiles_p
   return hipSuccess;
 }
 
-bool vec_common_ok(const Piece& p) {
-  const int64_t esz = elem_size(p.dtype);
-  const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
-  return p.cols % kBlockLen == 0 && virt % 16 == 0;
-}
+// The vector kernels take any fragment of a weight whose rows are whole 32-value blocks: the
+// input needs only its element alignment (dword loads, plus a 2-byte shift for BF16 at 2 mod
+// 4), and outputs at any byte offset are written through aligned windows.
+bool vec_common_ok(const Piece& p) { return p.cols % kBlockLen == 0; }
 
 // Pieces of one call, bucketed by kernel specialization: dtype x column-wise x pre-round x
 // vector path.
@@ -890,14 +1059,7 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
 
 bool amax_fast_ok(const Piece& p) { return vec_common_ok(p); }
 
-bool cast_fast_ok(const Piece& p) {
-  if (!vec_common_ok(p)) return false;
-  const uintptr_t e = (uintptr_t)(16 / elem_size(p.dtype));  // output bytes per chunk
-  auto ok = [&](const uint8_t* d) {
-    return d == nullptr || (reinterpret_cast<uintptr_t>(d) - (uintptr_t)p.start) % e == 0;
-  };
-  return ok(p.data_row) && ok(p.data_col);
-}
+bool cast_fast_ok(const Piece& p) { return vec_common_ok(p); }
 
 hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s);
 
@@ -966,11 +1128,22 @@ hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
   a.b_first = a.r_first / kBlockLen;
   a.b_last = a.r_last / kBlockLen;
   const bool col = p.amax_col != nullptr;
-  a.groups_row = cdiv(a.r_last - a.r_first + 1, 4);
-  a.col_chunks = cdiv(p.cols, 256);
-  const int64_t groups = a.groups_row + (col ? (a.b_last - a.b_first + 1) * a.col_chunks : 0);
-  if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)groups);
+  const int64_t esz = elem_size(p.dtype);
+  const int64_t nb = cdiv(p.cols, kBlockLen);
+  const int64_t items_row = cdiv(nb, 8), items_col = cdiv(p.cols, 8);
+  const int64_t total_row = (a.r_last - a.r_first + 1) * items_row;
+  const int64_t total_col = col ? (a.b_last - a.b_first + 1) * items_col : 0;
+  if (total_row + total_col + 255 > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;
+  a.items_row = (uint32_t)items_row;
+  a.items_row_total = (uint32_t)total_row;
+  a.items_col = (uint32_t)items_col;
+  a.items_col_total = (uint32_t)total_col;
+  auto aligned = [](const void* q, int64_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
+  a.row_vec = aligned(p.amax_row, 16) && (p.ld_ar * esz) % 16 == 0 && aligned(p.scale_row, 8) &&
+              p.ld_sr % 8 == 0;
+  a.col_vec = col && aligned(p.amax_col, 16) && (p.ld_ac * esz) % 16 == 0 &&
+              aligned(p.scale_col, 8) && p.ld_sc % 8 == 0;
+  const dim3 grid((unsigned)cdiv(total_row + total_col, 256));
   if (p.dtype == kBF16)
     hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
   else

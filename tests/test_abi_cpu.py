@@ -165,19 +165,18 @@ def test_combine_validation():
     assert L.mxfp8_combine_amax(BASE + 0x3000000, nul, 2, 16, B.BF16, None) == B.ERR_MISSING
 
 
-def test_query_path_selects_vector_kernel_only_for_aligned_layouts():
+def test_query_path_selects_vector_kernel_for_whole_block_rows():
     q = B.mxfp8_query_path
     assert q(raw_piece(), 0) == 1 and q(raw_piece(), 1) == 1
-    # start 17 with input = base + 17 elements: virtual base aligned -> vector path
+    # any alignment of input and outputs stays on the vector path when cols % 32 == 0
     assert q(raw_piece(start=17, length=100, input=BASE + 34,
                        data_row=BASE + 0x50000000 + 17, data_col=BASE + 0x60000000 + 17), 1) == 1
-    # a fragment held in its own (aligned) buffer: shifted by 17 elements -> element path
-    assert q(raw_piece(start=17, length=100), 0) == 0
-    # ragged width -> element path
-    assert q(raw_piece(rows=40, cols=40), 0) == 0
-    # fragment-relative outputs misaligned for the cast only
+    assert q(raw_piece(start=17, length=100), 0) == 1
     p = raw_piece(start=32, length=64, input=BASE + 64, data_row=BASE + 0x50000000 + 3)
-    assert q(p, 0) == 1 and q(p, 1) == 0
+    assert q(p, 0) == 1 and q(p, 1) == 1
+    # rows that are not whole 32-value blocks -> element-wise path
+    assert q(raw_piece(rows=40, cols=40), 0) == 0
+    assert q(raw_piece(rows=40, cols=40), 1) == 0
     assert q(raw_piece(rows=0), 0) == -B.ERR_ARG
     assert q(raw_piece(), 5) == -B.ERR_ARG
 

@@ -82,9 +82,13 @@ def test_vector_and_element_paths_are_both_exercised():
     x = torch.zeros(64 * 64, dtype=torch.bfloat16, device=DEV)
     ar = torch.zeros(64, 2, dtype=torch.bfloat16, device=DEV)
     p_view = B.make_piece(64, 64, 17, x[17:117], amax_row=ar)
-    p_own = B.make_piece(64, 64, 17, x[17:117].clone(), amax_row=ar)
+    own = x[17:117].clone()                     # input - start at 2 mod 4: shifted loads
+    p_own = B.make_piece(64, 64, 17, own, amax_row=ar)
     assert B.mxfp8_query_path(p_view, 0) == 1
-    assert B.mxfp8_query_path(p_own, 0) == 0
+    assert B.mxfp8_query_path(p_own, 0) == 1
+    y = torch.zeros(40 * 40, dtype=torch.bfloat16, device=DEV)
+    ar40 = torch.zeros(40, 2, dtype=torch.bfloat16, device=DEV)
+    assert B.mxfp8_query_path(B.make_piece(40, 40, 0, y, amax_row=ar40), 0) == 0
 
 
 # ------------------------------------------------------------------ padded leading dimensions
@@ -329,23 +333,32 @@ def test_bytes_outside_the_fragment_are_untouched(inputs):
     assert not first_mismatch(gc[s:s + l], o["data_col"][s:s + l])
 
 
-def test_fragment_sized_outputs():
-    """FSDP-style outputs: the data buffers hold only the fragment (misaligned relative to
-    the block grid), written through the element-wise cast."""
-    rows, cols = 64, 128
-    x = wl.random_matrix(rows, cols, "fp32", seed=13, kind="mixed")
-    s, l = 17, 5000
-    o = oracle.writeback(x, rows, cols, [(s, l)])
-    xd = to_dev(x)
-    dr = torch.zeros(l, dtype=torch.uint8, device=DEV)
-    dc = torch.zeros(l, dtype=torch.uint8, device=DEV)
-    p = B.make_piece(rows, cols, s, xd[s:s + l], scale_row=to_dev_u8(o["scale_row"]),
-                     scale_col=to_dev_u8(o["scale_col"]), data_row=dr, data_col=dc)
-    assert B.mxfp8_query_path(p, 1) == 0
-    B.mxfp8_partial_cast(p)
-    torch.cuda.synchronize()
-    assert not first_mismatch(to_np(dr), o["data_row"][s:s + l])
-    assert not first_mismatch(to_np(dc), o["data_col"][s:s + l])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("start", [17, 18, 19, 20, 5, 1030])
+@pytest.mark.parametrize("cols", [128, 1088])
+def test_fragment_sized_outputs(dtype, start, cols):
+    """FSDP-style outputs: the data buffers hold only the fragment, so they sit at any byte
+    offset from the block grid (window stores), and the input is the rank's own buffer
+    (shifted loads for BF16); several tiles per row, a partial last tile, edge tiles."""
+    rows = 96
+    x = wl.random_matrix(rows, cols, dtype, seed=13 + start, kind="mixed")
+    l = rows * cols - start - 300
+    o = oracle.writeback(x, rows, cols, [(start, l)])
+    xs = to_dev(x)[start:start + l].clone()
+    for pad in (0, 1, 2, 3):  # output buffer offset from an aligned allocation
+        drb = torch.full((l + 8,), 0xA5, dtype=torch.uint8, device=DEV)
+        dcb = torch.full((l + 8,), 0xA5, dtype=torch.uint8, device=DEV)
+        dr, dc = drb[pad:pad + l], dcb[pad:pad + l]
+        p = B.make_piece(rows, cols, start, xs, scale_row=to_dev_u8(o["scale_row"]),
+                         scale_col=to_dev_u8(o["scale_col"]), data_row=dr, data_col=dc)
+        assert B.mxfp8_query_path(p, 1) == 1
+        B.mxfp8_partial_cast(p)
+        torch.cuda.synchronize()
+        gr, gc = to_np(drb), to_np(dcb)
+        assert not first_mismatch(gr[pad:pad + l], o["data_row"][start:start + l]), pad
+        assert not first_mismatch(gc[pad:pad + l], o["data_col"][start:start + l]), pad
+        assert (gr[:pad] == 0xA5).all() and (gr[pad + l:] == 0xA5).all()
+        assert (gc[:pad] == 0xA5).all() and (gc[pad + l:] == 0xA5).all()
 
 
 # ------------------------------------------------------------------ updates, pointers, determinism
