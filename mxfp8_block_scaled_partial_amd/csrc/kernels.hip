@@ -72,6 +72,7 @@ struct TileArgs {
   int64_t ntc;     // tiles per band
   int64_t ntiles;  // bands * ntc
   int32_t col_vec; // amax_col rows are 16-byte aligned: column entries move as 16-byte vectors
+  int32_t row_vec;  // amax_row rows are 16-byte aligned: a tile's row entries move as vectors
   int32_t in_shift2;  // BF16 input with input - start at 2 mod 4 bytes: chunks need a 2-byte shift
   int32_t mo_row, mo_col;  // (data - start) mod 4 of each output: 0 = chunks store directly
 };
@@ -450,33 +451,64 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kAmax))) void amax_vec_kernel(G
         for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
       }
     }
-    // lane t of a block group owns rows i0 + t + k*LB of the block's amax_row column
+    // Entries of the tile: 32 rows x NBLK row-wise blocks (32 bytes per row) and 64*E
+    // column-wise blocks.  Their old values are fetched together with the input so that no
+    // memory latency remains after the reduction; wave 1 then writes the row-wise entries as
+    // one 16-byte vector per lane (row lane/2, half lane%2) while wave 0 merges the
+    // column-wise ones.  Tiles whose rows are not 16-byte aligned in amax_row, or that run
+    // past the last column, let every block's owner lanes write their entries one by one.
+    constexpr int EPV = 16 / (int)sizeof(T);  // entries per 16-byte vector (NBLK = 2 * EPV)
+    const bool rvec = p.row_vec && c0 + WC <= p.cols;  // uniform
     T* ar = static_cast<T*>(p.amax_row) + (r0 + i0 + lane % LB) * p.ld_ar + (c >> 5);
-    uint32_t old[NK], keep[NK];
+    T* arv = static_cast<T*>(p.amax_row) + (r0 + (lane >> 1)) * p.ld_ar + (c0 >> 5) +
+             (lane & 1) * EPV;
+    T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
+    uint32_t old[NK], keep[NK], orow[4] = {0, 0, 0, 0}, ocol[4] = {0, 0, 0, 0};
+    if (rvec) {
+      if (wave == 1) load16(arv, orow);
+    } else {
 #pragma unroll
-    for (int k = 0; k < NK; ++k) old[k] = cvalid ? (uint32_t)ar[(int64_t)k * LB * p.ld_ar] : 0u;
+      for (int k = 0; k < NK; ++k) old[k] = cvalid ? (uint32_t)ar[(int64_t)k * LB * p.ld_ar] : 0u;
+    }
+    if constexpr (kCol) {
+      if (wave == 0 && cvalid && p.col_vec) load16(ac, ocol);
+    }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       uint32_t m = chunk_absmax<T, kCol, kPre>(d[i], col);
       m = group_max<LB>(m);
-      if ((i % LB) == (lane % LB)) keep[i / LB] = m;
+      if (rvec) {
+        if ((lane % LB) == 0) s_rmax[i0 + i][lane / LB] = m;
+      } else if ((i % LB) == (lane % LB)) {
+        keep[i / LB] = m;
+      }
     }
-    if (cvalid) {
+    if (!rvec && cvalid) {
 #pragma unroll
       for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)umax(old[k], keep[k]);
     }
+    if constexpr (kCol) s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    if (rvec || kCol) __syncthreads();
+    if (rvec && wave == 1) {
+      uint32_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 2)
+          v[j] = s_rmax[lane >> 1][(lane & 1) * EPV + 2 * j] |
+                 (s_rmax[lane >> 1][(lane & 1) * EPV + 2 * j + 1] << 16);
+        else
+          v[j] = s_rmax[lane >> 1][(lane & 1) * EPV + j];
+      }
+      fold_col<T>(orow, make_uint4(v[0], v[1], v[2], v[3]));
+      *reinterpret_cast<uint4*>(arv) = make_uint4(orow[0], orow[1], orow[2], orow[3]);
+    }
     if constexpr (kCol) {
-      s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
-      __syncthreads();
       if (wave == 0 && cvalid) {
 #pragma unroll
         for (int w = 1; w < kWavesPerGroup; ++w) fold_col<T>(col, s_col[w][lane]);
-        T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
         if (p.col_vec) {
-          uint32_t o[4];
-          load16(ac, o);
-          fold_col<T>(o, make_uint4(col[0], col[1], col[2], col[3]));
-          *reinterpret_cast<uint4*>(ac) = make_uint4(o[0], o[1], o[2], o[3]);
+          fold_col<T>(ocol, make_uint4(col[0], col[1], col[2], col[3]));
+          *reinterpret_cast<uint4*>(ac) = make_uint4(ocol[0], ocol[1], ocol[2], ocol[3]);
         } else {
 #pragma unroll
           for (int e = 0; e < E; ++e) merge_plain(ac + e, col_entry<T>(col, e));
@@ -988,6 +1020,8 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   const int64_t esz = elem_size(p.dtype);
   a.col_vec = p.amax_col && (reinterpret_cast<uintptr_t>(p.amax_col) % 16 == 0) &&
               ((p.ld_ac * esz) % 16 == 0);
+  a.row_vec = p.amax_row && (reinterpret_cast<uintptr_t>(p.amax_row) % 16 == 0) &&
+              ((p.ld_ar * esz) % 16 == 0);
   const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
   a.in_shift2 = (virt % 4) == 2;
   auto mis = [&](const uint8_t* d) {
