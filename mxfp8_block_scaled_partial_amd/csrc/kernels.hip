@@ -645,92 +645,39 @@ __device__ __forceinline__ void store_window(uint8_t* p, const uint32_t* q, int 
   if (last) store_masked<E>(p, q, ((1u << E) - 1) & ~((1u << (E - mo)) - 1));
 }
 
-// Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
-// with all loads in flight.
+// Tiles a fragment boundary or the short last band cuts, and tiles whose outputs are not
+// dword aligned: masked loads, byte stores or window stores.  The common tile (interior,
+// dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.
 template <typename T, bool kCol, bool kPre>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(GroupArgs ga) {
+__device__ __forceinline__ void cast_tile_general(
+    const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows, bool interior,
+    const int* cshift) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
   constexpr uint32_t kFull = (1u << E) - 1;
-
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = threadIdx.x >> 6;
-  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
-  const int k = piece_of(ga, gtile);
-  const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
-  if (tile >= p.ntiles) return;  // uniform over the workgroup
-  const int64_t band = p.band0 + tile / p.ntc;
-  const int64_t c0 = (tile % p.ntc) * WC;
-  const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen;
   const bool cvalid = c < p.cols;
-  const int64_t cend = min<int64_t>(c0 + WC, p.cols);  // one past the tile's last column
+  const int64_t cend = min<int64_t>(c0 + WC, p.cols);
   const bool first = lane == 0, last = c + E == cend;
-  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
-  const int i0 = wave * RW;
-  const int64_t tile_first = r0 * p.cols + c0;
-  const int64_t tile_end = (r0 + nrows - 1) * p.cols + cend;
-  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
-  const bool aligned_out = p.mo_row == 0 && p.mo_col == 0;
-
-  int cshift[E];
-  if constexpr (kCol) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) cshift[e] = 0;
-    if (cvalid) {
-      const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
-#pragma unroll
-      for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
-    }
-  }
   const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
   const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
-  const int64_t o0 = (r0 + i0) * p.cols + c - p.start;  // fragment-relative output offset
+  const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
   uint32_t d[RW][4], em[RW];
   int rshift[RW];
-
   if (interior) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-      rshift[i] = 0;
       em[i] = cvalid ? kFull : 0u;
-    }
-    if (cvalid) {
-      if (p.in_shift2) {
-#pragma unroll
-        for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
+      if (cvalid) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
     }
   } else {
     load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
-#pragma unroll
-    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
   }
-
-  if (interior && aligned_out) {
-    if (!cvalid) return;
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const int64_t o = o0 + i * p.cols;
-      uint32_t q[E / 4];
-      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-      store_bytes<E>(p.data_row + o, q);
-      if constexpr (kCol) {
-        quantize_chunk<T, kPre>(d[i], cshift, true, q);
-        store_bytes<E>(p.data_col + o, q);
-      }
-    }
-    return;
-  }
+  for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
   if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -751,7 +698,7 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(G
     }
     return;
   }
-  // edge tile: full chunks store whole when the outputs are dword aligned, else byte by byte
+  // edge tile: whole chunks store whole when the outputs are dword aligned, else byte by byte
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     if (!em[i]) continue;
@@ -770,6 +717,77 @@ __attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(G
         store_masked<E>(p.data_col + o, q, em[i]);
     }
   }
+}
+
+// Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
+// with all loads in flight.
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(GroupArgs ga) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int WC = kWaveSize * E;
+  constexpr int RW = kRowsPerWave;
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x >> 6;
+  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
+  if (tile >= p.ntiles) return;  // uniform over the workgroup
+  const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
+  const int64_t band = p.band0 + bq;
+  const int64_t c0 = (int64_t)(t32 - bq * n32) * WC;
+  const int64_t c = c0 + lane * E;
+  const int64_t r0 = band * kBlockLen;
+  const bool cvalid = c < p.cols;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int i0 = wave * RW;
+  const int64_t tile_first = r0 * p.cols + c0;
+  const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
+  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+
+  int cshift[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) cshift[e] = 0;
+  if constexpr (kCol) {
+    if (cvalid) {
+      const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+#pragma unroll
+      for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+    }
+  }
+
+  if (interior && p.mo_row == 0 && p.mo_col == 0) {  // the common tile: straight-line code
+    if (!cvalid) return;
+    const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
+    const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
+    const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
+    uint32_t d[RW][4];
+    int rshift[RW];
+    if (p.in_shift2) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int64_t o = o0 + i * p.cols;
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+      store_bytes<E>(p.data_row + o, q);
+      if constexpr (kCol) {
+        quantize_chunk<T, kPre>(d[i], cshift, true, q);
+        store_bytes<E>(p.data_col + o, q);
+      }
+    }
+    return;
+  }
+  cast_tile_general<T, kCol, kPre>(p, band, c0, c, i0, nrows, interior, cshift);
 }
 
 // ------------------------------------------------------------------ element-wise path (any layout)
