@@ -49,11 +49,17 @@ constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round
 // Resident waves per SIMD the register allocator targets in the vector kernels, per kernel and
 // element type (chosen by measurement on MI355X; without a target the edge-tile path inflates
 // every wave's register budget).
+// Large amax launches run best with few, register-rich waves; small ones (a single rank's
+// fragment) need more resident waves to fill the GPU in one round, so both amax variants are
+// compiled and the launch picks one by its tile count.  The cast's register need is set by
+// its edge / unaligned-output path, so it has one variant.
 template <typename T>
 struct Occupancy {
   static constexpr int kAmax = 4;
+  static constexpr int kAmaxSmall = 6;
   static constexpr int kCast = sizeof(T) == 2 ? 3 : 2;
 };
+constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles, use kAmaxSmall
 
 struct TileArgs {
   int64_t rows, cols, start, end;
@@ -404,9 +410,9 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // with all eight 16-byte loads in flight; the four waves' column-wise maxima meet in LDS.
 // Tiles wholly inside the fragment read-max-write their entries (each has a single owner);
 // edge tiles merge every touched entry atomically, since a neighbouring piece may share it.
-template <typename T, bool kCol, bool kPre>
+template <typename T, bool kCol, bool kPre, int kOcc>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kAmax))) void amax_vec_kernel(GroupArgs ga) {
+__attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block (4 BF16, 8 FP32)
   constexpr int WC = kWaveSize * E;     // tile width in columns
@@ -721,9 +727,9 @@ __device__ __forceinline__ void cast_tile_general(
 
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.
-template <typename T, bool kCol, bool kPre>
+template <typename T, bool kCol, bool kPre, int kOcc>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(Occupancy<T>::kCast))) void cast_vec_kernel(GroupArgs ga) {
+__attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
@@ -1054,8 +1060,8 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
 // for the vector kernels (a workgroup per tile) and kWavesPerGroup for the element-wise ones
 // (a wave per tile).
 template <typename K>
-hipError_t launch_grouped(K kernel, const std::vector<TileArgs>& ps, int tiles_per_wg,
-                          hipStream_t s) {
+hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>& ps,
+                          int tiles_per_wg, hipStream_t s) {
   for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
     GroupArgs g{};
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
@@ -1069,7 +1075,8 @@ hipError_t launch_grouped(K kernel, const std::vector<TileArgs>& ps, int tiles_p
     g.first[g.n] = total;
     const int64_t groups = cdiv(total, tiles_per_wg);
     if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL(total < kSmallLaunchTiles ? small_kernel : kernel, dim3((unsigned)groups),
+                       dim3(kThreads), 0, s, g);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1091,9 +1098,12 @@ template <typename T, bool kCol, bool kPre>
 hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
                               hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (!vec.empty()) e = launch_grouped(amax_vec_kernel<T, kCol, kPre>, vec, 1, s);
+  if (!vec.empty())
+    e = launch_grouped(amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmax>,
+                       amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, vec, 1, s);
   if (e == hipSuccess && !elem.empty())
-    e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, elem, kWavesPerGroup, s);
+    e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, amax_elem_kernel<T, kCol, kPre>, elem,
+                       kWavesPerGroup, s);
   return e;
 }
 
@@ -1101,9 +1111,12 @@ template <typename T, bool kCol, bool kPre>
 hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
                               hipStream_t s) {
   hipError_t e = hipSuccess;
-  if (!vec.empty()) e = launch_grouped(cast_vec_kernel<T, kCol, kPre>, vec, 1, s);
+  if (!vec.empty())
+    e = launch_grouped(cast_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
+                       cast_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, s);
   if (e == hipSuccess && !elem.empty())
-    e = launch_grouped(cast_elem_kernel<T, kCol, kPre>, elem, kWavesPerGroup, s);
+    e = launch_grouped(cast_elem_kernel<T, kCol, kPre>, cast_elem_kernel<T, kCol, kPre>, elem,
+                       kWavesPerGroup, s);
   return e;
 }
 
