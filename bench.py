@@ -51,7 +51,8 @@ def parse():
                     help="distinct input/output sets rotate until this many GB are in use")
     ap.add_argument("--kernel-table", dest="kernel_table", action="store_true", default=True)
     ap.add_argument("--no-kernel-table", dest="kernel_table", action="store_false")
-    ap.add_argument("--kernel-calls", type=int, default=30)
+    ap.add_argument("--kernel-calls", type=int, default=20,
+                    help="graph replays (10 calls each) per kernel-table entry")
     ap.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-rows", type=int, default=8192,
@@ -245,11 +246,12 @@ def main():
 
 def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table: full input and
-    the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Each call is
-    timed alone with HIP events; calls rotate over distinct buffer sets holding >= the
-    footprint option in all (full runs: whole matrices; partial runs: quarter-size fragments
-    placed so that input - 17 elements stays 16-byte aligned), so inputs come from HBM rather
-    than the 256 MB Infinity Cache.  Median over calls."""
+    the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Timed like the
+    pages: HIP events around replays of a captured graph of 10 calls, median per call over the
+    replays.  Calls rotate over distinct buffer sets holding >= the footprint option in all
+    (full runs: whole matrices; partial runs: quarter-size fragments placed so that
+    input - 17 elements stays 16-byte aligned), so inputs come from HBM rather than the 256 MB
+    Infinity Cache."""
     import numpy as np
     import torch
 
@@ -300,14 +302,24 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
                 for i in range(3):
                     fn(pieces[i % n_sets])
                 torch.cuda.synchronize()
+                # the pages' method: HIP-event timing of graph replays, 10 calls per graph
+                # (each on the next buffer set), median per call over the replays
+                per_graph = 10
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(per_graph):
+                        fn(pieces[i % n_sets])
+                g.replay()
+                torch.cuda.synchronize()
                 ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                       for _ in range(args.kernel_calls)]
-                for i, (e0, e1) in enumerate(ev):
+                for e0, e1 in ev:
                     e0.record()
-                    fn(pieces[i % n_sets])
+                    g.replay()
                     e1.record()
                 torch.cuda.synchronize()
-                us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+                us = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
+                del g
                 gbs = pb[kname] / (us * 1e-6) / 1e9
                 table[f"{kname}_{dtype}_{run}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
                                                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
