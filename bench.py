@@ -3,17 +3,19 @@
 One step is the whole path over a 16384x6144 master weight (BF16 by default) held as four
 contiguous fragments whose boundaries fall inside 32-value blocks (cuts at N/4+17, N/2+17,
 3N/4+17), as four ranks would hold it: zero-fill of one packed amax buffer per fragment,
-partial amax of every fragment, MAX-combine of the four buffers, E8M0 scales for the whole
-weight, and the in-place partial cast of every fragment to E4M3 row-wise and column-wise
-data.  Inputs are resident in HBM before timing.  Steps walk over several distinct weights
+partial amax of every fragment, MAX-combine of the four buffers, then E8M0 scales and the
+in-place partial cast of every fragment to E4M3 row-wise and column-wise data: by default in
+one fused pass per fragment (mxfp8_scales_and_cast), with ``--separate-scales`` as the
+scales call over the whole weight followed by the cast call.  Inputs are resident in HBM before timing.  Steps walk over several distinct weights
 (buffer sets, >= 1.2 GB in all) like a writeback over a model: step i runs the amax side on
 weight i and the cast of weight i - 1, so no kernel reads an input another kernel has just
 left in the 256 MB Infinity Cache.
 
 Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
-``roofline`` is for the dominant kernel (the partial cast), from HIP events recorded on the
-launch stream around every cast call of the timed steps; ``kernels`` is the per-call table
-(full input and the quarter fragment at offset 17, BF16 and FP32); ``cpu_baseline`` times
+``roofline`` is for the dominant kernel (the cast, fused with the scales by default), from
+HIP events recorded on the launch stream around every cast call of the timed steps;
+``kernels`` is the per-call table (partial amax, partial cast and the fused scales + cast;
+full input and the quarter fragment at offset 17, BF16 and FP32); ``cpu_baseline`` times
 the oracle on the host over a band-aligned sample of the same workload.
 """
 from __future__ import annotations
@@ -34,7 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for partial amax + cast"
 KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_partial_amd", "csrc", "kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "cast_bf16_16384x6144_counters.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "writeback_step_bf16_16384x6144_counters.md")
 
 
 def log(*a):
@@ -57,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-rows", type=int, default=8192,
                     help="rows of the weight (a band-aligned sample) the oracle processes")
+    ap.add_argument("--separate-scales", dest="fused", action="store_false", default=True,
+                    help="run the scales and the cast as two calls instead of the fused call")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain device copy (the counter calibration kernel)")
     return ap.parse_args()
@@ -66,9 +70,9 @@ def kernel_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_counters(alg_bytes_per_launch):
-    """HBM bytes per cast launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; None otherwise."""
+def traffic_from_counters(kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; None otherwise."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
@@ -77,7 +81,7 @@ def traffic_from_counters(alg_bytes_per_launch):
     d = json.loads(m.group(1))
     if d.get("kernel_source_sha256_16") != kernel_sha():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_launch", {}).get(kernel)
 
 
 def main():
@@ -124,13 +128,13 @@ def main():
     sets = []
     for i in range(n_sets):
         x = x0 if i == 0 else x0.clone()
-        wb = W.Writeback([spec], tdt, dev, frags, shared=False)
+        wb = W.Writeback([spec], tdt, dev, frags, shared=False, fused=args.fused)
         plan = wb.plan([x[s:s + l] for s, l in frags])
         sets.append((x, wb, plan))
     for p in sets[0][2].amax:
         assert B.mxfp8_query_path(p, 0) == 1
     for p in sets[0][2].cast:
-        assert B.mxfp8_query_path(p, 1) == 1
+        assert B.mxfp8_query_path(p, 2 if args.fused else 1) == 1
 
     # algorithmic bytes of one step
     per = [BM.piece_bytes(rows, cols, s, l, s_in, True) for s, l in frags]
@@ -139,12 +143,15 @@ def main():
         "zero": BM.zero_bytes(4, packed, s_in),
         "amax": sum(p["amax"] for p in per),
         "combine": BM.combine_bytes(4, packed, s_in),
-        "scales": BM.piece_bytes(rows, cols, 0, n, s_in, True)["scales"],
-        "cast": sum(p["cast"] for p in per),
     }
+    if args.fused:
+        stage_bytes["scales_cast"] = sum(p["scales_cast"] for p in per)
+    else:
+        stage_bytes["scales"] = BM.piece_bytes(rows, cols, 0, n, s_in, True)["scales"]
+        stage_bytes["cast"] = sum(p["cast"] for p in per)
     step_bytes = sum(stage_bytes.values())
 
-    # Step i runs zero / amax / combine / scales on buffer set i and the cast of set i - 1,
+    # Step i runs zero / amax / combine (/ scales) on buffer set i and the cast of set i - 1,
     # the weight before it: as in a writeback over many weights, a fragment's cast never
     # directly follows its own amax, so the cast reads its input from HBM and not from the
     # Infinity Cache the amax just filled.  Every step still runs every stage once.
@@ -180,17 +187,21 @@ def main():
     stage_ms_mean = {name: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
                      for j, name in enumerate(stage_names)}
 
-    # dominant kernel: the partial cast.  The library launches the pieces of one call that
-    # share a kernel specialization together, up to 16 per launch: here the 4 fragments of
-    # the weight (all on the vector path, checked above) go out as one launch.
+    # dominant kernel: the cast (fused with the scales by default).  The library launches
+    # the pieces of one call that share a kernel specialization together, up to 16 per
+    # launch: here the 4 fragments of the weight (all on the vector path, checked above) go
+    # out as one launch.
+    cast_stage = stage_names[-1]
+    kname = (f"cast_vec_kernel<{args.dtype}, colwise, fused scales>" if args.fused
+             else f"cast_vec_kernel<{args.dtype}, colwise>")
     n_cast = -(-sets[0][2].n_cast // 16)
-    cast_launch_us = stage_ms_mean["cast"] * 1e3 / n_cast
-    cast_bytes_launch = stage_bytes["cast"] / n_cast
+    cast_launch_us = stage_ms_mean[cast_stage] * 1e3 / n_cast
+    cast_bytes_launch = stage_bytes[cast_stage] / n_cast
     achieved = cast_bytes_launch / (cast_launch_us * 1e-6) / 1e9
-    traffic = traffic_from_counters(cast_bytes_launch)
+    traffic = traffic_from_counters(kname) if args.dtype == "bf16" else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": f"cast_vec_kernel<{args.dtype}, colwise>",
+                "traffic": traffic, "kernel": kname,
                 "launch_us": round(cast_launch_us, 2),
                 "alg_bytes_per_launch": int(cast_bytes_launch)}
 
@@ -202,8 +213,9 @@ def main():
         "dtype": args.dtype, "data": "synthetic",
         "config": {"workload": f"{rows}x{cols} {args.dtype} master weight as 4 contiguous "
                                "fragments (cuts at N/4+17, N/2+17, 3N/4+17), bidirectional "
-                               "MXFP8 writeback: zero, partial amax, combine K=4, scales, "
-                               "partial cast",
+                               "MXFP8 writeback: zero, partial amax, combine K=4, "
+                               + ("scales fused into the partial cast" if args.fused
+                                  else "scales, partial cast"),
                    "rows": rows, "cols": cols, "fragments": frags, "buffer_sets": n_sets,
                    "step_alg_bytes": step_bytes},
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
@@ -245,7 +257,8 @@ def main():
 
 
 def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
-    """Per-call µs and GB/s of partial amax and partial cast, the pages' table: full input and
+    """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
+    scales + cast: full input and
     the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Timed like the
     pages: HIP events around replays of a captured graph of 10 calls, median per call over the
     replays.  Calls rotate over distinct buffer sets holding >= the footprint option in all
@@ -278,7 +291,7 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
             lead = s % 32                      # element offset that keeps input - s aligned
             per_set = l * s_in + 2 * l + 2 * (n // 32) * (s_in + 1)
             n_sets = max(2, int(np.ceil(args.min_footprint_gb * 1e9 / per_set)))
-            amax_p, cast_p, keep = [], [], []
+            amax_p, cast_p, fused_p, keep = [], [], [], []
             for i in range(n_sets):
                 xb = torch.empty(l + 32, dtype=tdt, device=dev)
                 xb[lead:lead + l] = x0[s:s + l]
@@ -294,11 +307,17 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
                 amax_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac))
                 cast_p.append(B.make_piece(rows, cols, s, x, scale_row=sr, scale_col=sc,
                                            data_row=dr, data_col=dc))
+                fused_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac,
+                                            scale_row=sr, scale_col=sc, data_row=dr,
+                                            data_col=dc))
                 assert B.mxfp8_query_path(amax_p[-1], 0) == 1
                 assert B.mxfp8_query_path(cast_p[-1], 1) == 1
+                assert B.mxfp8_query_path(fused_p[-1], 2) == 1
             pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
+            # the amax runs first, so the fused call reads real amax entries
             for kname, pieces, fn in (("amax", amax_p, B.mxfp8_partial_amax),
-                                      ("cast", cast_p, B.mxfp8_partial_cast)):
+                                      ("cast", cast_p, B.mxfp8_partial_cast),
+                                      ("scales_cast", fused_p, B.mxfp8_scales_and_cast)):
                 for i in range(3):
                     fn(pieces[i % n_sets])
                 torch.cuda.synchronize()
@@ -324,7 +343,7 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
                 table[f"{kname}_{dtype}_{run}"] = {"us": round(us, 2), "GBps": round(gbs, 1),
                                                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                                                    "alg_bytes": pb[kname], "buffer_sets": n_sets}
-            del keep, amax_p, cast_p
+            del keep, amax_p, cast_p, fused_p
             torch.cuda.empty_cache()
         del x0
     return table

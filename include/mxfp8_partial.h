@@ -128,10 +128,25 @@ int mxfp8_compute_scales(const mxfp8_piece* pieces, int n, void* hip_stream);
  * input, scale_row, scale_col, data_row, data_col. */
 int mxfp8_partial_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
 
+/* Steps 3 and 4 in one pass (the scale update and the output writes of the flow diagram,
+ * fused by this library; the pages run them as separate steps).
+ * Same results as mxfp8_compute_scales followed by mxfp8_partial_cast on the same pieces:
+ * the scale of each block the fragment touches is derived from its amax entry, written to
+ * scale_row / scale_col, and used directly for that block's E4M3 bytes; the scale arrays
+ * are written, never read.  The column-wise work (amax_col read, scale_col and data_col
+ * written) happens iff data_col != NULL, which then requires amax_col and scale_col; when
+ * data_col is NULL both are ignored even if set.  Required: input, amax_row, scale_row,
+ * data_row.  Scale and data outputs must not overlap the input, the amax arrays or each
+ * other.  Reads: rows, cols, start, len, in_dtype (also the amax dtype), preround_bf16,
+ * input, amax_row, amax_col, scale_row, scale_col, data_row, data_col.  Pieces whose
+ * fragments share a cut block write the same scale byte. */
+int mxfp8_scales_and_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
+
 /* Message for the calling thread's last non-OK status (static storage, thread-local). */
 const char* mxfp8_last_error(void);
 
-/* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast:
+/* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast,
+ * 2 = scales and cast (validated as for mxfp8_scales_and_cast; it takes the cast's path):
  * 1 = the vectorized path (16-byte loads of row segments of whole 32-value blocks, for any
  * cols % 32 == 0, whatever the alignment of input and outputs), 0 = the element-wise path
  * (cols % 32 != 0), negative = the piece fails validation (the status code, negated).

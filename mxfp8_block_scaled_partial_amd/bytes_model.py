@@ -12,6 +12,8 @@ T_col the row-wise / column-wise blocks the fragment touches:
   partial amax    len * s_in + 2 * (T_row + T_col) * s_in
   compute scales  (T_row + T_col) * (s_in + 1)
   partial cast    len * s_in + (T_row + T_col) * 1 + len * D
+  scales + cast   len * s_in + (T_row + T_col) * (s_in + 1) + len * D   (fused: amax entries
+                  read, scale bytes written, no scale read-back)
   combine         (K + 1) * P * s_in     (K partial packed buffers of P entries -> one)
   zero-fill       K * P * s_in
 """
@@ -56,13 +58,14 @@ def touched_col_blocks(rows: int, cols: int, start: int, length: int) -> int:
 
 
 def piece_bytes(rows: int, cols: int, start: int, length: int, s_in: int, colwise: bool):
-    """Per-step algorithmic bytes of one piece: dict with amax, scales, cast."""
+    """Per-step algorithmic bytes of one piece: dict with amax, scales, cast, scales_cast."""
     tr = touched_row_blocks(rows, cols, start, length)
     tc = touched_col_blocks(rows, cols, start, length) if colwise else 0
     d = 2 if colwise else 1
     return {"amax": length * s_in + 2 * (tr + tc) * s_in,
             "scales": (tr + tc) * (s_in + 1),
             "cast": length * s_in + (tr + tc) + length * d,
+            "scales_cast": length * s_in + (tr + tc) * (s_in + 1) + length * d,
             "touched_row": tr, "touched_col": tc}
 
 

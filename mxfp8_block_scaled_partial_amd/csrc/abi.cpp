@@ -48,8 +48,9 @@ Span span1d(const void* p, int64_t bytes) {
 
 int64_t nblk(int64_t n) { return (n + 31) / 32; }
 
-enum Kind { kAmax, kScales, kCast };
-const char* kKindName[] = {"mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast"};
+enum Kind { kAmax, kScales, kCast, kFused };
+const char* kKindName[] = {"mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast",
+                           "mxfp8_scales_and_cast"};
 
 bool aligned(const void* p, int64_t a) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)a == 0; }
 
@@ -120,7 +121,7 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
     return MXFP8_OK;
   };
   int st;
-  if (kind == kAmax || kind == kCast) {
+  if (kind != kScales) {
     if (!q.input) return fail(MXFP8_ERR_ARG, "%s: piece %d: input is NULL with len > 0", fn, idx);
     if (!aligned(q.input, esz))
       return fail(MXFP8_ERR_LAYOUT, "%s: piece %d: input is not aligned to its element size", fn,
@@ -138,7 +139,13 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
       return st;
     if (!p.amax_col) p.scale_col = nullptr;  // column-wise scales not updated when absent
   }
-  if (kind == kCast) {
+  if (kind == kFused) {  // the column-wise work, amax included, follows data_col
+    if ((st = need_amax(q.amax_row, nb, "amax_row", true, &p.amax_row, &p.ld_ar))) return st;
+    if (q.data_col &&
+        (st = need_amax(q.amax_col, q.cols, "amax_col", true, &p.amax_col, &p.ld_ac)))
+      return st;
+  }
+  if (kind == kCast || kind == kFused) {
     if (!q.data_row) return fail(MXFP8_ERR_MISSING, "%s: piece %d: data_row is required", fn, idx);
     if ((st = need_scale(q.scale_row, nb, "scale_row", true, &p.scale_row, &p.ld_sr))) return st;
     p.data_row = static_cast<uint8_t*>(q.data_row);
@@ -175,6 +182,14 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
         (st = clash(sr, sc, "scale_row", "scale_col")))
       return st;
   } else {
+    if (kind == kFused &&
+        ((st = clash(sr, in, "scale_row", "input")) || (st = clash(sc, in, "scale_col", "input")) ||
+         (st = clash(sr, sc, "scale_row", "scale_col")) ||
+         (st = clash(sr, ar, "scale_row", "amax_row")) || (st = clash(sr, ac, "scale_row", "amax_col")) ||
+         (st = clash(sc, ar, "scale_col", "amax_row")) || (st = clash(sc, ac, "scale_col", "amax_col")) ||
+         (st = clash(dr, ar, "data_row", "amax_row")) || (st = clash(dr, ac, "data_row", "amax_col")) ||
+         (st = clash(dc, ar, "data_col", "amax_row")) || (st = clash(dc, ac, "data_col", "amax_col"))))
+      return st;
     if ((st = clash(dr, in, "data_row", "input")) || (st = clash(dc, in, "data_col", "input")) ||
         (st = clash(dr, dc, "data_row", "data_col")) || (st = clash(dr, sr, "data_row", "scale_row")) ||
         (st = clash(dr, sc, "data_row", "scale_col")) || (st = clash(dc, sr, "data_col", "scale_row")) ||
@@ -227,6 +242,10 @@ int mxfp8_partial_cast(const mxfp8_piece* pieces, int n, void* hip_stream) {
   return run_pieces(pieces, n, hip_stream, kCast, mxfp8::launch_partial_cast);
 }
 
+int mxfp8_scales_and_cast(const mxfp8_piece* pieces, int n, void* hip_stream) {
+  return run_pieces(pieces, n, hip_stream, kFused, mxfp8::launch_scales_and_cast);
+}
+
 int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
                        int32_t amax_dtype, void* hip_stream) {
   const char* fn = "mxfp8_combine_amax";
@@ -259,11 +278,13 @@ const char* mxfp8_last_error(void) { return g_err; }
 
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel) {
   if (!piece) return -fail(MXFP8_ERR_ARG, "mxfp8_query_path: piece is NULL");
-  if (kernel != 0 && kernel != 1)
-    return -fail(MXFP8_ERR_ARG, "mxfp8_query_path: kernel must be 0 (amax) or 1 (cast)");
+  if (kernel < 0 || kernel > 2)
+    return -fail(MXFP8_ERR_ARG,
+                 "mxfp8_query_path: kernel must be 0 (amax), 1 (cast) or 2 (scales and cast)");
   mxfp8::Piece p;
   bool skip;
-  const int st = check_piece(*piece, kernel == 0 ? kAmax : kCast, 0, &p, &skip);
+  const Kind kinds[3] = {kAmax, kCast, kFused};
+  const int st = check_piece(*piece, kinds[kernel], 0, &p, &skip);
   if (st) return -st;
   if (skip) return 0;
   return kernel == 0 ? (int)mxfp8::amax_fast_ok(p) : (int)mxfp8::cast_fast_ok(p);

@@ -68,9 +68,9 @@ struct TileArgs {
   int64_t ld_ar;
   void* amax_col;
   int64_t ld_ac;
-  const uint8_t* scale_row;
+  uint8_t* scale_row;  // read by the cast; written by the fused scales + cast
   int64_t ld_sr;
-  const uint8_t* scale_col;
+  uint8_t* scale_col;
   int64_t ld_sc;
   uint8_t* data_row;
   uint8_t* data_col;
@@ -395,6 +395,45 @@ __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src
   }
 }
 
+// Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
+// values, so the biased MX exponent is field - 8, clamped at 0 (subnormal and zero amax
+// included); the field is at most 254 for finite amax, so the upper clamp never applies.
+template <typename T>
+__device__ __forceinline__ uint8_t e8m0_of(uint32_t bits) {
+  const int field = sizeof(T) == 2 ? (int)((bits >> 7) & 0xFF) : (int)((bits >> 23) & 0xFF);
+  return (uint8_t)(field > 8 ? field - 8 : 0);
+}
+
+// Whether row-wise block (r, c / 32) holds an element of the fragment (any width of row).
+__device__ __forceinline__ bool row_block_touched(const TileArgs& p, int64_t r, int64_t c) {
+  const int64_t gb = r * p.cols + (c & ~int64_t(kBlockLen - 1));
+  const int64_t ge = min<int64_t>(gb + kBlockLen, (r + 1) * p.cols);
+  return gb < p.end && ge > p.start;
+}
+
+// Row and column of the fragment's first and last element.
+struct Corners {
+  int64_t rs, cs, re, ce;
+};
+__device__ __forceinline__ Corners corners_of(const TileArgs& p) {
+  Corners f;
+  f.rs = p.start / p.cols;
+  f.cs = p.start - f.rs * p.cols;
+  f.re = (p.end - 1) / p.cols;
+  f.ce = p.end - 1 - f.re * p.cols;
+  return f;
+}
+
+// Whether the column-wise block of rows [r0, r1] in column col holds an element of the
+// fragment: the fragment's rows in column col run from rs (rs + 1 left of cs) to re (re - 1
+// right of ce).
+__device__ __forceinline__ bool col_block_touched(const Corners& f, int64_t r0, int64_t r1,
+                                                  int64_t col) {
+  const int64_t lo = max(r0, col >= f.cs ? f.rs : f.rs + 1);
+  const int64_t hi = min(r1, col <= f.ce ? f.re : f.re - 1);
+  return lo <= hi;
+}
+
 // ------------------------------------------------------------------ partial amax, vector path
 
 constexpr int kRowsPerWave = kBlockLen / kWavesPerGroup;  // 8 rows of the band per wave
@@ -651,10 +690,73 @@ __device__ __forceinline__ void store_window(uint8_t* p, const uint32_t* q, int 
   if (last) store_masked<E>(p, q, ((1u << E) - 1) & ~((1u << (E - mo)) - 1));
 }
 
+// Fused scales: the E8M0 bytes of the lane's E column-wise blocks, from their amax entries.
+template <typename T>
+__device__ __forceinline__ void col_scales(const TileArgs& p, int64_t band, int64_t c,
+                                           uint8_t (&s)[Chunk<T>::E]) {
+  constexpr int E = Chunk<T>::E;
+  const T* a = static_cast<const T*>(p.amax_col) + band * p.ld_ac + c;
+  if (p.col_vec) {
+    uint32_t d[4];
+    load16(a, d);
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = e8m0_of<T>(chunk_elem<T>(d, e));
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) s[e] = e8m0_of<T>(a[e]);
+  }
+}
+
+// E scale bytes at p; bit e of mask selects byte e.  Whole dword-aligned runs go out as one
+// store.
+template <int E>
+__device__ __forceinline__ void store_scale_bytes(uint8_t* p, const uint8_t (&s)[E],
+                                                  uint32_t mask) {
+  if (mask == (1u << E) - 1 && (reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+    uint32_t w[E / 4];
+#pragma unroll
+    for (int j = 0; j < E / 4; ++j)
+      w[j] = s[4 * j] | (s[4 * j + 1] << 8) | (s[4 * j + 2] << 16) | ((uint32_t)s[4 * j + 3] << 24);
+    if constexpr (E == 8)
+      *reinterpret_cast<v2u*>(p) = v2u{w[0], w[1]};
+    else
+      *reinterpret_cast<uint32_t*>(p) = w[0];
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((mask >> e) & 1u) p[e] = s[e];
+}
+
+// Fused scales: the amax entry of row-wise block (r, c / 32).
+template <typename T>
+__device__ __forceinline__ uint32_t row_amax(const TileArgs& p, int64_t r, int64_t c) {
+  return static_cast<const T*>(p.amax_row)[r * p.ld_ar + (c >> 5)];
+}
+
+// Fused scales: wave 0 writes the scale bytes of the lane's column-wise blocks that the
+// fragment touches (all of them in an interior tile).  Called after the tile's loads.
+template <typename T>
+__device__ __forceinline__ void store_col_scales(const TileArgs& p, int64_t band, int64_t c,
+                                                 int nrows, bool interior,
+                                                 const uint8_t (&sb)[Chunk<T>::E]) {
+  constexpr int E = Chunk<T>::E;
+  uint32_t m = (1u << E) - 1;
+  if (!interior) {
+    const Corners f = corners_of(p);
+    const int64_t r0 = band * kBlockLen;
+    m = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (col_block_touched(f, r0, r0 + nrows - 1, c + e)) m |= 1u << e;
+  }
+  store_scale_bytes<E>(p.scale_col + band * p.ld_sc + c, sb, m);
+}
+
 // Tiles a fragment boundary or the short last band cuts, and tiles whose outputs are not
 // dword aligned: masked loads, byte stores or window stores.  The common tile (interior,
 // dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.
-template <typename T, bool kCol, bool kPre>
+template <typename T, bool kCol, bool kPre, bool kFuse>
 __device__ __forceinline__ void cast_tile_general(
     const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows, bool interior,
     const int* cshift) {
@@ -682,8 +784,27 @@ __device__ __forceinline__ void cast_tile_general(
   } else {
     load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   }
+  if constexpr (kFuse) {
+    // the first lane of each row-wise block writes the scale of a block the fragment
+    // touches; every amax entry is loaded before the first store, so no load waits on one
+    uint32_t ab[RW];
+    bool wr[RW];
 #pragma unroll
-  for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
+    for (int i = 0; i < RW; ++i) {
+      wr[i] = (lane & (kBlockLen / E - 1)) == 0 && cvalid && i < nrows - i0 &&
+              (interior || row_block_touched(p, r0 + i0 + i, c));
+      ab[i] = (em[i] || wr[i]) ? row_amax<T>(p, r0 + i0 + i, c) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const uint8_t sb = e8m0_of<T>(ab[i]);
+      rshift[i] = 127 - (int)sb;
+      if (wr[i]) p.scale_row[(r0 + i0 + i) * p.ld_sr + (c >> 5)] = sb;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
+  }
   if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -727,7 +848,7 @@ __device__ __forceinline__ void cast_tile_general(
 
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.
-template <typename T, bool kCol, bool kPre, int kOcc>
+template <typename T, bool kCol, bool kPre, bool kFuse, int kOcc>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -754,13 +875,23 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
 
   int cshift[E];
+  uint8_t csb[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) cshift[e] = 0;
+  for (int e = 0; e < E; ++e) {
+    cshift[e] = 0;
+    csb[e] = 0;
+  }
   if constexpr (kCol) {
     if (cvalid) {
-      const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+      if constexpr (kFuse) {
+        col_scales<T>(p, band, c, csb);  // written after the tile's loads
 #pragma unroll
-      for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+        for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)csb[e];
+      } else {
+        const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+#pragma unroll
+        for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
+      }
     }
   }
 
@@ -778,8 +909,21 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
     }
+    if constexpr (kFuse) {
+      // all amax entries are loaded before the first store, so no load waits on a store
+      uint32_t ab[RW];
 #pragma unroll
-    for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
+      for (int i = 0; i < RW; ++i) ab[i] = row_amax<T>(p, r0 + i0 + i, c);
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const uint8_t sb = e8m0_of<T>(ab[i]);
+        rshift[i] = 127 - (int)sb;
+        if ((lane & (kBlockLen / E - 1)) == 0) p.scale_row[(r0 + i0 + i) * p.ld_sr + (c >> 5)] = sb;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
+    }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       const int64_t o = o0 + i * p.cols;
@@ -791,9 +935,15 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
         store_bytes<E>(p.data_col + o, q);
       }
     }
+    if constexpr (kFuse && kCol) {
+      if (wave == 0) store_col_scales<T>(p, band, c, nrows, true, csb);
+    }
     return;
   }
-  cast_tile_general<T, kCol, kPre>(p, band, c0, c, i0, nrows, interior, cshift);
+  cast_tile_general<T, kCol, kPre, kFuse>(p, band, c0, c, i0, nrows, interior, cshift);
+  if constexpr (kFuse && kCol) {
+    if (wave == 0 && cvalid) store_col_scales<T>(p, band, c, nrows, interior, csb);
+  }
 }
 
 // ------------------------------------------------------------------ element-wise path (any layout)
@@ -838,7 +988,7 @@ __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
   }
 }
 
-template <typename T, bool kCol, bool kPre>
+template <typename T, bool kCol, bool kPre, bool kFuse>
 __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
@@ -852,13 +1002,28 @@ __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   const int64_t r0 = band * kBlockLen;
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
   int cshift = 0;
-  if constexpr (kCol) cshift = 127 - (int)p.scale_col[band * p.ld_sc + c];
+  if constexpr (kCol) {
+    if constexpr (kFuse) {
+      const uint8_t sb = e8m0_of<T>(static_cast<const T*>(p.amax_col)[band * p.ld_ac + c]);
+      cshift = 127 - (int)sb;
+      if (col_block_touched(corners_of(p), r0, r0 + nrows - 1, c))
+        p.scale_col[band * p.ld_sc + c] = sb;
+    } else {
+      cshift = 127 - (int)p.scale_col[band * p.ld_sc + c];
+    }
+  }
   for (int i = 0; i < nrows; ++i) {
     const int64_t r = r0 + i;
     const int64_t g = r * p.cols + c;
-    if (g < p.start || g >= p.end) continue;
+    const bool inside = g >= p.start && g < p.end;
+    // fused: the lane at the start of a row-wise block writes its scale if the block is touched
+    const bool wr = kFuse && (c & (kBlockLen - 1)) == 0 && row_block_touched(p, r, c);
+    if (!inside && !wr) continue;
+    const uint8_t sb = kFuse ? e8m0_of<T>(row_amax<T>(p, r, c)) : p.scale_row[r * p.ld_sr + (c >> 5)];
+    if (wr) p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
+    if (!inside) continue;
     const float w = work_value<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
-    p.data_row[g - p.start] = cvt1(w, 127 - (int)p.scale_row[r * p.ld_sr + (c >> 5)]);
+    p.data_row[g - p.start] = cvt1(w, 127 - (int)sb);
     if constexpr (kCol) p.data_col[g - p.start] = cvt1(w, cshift);
   }
 }
@@ -884,14 +1049,6 @@ struct ScaleArgs {
   int32_t row_vec, col_vec;  // rows of amax / scales aligned for 16-byte / 8-byte vectors
 };
 
-// Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
-// values, so the biased MX exponent is field - 8, clamped at 0 (subnormal and zero amax
-// included); the field is at most 254 for finite amax, so the upper clamp never applies.
-template <typename T>
-__device__ __forceinline__ uint8_t e8m0_of(uint32_t bits) {
-  const int field = sizeof(T) == 2 ? (int)((bits >> 7) & 0xFF) : (int)((bits >> 23) & 0xFF);
-  return (uint8_t)(field > 8 ? field - 8 : 0);
-}
 
 // Whether column-wise block (b, c) holds an element of [start, end).
 __device__ __forceinline__ bool col_block_touched(const ScaleArgs& p, int64_t b, int64_t c) {
@@ -1107,16 +1264,36 @@ hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vecto
   return e;
 }
 
-template <typename T, bool kCol, bool kPre>
+template <typename T, bool kCol, bool kPre, bool kFuse>
 hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
                               hipStream_t s) {
   hipError_t e = hipSuccess;
   if (!vec.empty())
-    e = launch_grouped(cast_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
-                       cast_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, s);
+    e = launch_grouped(cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>,
+                       cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1, s);
   if (e == hipSuccess && !elem.empty())
-    e = launch_grouped(cast_elem_kernel<T, kCol, kPre>, cast_elem_kernel<T, kCol, kPre>, elem,
-                       kWavesPerGroup, s);
+    e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
+                       elem, kWavesPerGroup, s);
+  return e;
+}
+
+template <bool kFuse>
+hipError_t launch_cast_pieces(const Piece* ps, int n, hipStream_t s) {
+  Buckets bk;
+  for (int i = 0; i < n; ++i) {
+    const Piece& p = ps[i];
+    const bool vec = vec_common_ok(p);
+    const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
+    bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
+  }
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  run(launch_cast_bucket<uint16_t, true, false, kFuse>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
+  run(launch_cast_bucket<uint16_t, false, false, kFuse>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
+  run(launch_cast_bucket<uint32_t, true, false, kFuse>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
+  run(launch_cast_bucket<uint32_t, false, false, kFuse>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
+  run(launch_cast_bucket<uint32_t, true, true, kFuse>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
+  run(launch_cast_bucket<uint32_t, false, true, kFuse>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
   return e;
 }
 
@@ -1148,22 +1325,11 @@ hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
 }
 
 hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s) {
-  Buckets bk;
-  for (int i = 0; i < n; ++i) {
-    const Piece& p = ps[i];
-    const bool vec = cast_fast_ok(p);
-    const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
-    bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
-  }
-  hipError_t e = hipSuccess;
-  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  run(launch_cast_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
-  run(launch_cast_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
-  run(launch_cast_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
-  run(launch_cast_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
-  run(launch_cast_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
-  run(launch_cast_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
-  return e;
+  return launch_cast_pieces<false>(ps, n, s);
+}
+
+hipError_t launch_scales_and_cast(const Piece* ps, int n, hipStream_t s) {
+  return launch_cast_pieces<true>(ps, n, s);
 }
 
 hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {

@@ -36,6 +36,8 @@ bool cast_fast_ok(const Piece& p);
 // Pieces sharing a kernel specialization go out in as few launches as possible.
 hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s);
+// The cast with the scales computed from the amax on the fly (and written for touched blocks).
+hipError_t launch_scales_and_cast(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,
                           hipStream_t s);

@@ -13,7 +13,9 @@ Validation: mixed row-only / bidirectional batches, fragment outputs, boundaries
     the kernel's atomic max), or each fragment gets its own packed buffer, as a rank would,
     and ``mxfp8_combine_amax`` MAX-combines them;
   * scales are computed once per weight over the range its fragments cover, and every
-    piece is cast in place into caller-owned, full-size MXFP8 storage.
+    piece is cast in place into caller-owned, full-size MXFP8 storage; with ``fused=True``
+    each piece instead derives its scales from the combined amax inside its cast
+    (``mxfp8_scales_and_cast``), so the scales take no pass of their own.
 
 All arithmetic runs in the library's kernels; buffers are zero-filled with torch's fill.
 """
@@ -119,9 +121,11 @@ class Plan:
                 xin = x[off:off + n]
                 amax_pieces.append(B.make_piece(spec.rows, spec.cols, s, xin, amax_row=ar,
                                                 amax_col=ac, preround=wb.preround))
+                car, cac = wb.combined.views(i) if wb.fused else (None, None)
                 cast_pieces.append(B.make_piece(
-                    spec.rows, spec.cols, s, xin, scale_row=st.scale_row,
-                    scale_col=st.scale_col, data_row=st.data_row[s:s + n],
+                    spec.rows, spec.cols, s, xin, amax_row=car, amax_col=cac,
+                    scale_row=st.scale_row, scale_col=st.scale_col,
+                    data_row=st.data_row[s:s + n],
                     data_col=st.data_col[s:s + n] if spec.colwise else None,
                     preround=wb.preround))
         self.amax = (B.Piece * len(amax_pieces))(*amax_pieces)
@@ -130,7 +134,8 @@ class Plan:
 
     def stages(self, stream=None):
         """The writeback as (name, callable) stages, in order: zero-fill of the packed amax,
-        partial amax, MAX-combine (only with one packed buffer per fragment), scales, cast."""
+        partial amax, MAX-combine (only with one packed buffer per fragment), then scales and
+        cast, or one fused scales-and-cast stage."""
         wb = self.wb
         lib = B.lib()
         sp = B._stream(stream)
@@ -151,9 +156,14 @@ class Plan:
         def cast():
             B._check(lib.mxfp8_partial_cast(self.cast, self.n_cast, sp))
 
+        def scales_cast():
+            B._check(lib.mxfp8_scales_and_cast(self.cast, self.n_cast, sp))
+
         out = [("zero", zero), ("amax", amax)]
         if not wb.shared and len(wb.packed) > 1:
             out.append(("combine", combine))
+        if wb.fused:
+            return out + [("scales_cast", scales_cast)]
         return out + [("scales", scales), ("cast", cast)]
 
     def run(self, stream=None):
@@ -165,12 +175,14 @@ class Writeback:
     """Writeback of one batch of weights, held as contiguous fragments of a flat buffer.
 
     ``shared=True`` accumulates every fragment's amax in one packed buffer; ``shared=False``
-    gives each fragment its own packed buffer (one per rank) and MAX-combines them."""
+    gives each fragment its own packed buffer (one per rank) and MAX-combines them.
+    ``fused=True`` computes the scales inside the cast."""
 
     def __init__(self, specs, dtype: torch.dtype, device, fragments, shared: bool = True,
-                 preround: bool = False):
+                 preround: bool = False, fused: bool = False):
         self.specs = list(specs)
         self.dtype = dtype
+        self.fused = fused
         self.fragments = [(int(s), int(l)) for s, l in fragments]
         self.shared = shared
         self.preround = preround

@@ -78,9 +78,10 @@ def call(fn, *pieces):
 
 
 AMAX, SCALES, CAST = "mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast"
+FUSED = "mxfp8_scales_and_cast"
 
 
-@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST])
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED])
 def test_shape_range_dtype_errors(fn):
     assert call(fn, raw_piece(rows=0)) == B.ERR_ARG
     assert call(fn, raw_piece(cols=-3)) == B.ERR_ARG
@@ -96,10 +97,11 @@ def test_shape_range_dtype_errors(fn):
 def test_preround_needs_fp32():
     assert call(AMAX, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
     assert call(CAST, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
+    assert call(FUSED, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
     assert call(AMAX, raw_piece(dtype=B.BF16, pre=2)) == B.ERR_ARG
 
 
-@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST])
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED])
 def test_empty_fragment_is_a_no_op_even_with_null_buffers(fn):
     p = B.Piece(64, 64, 17, 0, B.BF16, 0, None, B.Buf(None, 0), B.Buf(None, 0), B.Buf(None, 0),
                 B.Buf(None, 0), None, None)
@@ -118,6 +120,45 @@ def test_required_buffers():
     # requested column-wise output needs its scales
     assert call(CAST, raw_piece(scale_col=B.Buf(None, 0))) == B.ERR_MISSING
     assert "scale_col" in B.mxfp8_last_error()
+
+
+def test_scales_and_cast_required_buffers():
+    assert call(FUSED, raw_piece(input=None)) == B.ERR_ARG
+    for name in ("amax_row", "scale_row"):
+        assert call(FUSED, raw_piece(**{name: B.Buf(None, 0)})) == B.ERR_MISSING
+        assert name in B.mxfp8_last_error()
+    assert call(FUSED, raw_piece(data_row=None)) == B.ERR_MISSING
+    # column-wise output present: its amax and scales are required
+    for name in ("amax_col", "scale_col"):
+        assert call(FUSED, raw_piece(**{name: B.Buf(None, 0)})) == B.ERR_MISSING
+        assert name in B.mxfp8_last_error()
+    # column-wise output absent: amax_col and scale_col are ignored, even when invalid
+    p = raw_piece(data_col=None, amax_col=B.Buf(BASE + 0x20000001, 1),
+                  scale_col=B.Buf(BASE + 0x40000000, 1))
+    assert B.mxfp8_query_path(p, 2) == 1
+    assert B.mxfp8_query_path(raw_piece(data_col=None, amax_col=B.Buf(None, 0),
+                                        scale_col=B.Buf(None, 0)), 2) == 1
+    # the cast alone needs no amax at all
+    assert B.mxfp8_query_path(raw_piece(amax_row=B.Buf(None, 0), amax_col=B.Buf(None, 0)), 1) == 1
+    assert B.mxfp8_query_path(raw_piece(amax_row=B.Buf(None, 0)), 2) == -B.ERR_MISSING
+
+
+def test_scales_and_cast_layout_and_overlap_errors():
+    q = B.mxfp8_query_path
+    assert q(raw_piece(amax_row=B.Buf(BASE + 0x10000000, 1)), 2) == -B.ERR_LAYOUT  # ld < 2
+    assert q(raw_piece(amax_col=B.Buf(BASE + 0x20000002 - 1, 64)), 2) == -B.ERR_LAYOUT
+    assert q(raw_piece(scale_col=B.Buf(BASE + 0x40000000, 63)), 2) == -B.ERR_LAYOUT
+    # written scales or data overlapping what the call reads, or each other
+    cases = [dict(scale_row=B.Buf(BASE + 0x10000000, 2)),            # scale_row on amax_row
+             dict(scale_col=B.Buf(BASE + 0x20000000 + 64, 64)),     # scale_col on amax_col
+             dict(scale_row=B.Buf(BASE + 8, 2)),                    # scale_row on input
+             dict(data_row=BASE + 0x10000000),                      # data_row on amax_row
+             dict(data_col=BASE + 0x20000000 + 2),                  # data_col on amax_col
+             dict(scale_col=B.Buf(BASE + 0x30000000 + 64, 64)),     # scale_col on scale_row
+             dict(data_row=BASE + 0x40000000)]                      # data_row on scale_col
+    for c in cases:
+        assert q(raw_piece(**c), 2) == -B.ERR_LAYOUT, c
+        assert "overlaps" in B.mxfp8_last_error()
 
 
 def test_omitted_columnwise_output_ignores_its_scales():
@@ -179,6 +220,7 @@ def test_query_path_selects_vector_kernel_for_whole_block_rows():
     assert q(raw_piece(rows=40, cols=40), 1) == 0
     assert q(raw_piece(rows=0), 0) == -B.ERR_ARG
     assert q(raw_piece(), 5) == -B.ERR_ARG
+    assert q(raw_piece(), 2) == 1 and q(raw_piece(rows=40, cols=40), 2) == 0
 
 
 # ------------------------------------------------------------------ binding marshalling

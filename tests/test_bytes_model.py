@@ -33,3 +33,5 @@ def test_bytes_per_element_at_full_size():
     assert b["touched_row"] == n // 32 and b["touched_col"] == n // 32
     assert b["amax"] / n == pytest.approx(2 + 2 * 2 * 2 / 32)
     assert b["cast"] / n == pytest.approx(2 + 2 / 32 + 2)
+    # fused: each element's share of its two blocks' amax entries (2 bytes) and scales (1)
+    assert b["scales_cast"] / n == pytest.approx(2 + 2 * (2 + 1) / 32 + 2)

@@ -1,0 +1,307 @@
+"""GPU parity of the fused scales + cast (mxfp8_scales_and_cast), byte for byte against the
+oracle's two steps run one after the other: compute_scales over the piece's fragment, then
+partial_cast.  The amax it reads are arbitrary non-negative values (zero, subnormal, every
+binade), not only those of the data, and every scale byte outside the touched blocks must
+keep its previous value.  Covers both kernels (vector and element-wise), short last bands,
+tiny fragments, several pieces of one weight in one call, fragment-sized outputs at every
+byte offset, own-buffer inputs, row-only calls, BF16 pre-rounding, and the whole writeback
+with the fused stage on the five workloads."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp8_block_scaled_partial_amd import binding as B
+from mxfp8_block_scaled_partial_amd import workloads as wl
+from mxfp8_block_scaled_partial_amd import writeback as W
+
+from gpu_util import (DEV, assert_same, bits, first_mismatch, require_gpu, run_matrix, to_dev,
+                      to_np)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xEE  # scale bytes the call must not touch keep this value
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def splits(n, k, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cuts = np.sort(g.integers(0, n + 1, k - 1))
+    cuts = np.concatenate([[0], cuts, [n]])
+    return [(int(a), int(b - a)) for a, b in zip(cuts[:-1], cuts[1:])]
+
+
+def random_amax(shape, dtype, seed):
+    """Non-negative amax entries over the whole finite range, zeros and subnormals included."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    if dtype == "bf16":
+        a = g.integers(0, 0x7F80, size=shape, dtype=np.uint16)
+        a[g.random(shape) < 0.05] = 0
+        return a
+    a = g.integers(0, 0x7F800000, size=shape, dtype=np.uint32)
+    a[g.random(shape) < 0.05] = 0
+    return a.view(np.float32)
+
+
+def u8_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def amax_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def expected(x, rows, cols, frags, ar, ac, pre):
+    """Oracle: for each fragment, its touched scales, then its cast (full-size data)."""
+    n = rows * cols
+    nb, nbands = oracle.nblocks(cols), oracle.nblocks(rows)
+    sr = np.full((rows, nb), SENTINEL, np.uint8)
+    sc = np.full((nbands, cols), SENTINEL, np.uint8) if ac is not None else None
+    dr = np.zeros(n, np.uint8)
+    dc = np.zeros(n, np.uint8) if ac is not None else None
+    for s, l in frags:
+        if l == 0:
+            continue
+        oracle.compute_scales(rows, cols, s, l, ar, sr, ac, sc)
+        oracle.partial_cast(x[s:s + l], rows, cols, s, sr, dr[s:s + l], sc,
+                            None if dc is None else dc[s:s + l], pre)
+    return sr, sc, dr, dc
+
+
+def run_fused(x, rows, cols, frags, ar, ac, pre, inputs):
+    """All fragments as pieces of one call, writing full-size outputs in place."""
+    n = rows * cols
+    nb, nbands = oracle.nblocks(cols), oracle.nblocks(rows)
+    xd = to_dev(x)
+    ard = amax_dev(ar)
+    acd = amax_dev(ac) if ac is not None else None
+    sr = torch.full((rows, nb), SENTINEL, dtype=torch.uint8, device=DEV)
+    sc = (torch.full((nbands, cols), SENTINEL, dtype=torch.uint8, device=DEV)
+          if ac is not None else None)
+    dr = torch.zeros(n, dtype=torch.uint8, device=DEV)
+    dc = torch.zeros(n, dtype=torch.uint8, device=DEV) if ac is not None else None
+    keep, pieces = [], []
+    for s, l in frags:
+        xs = xd[s:s + l] if inputs == "views" else xd[s:s + l].clone()
+        keep.append(xs)
+        pieces.append(B.make_piece(rows, cols, s, xs, amax_row=ard, amax_col=acd, scale_row=sr,
+                                   scale_col=sc, data_row=dr[s:s + l],
+                                   data_col=None if dc is None else dc[s:s + l], preround=pre))
+    B.mxfp8_scales_and_cast(pieces)
+    torch.cuda.synchronize()
+    return (to_np(sr), None if sc is None else to_np(sc), to_np(dr),
+            None if dc is None else to_np(dc))
+
+
+def check(got, want, rows, cols, label):
+    names = ("scale_row", "scale_col", "data_row", "data_col")
+    for name, g, w in zip(names, got, want):
+        if w is None:
+            assert g is None, f"{label}{name}: expected absent"
+            continue
+        shape = (rows, cols) if name.startswith("data") else None
+        msg = first_mismatch(g, w, shape)
+        assert not msg, f"{label}{name}: {msg}"
+
+
+SHAPES = [(37, 45), (33, 40), (1, 70), (70, 1), (96, 33), (65, 96), (100, 64), (31, 4128),
+          (64, 64), (2, 32), (40, 1024), (97, 2048)]
+
+
+@pytest.mark.parametrize("rows,cols", SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fused_matches_scales_then_cast(rows, cols, dtype):
+    x = wl.random_matrix(rows, cols, dtype, seed=rows * 11 + cols, kind="mixed")
+    n = rows * cols
+    nb, nbands = oracle.nblocks(cols), oracle.nblocks(rows)
+    ar = random_amax((rows, nb), dtype, seed=rows + 3 * cols)
+    ac_full = random_amax((nbands, cols), dtype, seed=rows * cols + 1)
+    for frags in ([(0, n)], splits(n, 3, rows + cols), splits(n, 6, rows * cols)):
+        for colwise in (True, False):
+            ac = ac_full if colwise else None
+            pres = (False, True) if dtype == "fp32" else (False,)
+            for pre in pres:
+                want = expected(x, rows, cols, frags, ar, ac, pre)
+                for inputs in ("views", "own"):
+                    got = run_fused(x, rows, cols, frags, ar, ac, pre, inputs)
+                    check(got, want, rows, cols,
+                          f"{frags} colwise={colwise} pre={pre} {inputs}: ")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_fused_tiny_fragments(dtype):
+    """Fragments of 1..40 elements at every offset class: only their own blocks' scales."""
+    rows, cols = 70, 96
+    x = wl.random_matrix(rows, cols, dtype, seed=21, kind="mixed")
+    ar = random_amax((rows, 3), dtype, seed=22)
+    ac = random_amax((3, cols), dtype, seed=23)
+    for start in (0, 1, 31, 32, 95, 96, 1000, 3071, 3072, 6700 - 40):
+        for l in (1, 2, 7, 33, 40):
+            if start + l > rows * cols:
+                continue
+            want = expected(x, rows, cols, [(start, l)], ar, ac, False)
+            got = run_fused(x, rows, cols, [(start, l)], ar, ac, False, "own")
+            check(got, want, rows, cols, f"start={start} len={l}: ")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("start", [17, 18, 19, 20, 5, 1030])
+@pytest.mark.parametrize("cols", [128, 1088])
+def test_fused_fragment_sized_outputs(dtype, start, cols):
+    """Data buffers that hold only the fragment, at every byte offset (window stores), with
+    the rank's own input buffer (shifted loads for BF16)."""
+    rows = 96
+    x = wl.random_matrix(rows, cols, dtype, seed=31 + start, kind="mixed")
+    l = rows * cols - start - 300
+    nb, nbands = oracle.nblocks(cols), oracle.nblocks(rows)
+    ar = random_amax((rows, nb), dtype, seed=start)
+    ac = random_amax((nbands, cols), dtype, seed=start + 1)
+    want = expected(x, rows, cols, [(start, l)], ar, ac, False)
+    xs = to_dev(x)[start:start + l].clone()
+    ard, acd = amax_dev(ar), amax_dev(ac)
+    for pad in (0, 1, 2, 3):
+        sr = torch.full((rows, nb), SENTINEL, dtype=torch.uint8, device=DEV)
+        sc = torch.full((nbands, cols), SENTINEL, dtype=torch.uint8, device=DEV)
+        drb = torch.full((l + 8,), 0xA5, dtype=torch.uint8, device=DEV)
+        dcb = torch.full((l + 8,), 0xA5, dtype=torch.uint8, device=DEV)
+        p = B.make_piece(rows, cols, start, xs, amax_row=ard, amax_col=acd, scale_row=sr,
+                         scale_col=sc, data_row=drb[pad:pad + l], data_col=dcb[pad:pad + l])
+        assert B.mxfp8_query_path(p, 2) == 1
+        B.mxfp8_scales_and_cast(p)
+        torch.cuda.synchronize()
+        gr, gc = to_np(drb), to_np(dcb)
+        assert not first_mismatch(to_np(sr), want[0]), pad
+        assert not first_mismatch(to_np(sc), want[1]), pad
+        assert not first_mismatch(gr[pad:pad + l], want[2][start:start + l]), pad
+        assert not first_mismatch(gc[pad:pad + l], want[3][start:start + l]), pad
+        assert (gr[:pad] == 0xA5).all() and (gr[pad + l:] == 0xA5).all()
+        assert (gc[:pad] == 0xA5).all() and (gc[pad + l:] == 0xA5).all()
+
+
+def test_fused_padded_leading_dimensions_and_unaligned_scale_rows():
+    """amax and scale arrays with padded rows (ld > width, odd ld for the scales: column
+    scale rows at every byte offset); padding is neither read nor written."""
+    rows, cols = 100, 192
+    x = wl.random_matrix(rows, cols, "bf16", seed=41, kind="mixed")
+    nb, nbands = oracle.nblocks(cols), oracle.nblocks(rows)
+    ar = random_amax((rows, nb), "bf16", seed=42)
+    ac = random_amax((nbands, cols), "bf16", seed=43)
+    frags = splits(rows * cols, 4, 44)
+    want = expected(x, rows, cols, frags, ar, ac, False)
+    ard = torch.zeros(rows, nb + 5, dtype=torch.bfloat16, device=DEV)
+    acd = torch.zeros(nbands, cols + 3, dtype=torch.bfloat16, device=DEV)
+    ard[:, :nb] = amax_dev(ar)
+    acd[:, :cols] = amax_dev(ac)
+    srb = torch.full((rows, nb + 3), SENTINEL, dtype=torch.uint8, device=DEV)
+    scb = torch.full((nbands, cols + 1), SENTINEL, dtype=torch.uint8, device=DEV)
+    dr = torch.zeros(rows * cols, dtype=torch.uint8, device=DEV)
+    dc = torch.zeros(rows * cols, dtype=torch.uint8, device=DEV)
+    xd = to_dev(x)
+    pieces = [B.make_piece(rows, cols, s, xd[s:s + l], amax_row=ard[:, :nb],
+                           amax_col=acd[:, :cols], scale_row=srb[:, :nb], scale_col=scb[:, :cols],
+                           data_row=dr[s:s + l], data_col=dc[s:s + l]) for s, l in frags]
+    B.mxfp8_scales_and_cast(pieces)
+    torch.cuda.synchronize()
+    srn, scn = to_np(srb), to_np(scb)
+    assert not first_mismatch(srn[:, :nb], want[0])
+    assert not first_mismatch(scn[:, :cols], want[1])
+    assert (srn[:, nb:] == SENTINEL).all() and (scn[:, cols:] == SENTINEL).all()
+    assert not first_mismatch(to_np(dr), want[2], (rows, cols))
+    assert not first_mismatch(to_np(dc), want[3], (rows, cols))
+
+
+def test_fused_row_only_ignores_columnwise_buffers():
+    """data_col absent: amax_col and scale_col are neither read nor written, even if set."""
+    rows, cols = 64, 256
+    x = wl.random_matrix(rows, cols, "fp32", seed=51, kind="normal")
+    ar = random_amax((rows, 8), "fp32", seed=52)
+    want = expected(x, rows, cols, [(100, 9000)], ar, None, False)
+    sr = torch.full((rows, 8), SENTINEL, dtype=torch.uint8, device=DEV)
+    sc = torch.full((2, cols), SENTINEL, dtype=torch.uint8, device=DEV)
+    ac = torch.full((2, cols), float("nan"), dtype=torch.float32, device=DEV)
+    dr = torch.zeros(9000, dtype=torch.uint8, device=DEV)
+    xd = to_dev(x)[100:9100]
+    B.mxfp8_scales_and_cast(B.make_piece(rows, cols, 100, xd, amax_row=amax_dev(ar),
+                                         amax_col=ac, scale_row=sr, scale_col=sc, data_row=dr))
+    torch.cuda.synchronize()
+    assert not first_mismatch(to_np(sr), want[0])
+    assert not first_mismatch(to_np(dr), want[2][100:9100])
+    assert (to_np(sc) == SENTINEL).all()
+
+
+# ------------------------------------------------------------------ the whole writeback, fused
+
+
+def _w(m, run, colwise=True, pre=False, inputs="views", shared=True):
+    want = oracle.writeback(m.data, m.rows, m.cols, m.runs[run], colwise, pre)
+    got = run_matrix(m.data, m.rows, m.cols, m.runs[run], colwise, pre, inputs=inputs,
+                     shared=shared, fused=True)
+    assert_same(got, want, m.rows, m.cols, f"{run} fused: ")
+
+
+@pytest.mark.parametrize("inputs", ["views", "own"])
+def test_writeback_fused_small_and_rowonly(inputs):
+    m = wl.matrix_small()
+    _w(m, "full", inputs=inputs)
+    _w(m, "partial", inputs=inputs)
+    r = wl.matrix_rowonly_fragments()
+    _w(r, "fragments", colwise=False, inputs=inputs, shared=False)
+
+
+@pytest.mark.parametrize("dtype,pre", [("bf16", False), ("fp32", False), ("fp32", True)])
+def test_writeback_fused_square(dtype, pre):
+    m = wl.matrix_square(dtype)
+    _w(m, "full", pre=pre)
+    _w(m, "partial", pre=pre, inputs="own")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_writeback_fused_large_four_fragments(dtype):
+    """The launch configuration the benchmark times: 16384 x 6144 as 4 fragments with cuts
+    inside blocks, one packed amax per fragment, MAX-combined, then the fused stage."""
+    m = wl.matrix_large(dtype)
+    n = m.rows * m.cols
+    cuts = [0, n // 4 + 17, n // 2 + 17, 3 * n // 4 + 17, n]
+    four = [(cuts[i], cuts[i + 1] - cuts[i]) for i in range(4)]
+    want = oracle.writeback(m.data, m.rows, m.cols, m.runs["full"], True)
+    got = run_matrix(m.data, m.rows, m.cols, four, True, inputs="views", shared=False,
+                     fused=True)
+    assert_same(got, want, m.rows, m.cols, "4 fragments fused: ")
+    got = run_matrix(m.data, m.rows, m.cols, m.runs["partial"], True, inputs="views",
+                     fused=True)
+    assert_same(got, oracle.writeback(m.data, m.rows, m.cols, m.runs["partial"], True),
+                m.rows, m.cols, "partial fused: ")
+
+
+def test_writeback_fused_layer_batch():
+    batch = wl.layer_batch()
+    specs = [W.WeightSpec(r, c, colwise) for (_, r, c, colwise) in batch.tensors]
+    x_dev = to_dev(batch.data)
+    for shared in (True, False):
+        wb = W.Writeback(specs, torch.bfloat16, DEV, batch.fragments, shared=shared, fused=True)
+        plan = wb.plan([x_dev[s:s + l] for s, l in batch.fragments])
+        assert [n for n, _ in plan.stages()][-1] == "scales_cast"
+        plan.run()
+        torch.cuda.synchronize()
+        for i, (name, r, c, colwise) in enumerate(batch.tensors):
+            o = batch.offsets[i]
+            pieces = []
+            for fs, fl in batch.fragments:
+                lo, hi = max(fs, o), min(fs + fl, o + r * c)
+                if lo < hi:
+                    pieces.append((lo - o, hi - lo))
+            want = oracle.writeback(batch.data[o:o + r * c], r, c, pieces, colwise)
+            ar, ac = wb.combined.views(i)
+            st = wb.storage[i]
+            got = {"amax_row": to_np(ar), "amax_col": to_np(ac) if colwise else None,
+                   "scale_row": to_np(st.scale_row),
+                   "scale_col": to_np(st.scale_col) if colwise else None,
+                   "data_row": to_np(st.data_row),
+                   "data_col": to_np(st.data_col) if colwise else None}
+            assert_same(got, want, r, c, f"{name} shared={shared}: ")
