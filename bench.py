@@ -258,7 +258,7 @@ def main():
 
 def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
-    scales + cast: full input and
+    scales + cast and (full input only) the single-pass quantize: full input and
     the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Timed like the
     pages: HIP events around replays of a captured graph of 10 calls, median per call over the
     replays.  Calls rotate over distinct buffer sets holding >= the footprint option in all
@@ -313,11 +313,16 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
                 assert B.mxfp8_query_path(amax_p[-1], 0) == 1
                 assert B.mxfp8_query_path(cast_p[-1], 1) == 1
                 assert B.mxfp8_query_path(fused_p[-1], 2) == 1
+                assert run != "full" or B.mxfp8_query_path(fused_p[-1], 3) == 1
             pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
-            # the amax runs first, so the fused call reads real amax entries
-            for kname, pieces, fn in (("amax", amax_p, B.mxfp8_partial_amax),
-                                      ("cast", cast_p, B.mxfp8_partial_cast),
-                                      ("scales_cast", fused_p, B.mxfp8_scales_and_cast)):
+            # the amax runs first, so the fused call reads real amax entries; the single-pass
+            # quantize needs whole bands, so it runs on the full input only
+            kernels = [("amax", amax_p, B.mxfp8_partial_amax),
+                       ("cast", cast_p, B.mxfp8_partial_cast),
+                       ("scales_cast", fused_p, B.mxfp8_scales_and_cast)]
+            if run == "full":
+                kernels.append(("quantize", fused_p, B.mxfp8_quantize))
+            for kname, pieces, fn in kernels:
                 for i in range(3):
                     fn(pieces[i % n_sets])
                 torch.cuda.synchronize()

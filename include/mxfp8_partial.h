@@ -142,11 +142,27 @@ int mxfp8_partial_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
  * fragments share a cut block write the same scale byte. */
 int mxfp8_scales_and_cast(const mxfp8_piece* pieces, int n, void* hip_stream);
 
+/* Steps 1, 3 and 4 in one pass over a fragment that needs no combine (the steps of the flow
+ * diagram around the all-reduce, fused by this library for fragments that own all their
+ * blocks).  The fragment must consist of whole 32-row bands: start a multiple of 32 * cols
+ * and start + len a multiple of 32 * cols or equal to rows * cols (the whole weight is one
+ * such fragment); otherwise MXFP8_ERR_RANGE.  Every block it touches then lies wholly
+ * inside it, so its amax are final: the call computes them, writes them to amax_row /
+ * amax_col when those are given (overwriting, not merging), and writes the E8M0 scales and
+ * the E4M3 data exactly as mxfp8_partial_amax into zero-filled amax, mxfp8_compute_scales
+ * and mxfp8_partial_cast would.  The input is read once.  The column-wise work (amax_col,
+ * scale_col, data_col) happens iff data_col != NULL, which then requires scale_col; when
+ * data_col is NULL, amax_col and scale_col are ignored.  Required: input, scale_row,
+ * data_row; amax_row and amax_col are optional outputs.  Outputs must not overlap the input
+ * or each other.  Reads: rows, cols, start, len, in_dtype, preround_bf16, input, amax_row,
+ * amax_col, scale_row, scale_col, data_row, data_col. */
+int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream);
+
 /* Message for the calling thread's last non-OK status (static storage, thread-local). */
 const char* mxfp8_last_error(void);
 
 /* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast,
- * 2 = scales and cast (validated as for mxfp8_scales_and_cast; it takes the cast's path):
+ * 2 = scales and cast, 3 = quantize (each validated as for its entry point):
  * 1 = the vectorized path (16-byte loads of row segments of whole 32-value blocks, for any
  * cols % 32 == 0, whatever the alignment of input and outputs), 0 = the element-wise path
  * (cols % 32 != 0), negative = the piece fails validation (the status code, negated).

@@ -25,7 +25,8 @@ STATUS_NAMES = {OK: "OK", ERR_ARG: "ERR_ARG", ERR_RANGE: "ERR_RANGE", ERR_DTYPE:
 
 # every entry point declared in include/mxfp8_partial.h
 EXPORTS = ("mxfp8_partial_amax", "mxfp8_combine_amax", "mxfp8_compute_scales",
-           "mxfp8_partial_cast", "mxfp8_scales_and_cast", "mxfp8_last_error", "mxfp8_query_path")
+           "mxfp8_partial_cast", "mxfp8_scales_and_cast", "mxfp8_quantize", "mxfp8_last_error",
+           "mxfp8_query_path")
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -67,7 +68,7 @@ def lib():
             raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
         PP = ctypes.POINTER(Piece)
         for name in ("mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast",
-                     "mxfp8_scales_and_cast"):
+                     "mxfp8_scales_and_cast", "mxfp8_quantize"):
             f = getattr(L, name)
             f.argtypes = [PP, ctypes.c_int, ctypes.c_void_p]
             f.restype = ctypes.c_int
@@ -235,6 +236,12 @@ def mxfp8_scales_and_cast(pieces, stream=None) -> None:
     """mxfp8_compute_scales then mxfp8_partial_cast, in one pass over the fragment."""
     arr, n = _array(pieces)
     _check(lib().mxfp8_scales_and_cast(arr, n, _stream(stream)))
+
+
+def mxfp8_quantize(pieces, stream=None) -> None:
+    """amax, scales and cast in one pass, for fragments made of whole 32-row bands."""
+    arr, n = _array(pieces)
+    _check(lib().mxfp8_quantize(arr, n, _stream(stream)))
 
 
 def mxfp8_query_path(piece: Piece, kernel: int) -> int:

@@ -14,6 +14,8 @@ T_col the row-wise / column-wise blocks the fragment touches:
   partial cast    len * s_in + (T_row + T_col) * 1 + len * D
   scales + cast   len * s_in + (T_row + T_col) * (s_in + 1) + len * D   (fused: amax entries
                   read, scale bytes written, no scale read-back)
+  quantize        len * s_in + (T_row + T_col) * (s_in + 1) + len * D   (single pass over
+                  whole bands: input read once, amax and scales written once)
   combine         (K + 1) * P * s_in     (K partial packed buffers of P entries -> one)
   zero-fill       K * P * s_in
 """
@@ -58,7 +60,8 @@ def touched_col_blocks(rows: int, cols: int, start: int, length: int) -> int:
 
 
 def piece_bytes(rows: int, cols: int, start: int, length: int, s_in: int, colwise: bool):
-    """Per-step algorithmic bytes of one piece: dict with amax, scales, cast, scales_cast."""
+    """Per-step algorithmic bytes of one piece: dict with amax, scales, cast, scales_cast,
+    quantize."""
     tr = touched_row_blocks(rows, cols, start, length)
     tc = touched_col_blocks(rows, cols, start, length) if colwise else 0
     d = 2 if colwise else 1
@@ -66,6 +69,7 @@ def piece_bytes(rows: int, cols: int, start: int, length: int, s_in: int, colwis
             "scales": (tr + tc) * (s_in + 1),
             "cast": length * s_in + (tr + tc) + length * d,
             "scales_cast": length * s_in + (tr + tc) * (s_in + 1) + length * d,
+            "quantize": length * s_in + (tr + tc) * (s_in + 1) + length * d,
             "touched_row": tr, "touched_col": tc}
 
 

@@ -48,9 +48,9 @@ Span span1d(const void* p, int64_t bytes) {
 
 int64_t nblk(int64_t n) { return (n + 31) / 32; }
 
-enum Kind { kAmax, kScales, kCast, kFused };
+enum Kind { kAmax, kScales, kCast, kFused, kQuant };
 const char* kKindName[] = {"mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast",
-                           "mxfp8_scales_and_cast"};
+                           "mxfp8_scales_and_cast", "mxfp8_quantize"};
 
 bool aligned(const void* p, int64_t a) { return reinterpret_cast<uintptr_t>(p) % (uintptr_t)a == 0; }
 
@@ -76,6 +76,14 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
   if (q.len == 0) {  // empty master shard: a no-op
     *skip = true;
     return MXFP8_OK;
+  }
+  if (kind == kQuant) {  // every touched block must lie wholly inside the fragment
+    const int64_t band = 32 * q.cols;
+    const int64_t end = q.start + q.len;
+    if (q.start % band != 0 || (end != n && end % band != 0))
+      return fail(MXFP8_ERR_RANGE,
+                  "%s: piece %d: fragment [%lld, %lld) does not cover whole 32-row bands", fn,
+                  idx, (long long)q.start, (long long)end);
   }
   const int64_t esz = mxfp8::elem_size(q.in_dtype);
   const int64_t nb = nblk(q.cols), nbands = nblk(q.rows);
@@ -145,7 +153,13 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
         (st = need_amax(q.amax_col, q.cols, "amax_col", true, &p.amax_col, &p.ld_ac)))
       return st;
   }
-  if (kind == kCast || kind == kFused) {
+  if (kind == kQuant) {  // amax are optional outputs; the column-wise ones follow data_col
+    if ((st = need_amax(q.amax_row, nb, "amax_row", false, &p.amax_row, &p.ld_ar))) return st;
+    if (q.data_col &&
+        (st = need_amax(q.amax_col, q.cols, "amax_col", false, &p.amax_col, &p.ld_ac)))
+      return st;
+  }
+  if (kind == kCast || kind == kFused || kind == kQuant) {
     if (!q.data_row) return fail(MXFP8_ERR_MISSING, "%s: piece %d: data_row is required", fn, idx);
     if ((st = need_scale(q.scale_row, nb, "scale_row", true, &p.scale_row, &p.ld_sr))) return st;
     p.data_row = static_cast<uint8_t*>(q.data_row);
@@ -182,7 +196,11 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
         (st = clash(sr, sc, "scale_row", "scale_col")))
       return st;
   } else {
-    if (kind == kFused &&
+    if (kind == kQuant &&  // the amax are outputs here
+        ((st = clash(ar, in, "amax_row", "input")) || (st = clash(ac, in, "amax_col", "input")) ||
+         (st = clash(ar, ac, "amax_row", "amax_col"))))
+      return st;
+    if ((kind == kFused || kind == kQuant) &&
         ((st = clash(sr, in, "scale_row", "input")) || (st = clash(sc, in, "scale_col", "input")) ||
          (st = clash(sr, sc, "scale_row", "scale_col")) ||
          (st = clash(sr, ar, "scale_row", "amax_row")) || (st = clash(sr, ac, "scale_row", "amax_col")) ||
@@ -246,6 +264,10 @@ int mxfp8_scales_and_cast(const mxfp8_piece* pieces, int n, void* hip_stream) {
   return run_pieces(pieces, n, hip_stream, kFused, mxfp8::launch_scales_and_cast);
 }
 
+int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream) {
+  return run_pieces(pieces, n, hip_stream, kQuant, mxfp8::launch_quantize);
+}
+
 int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
                        int32_t amax_dtype, void* hip_stream) {
   const char* fn = "mxfp8_combine_amax";
@@ -278,12 +300,12 @@ const char* mxfp8_last_error(void) { return g_err; }
 
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel) {
   if (!piece) return -fail(MXFP8_ERR_ARG, "mxfp8_query_path: piece is NULL");
-  if (kernel < 0 || kernel > 2)
-    return -fail(MXFP8_ERR_ARG,
-                 "mxfp8_query_path: kernel must be 0 (amax), 1 (cast) or 2 (scales and cast)");
+  if (kernel < 0 || kernel > 3)
+    return -fail(MXFP8_ERR_ARG, "mxfp8_query_path: kernel must be 0 (amax), 1 (cast), 2 "
+                                "(scales and cast) or 3 (quantize)");
   mxfp8::Piece p;
   bool skip;
-  const Kind kinds[3] = {kAmax, kCast, kFused};
+  const Kind kinds[4] = {kAmax, kCast, kFused, kQuant};
   const int st = check_piece(*piece, kinds[kernel], 0, &p, &skip);
   if (st) return -st;
   if (skip) return 0;

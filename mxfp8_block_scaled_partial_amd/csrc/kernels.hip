@@ -946,6 +946,128 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   }
 }
 
+// ------------------------------------------------------------------ single-pass quantize
+
+// A fragment made of whole 32-row bands holds every block it touches entirely, so its block
+// amax are final without any combine: one pass reads each tile once, keeps it in registers,
+// reduces the row-wise blocks with DPP and the column-wise blocks over the four waves in LDS,
+// and writes the amax (when requested), the E8M0 scales and the E4M3 data.  All loads are
+// issued before the first store.
+template <typename T, bool kCol, bool kPre, int kOcc>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int LB = kBlockLen / E;
+  constexpr int WC = kWaveSize * E;
+  constexpr int RW = kRowsPerWave;
+  __shared__ uint4 s_col[kWavesPerGroup][kWaveSize];
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x >> 6;
+  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
+  if (tile >= p.ntiles) return;  // uniform over the workgroup
+  const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
+  const int64_t band = p.band0 + bq;
+  const int64_t c0 = (int64_t)(t32 - bq * n32) * WC;
+  const int64_t c = c0 + lane * E;
+  const int64_t r0 = band * kBlockLen;
+  const bool cvalid = c < p.cols;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int i0 = wave * RW;
+  const int nr = nrows - i0;  // rows of this wave inside the weight (uniform; may be <= 0)
+
+  const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
+  uint32_t d[RW][4];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+  if (cvalid) {
+    if (nr >= RW) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        if (i < nr) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
+    }
+  }
+
+  // amax: rows absent from a short last band, and lanes past the last column, hold zeros
+  uint32_t col[4] = {0, 0, 0, 0};
+  uint32_t rmax[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) rmax[i] = group_max<LB>(chunk_absmax<T, kCol, kPre>(d[i], col));
+  if constexpr (kCol) {
+    s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w)
+      if (w != wave) fold_col<T>(col, s_col[w][lane]);
+  }
+
+  // row-wise amax and scales: the first lane of each block writes them
+  int rshift[RW];
+  const bool writer = (lane % LB) == 0 && cvalid;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const uint8_t sb = e8m0_of<T>(rmax[i]);
+    rshift[i] = 127 - (int)sb;
+    if (writer && i < nr) {
+      const int64_t r = r0 + i0 + i;
+      p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
+      if (p.amax_row) static_cast<T*>(p.amax_row)[r * p.ld_ar + (c >> 5)] = (T)rmax[i];
+    }
+  }
+  int cshift[E];
+  uint8_t csb[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    csb[e] = kCol ? e8m0_of<T>(col_entry<T>(col, e)) : 0;
+    cshift[e] = 127 - (int)csb[e];
+  }
+
+  // data: direct stores when the outputs are dword aligned, else window stores
+  const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
+  const int64_t cend = min<int64_t>(c0 + WC, p.cols);
+  const bool first = lane == 0, last = c + E == cend;
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const bool valid = cvalid && i < nr;
+    const int64_t o = o0 + i * p.cols;
+    uint32_t q[E / 4];
+    quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+    if (p.mo_row)
+      store_window<E>(p.data_row + o, q, p.mo_row, valid, first, last);
+    else if (valid)
+      store_bytes<E>(p.data_row + o, q);
+    if constexpr (kCol) {
+      quantize_chunk<T, kPre>(d[i], cshift, true, q);
+      if (p.mo_col)
+        store_window<E>(p.data_col + o, q, p.mo_col, valid, first, last);
+      else if (valid)
+        store_bytes<E>(p.data_col + o, q);
+    }
+  }
+
+  // column-wise amax and scales: wave 0 writes them
+  if constexpr (kCol) {
+    if (wave == 0 && cvalid) {
+      store_scale_bytes<E>(p.scale_col + band * p.ld_sc + c, csb, (1u << E) - 1);
+      if (p.amax_col) {
+        T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
+        if (p.col_vec) {
+          *reinterpret_cast<uint4*>(ac) = make_uint4(col[0], col[1], col[2], col[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < E; ++e) ac[e] = (T)col_entry<T>(col, e);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ element-wise path (any layout)
 
 constexpr int kElemTileCols = kWaveSize;  // one lane per column
@@ -1025,6 +1147,57 @@ __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
     const float w = work_value<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
     p.data_row[g - p.start] = cvt1(w, 127 - (int)sb);
     if constexpr (kCol) p.data_col[g - p.start] = cvt1(w, cshift);
+  }
+}
+
+// Single-pass quantize for any layout: a wave per (band, 64 columns), one lane per column,
+// the band's 32 values of the column held in registers.
+template <typename T, bool kCol, bool kPre>
+__global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
+  if (tile >= p.ntiles) return;
+  const int64_t band = p.band0 + tile / p.ntc;
+  const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
+  const int64_t r0 = band * kBlockLen;
+  const bool cvalid = c < p.cols;
+  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  uint32_t raw[kBlockLen];
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i)
+    raw[i] = (cvalid && i < nrows)
+                 ? load_raw(p.input, (r0 + i) * p.cols + c - p.start, (int)sizeof(T))
+                 : 0u;
+  int cshift = 0;
+  if constexpr (kCol) {
+    uint32_t cmax = 0;
+#pragma unroll
+    for (int i = 0; i < kBlockLen; ++i) cmax = umax(cmax, abs_bits<T, kPre>(raw[i]));
+    const uint8_t sb = e8m0_of<T>(cmax);
+    cshift = 127 - (int)sb;
+    if (cvalid) {
+      p.scale_col[band * p.ld_sc + c] = sb;
+      if (p.amax_col) static_cast<T*>(p.amax_col)[band * p.ld_ac + c] = (T)cmax;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i) {
+    if (i >= nrows) break;
+    const int64_t r = r0 + i;
+    const uint32_t m = half_wave_max(abs_bits<T, kPre>(raw[i]));  // the lane's row-wise block
+    const uint8_t sb = e8m0_of<T>(m);
+    if (cvalid && (lane & 31) == 0) {
+      p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
+      if (p.amax_row) static_cast<T*>(p.amax_row)[r * p.ld_ar + (c >> 5)] = (T)m;
+    }
+    if (!cvalid) continue;
+    const float w = work_value<T, kPre>(raw[i]);
+    const int64_t o = r * p.cols + c - p.start;
+    p.data_row[o] = cvt1(w, 127 - (int)sb);
+    if constexpr (kCol) p.data_col[o] = cvt1(w, cshift);
   }
 }
 
@@ -1321,6 +1494,38 @@ hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
   run(launch_amax_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
   run(launch_amax_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
   run(launch_amax_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
+  return e;
+}
+
+template <typename T, bool kCol, bool kPre>
+hipError_t launch_quantize_bucket(const std::vector<TileArgs>& vec,
+                                  const std::vector<TileArgs>& elem, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  if (!vec.empty())
+    e = launch_grouped(quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
+                       quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, s);
+  if (e == hipSuccess && !elem.empty())
+    e = launch_grouped(quantize_elem_kernel<T, kCol, kPre>, quantize_elem_kernel<T, kCol, kPre>,
+                       elem, kWavesPerGroup, s);
+  return e;
+}
+
+hipError_t launch_quantize(const Piece* ps, int n, hipStream_t s) {
+  Buckets bk;
+  for (int i = 0; i < n; ++i) {
+    const Piece& p = ps[i];
+    const bool vec = vec_common_ok(p);
+    const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
+    bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
+  }
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  run(launch_quantize_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
+  run(launch_quantize_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
+  run(launch_quantize_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
+  run(launch_quantize_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
+  run(launch_quantize_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
+  run(launch_quantize_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
   return e;
 }
 

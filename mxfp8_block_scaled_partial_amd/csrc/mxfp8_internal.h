@@ -38,6 +38,8 @@ hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s);
 // The cast with the scales computed from the amax on the fly (and written for touched blocks).
 hipError_t launch_scales_and_cast(const Piece* ps, int n, hipStream_t s);
+// amax, scales and cast in one pass, for fragments of whole 32-row bands.
+hipError_t launch_quantize(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,
                           hipStream_t s);

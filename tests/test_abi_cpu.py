@@ -79,9 +79,10 @@ def call(fn, *pieces):
 
 AMAX, SCALES, CAST = "mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast"
 FUSED = "mxfp8_scales_and_cast"
+QUANT = "mxfp8_quantize"
 
 
-@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED])
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED, QUANT])
 def test_shape_range_dtype_errors(fn):
     assert call(fn, raw_piece(rows=0)) == B.ERR_ARG
     assert call(fn, raw_piece(cols=-3)) == B.ERR_ARG
@@ -98,10 +99,11 @@ def test_preround_needs_fp32():
     assert call(AMAX, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
     assert call(CAST, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
     assert call(FUSED, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
+    assert call(QUANT, raw_piece(dtype=B.BF16, pre=1)) == B.ERR_DTYPE
     assert call(AMAX, raw_piece(dtype=B.BF16, pre=2)) == B.ERR_ARG
 
 
-@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED])
+@pytest.mark.parametrize("fn", [AMAX, SCALES, CAST, FUSED, QUANT])
 def test_empty_fragment_is_a_no_op_even_with_null_buffers(fn):
     p = B.Piece(64, 64, 17, 0, B.BF16, 0, None, B.Buf(None, 0), B.Buf(None, 0), B.Buf(None, 0),
                 B.Buf(None, 0), None, None)
@@ -158,6 +160,42 @@ def test_scales_and_cast_layout_and_overlap_errors():
              dict(data_row=BASE + 0x40000000)]                      # data_row on scale_col
     for c in cases:
         assert q(raw_piece(**c), 2) == -B.ERR_LAYOUT, c
+        assert "overlaps" in B.mxfp8_last_error()
+
+
+def test_quantize_needs_whole_bands():
+    q = B.mxfp8_query_path
+    # 100 x 64: bands of 32 rows = 2048 elements; the last band is short (4 rows)
+    assert q(raw_piece(rows=100, cols=64), 3) == 1                      # the whole weight
+    assert q(raw_piece(rows=100, cols=64, start=2048, length=4096), 3) == 1
+    assert q(raw_piece(rows=100, cols=64, start=6144, length=256), 3) == 1  # short last band
+    assert q(raw_piece(rows=100, cols=64, start=2048, length=2048), 3) == 1
+    for s, l in ((1, 2047), (0, 2047), (2048, 100), (32, 2016), (0, 6399)):
+        assert q(raw_piece(rows=100, cols=64, start=s, length=l), 3) == -B.ERR_RANGE, (s, l)
+        assert "32-row bands" in B.mxfp8_last_error()
+    assert call(QUANT, raw_piece(rows=100, cols=64, start=64, length=64)) == B.ERR_RANGE
+    # element-wise layout for cols % 32 != 0
+    assert q(raw_piece(rows=40, cols=40), 3) == 0
+
+
+def test_quantize_buffers():
+    q = B.mxfp8_query_path
+    # amax are optional outputs
+    assert q(raw_piece(amax_row=B.Buf(None, 0), amax_col=B.Buf(None, 0)), 3) == 1
+    assert call(QUANT, raw_piece(data_row=None)) == B.ERR_MISSING
+    assert call(QUANT, raw_piece(scale_row=B.Buf(None, 0))) == B.ERR_MISSING
+    assert call(QUANT, raw_piece(scale_col=B.Buf(None, 0))) == B.ERR_MISSING
+    assert call(QUANT, raw_piece(input=None)) == B.ERR_ARG
+    # row-only: column-wise buffers ignored, even when invalid
+    assert q(raw_piece(data_col=None, amax_col=B.Buf(BASE + 1, 1), scale_col=B.Buf(None, 0)),
+             3) == 1
+    # a given amax must be laid out correctly and must not overlap anything
+    assert q(raw_piece(amax_row=B.Buf(BASE + 0x10000000, 1)), 3) == -B.ERR_LAYOUT
+    for c in (dict(amax_row=B.Buf(BASE + 64, 2)),                     # amax_row on input
+              dict(amax_col=B.Buf(BASE + 0x10000000, 64)),            # amax_col on amax_row
+              dict(amax_col=B.Buf(BASE + 0x30000000 + 16, 64)),       # amax_col on scale_row
+              dict(data_col=BASE + 0x20000000 + 4)):                  # data_col on amax_col
+        assert q(raw_piece(**c), 3) == -B.ERR_LAYOUT, c
         assert "overlaps" in B.mxfp8_last_error()
 
 
@@ -221,6 +259,7 @@ def test_query_path_selects_vector_kernel_for_whole_block_rows():
     assert q(raw_piece(rows=0), 0) == -B.ERR_ARG
     assert q(raw_piece(), 5) == -B.ERR_ARG
     assert q(raw_piece(), 2) == 1 and q(raw_piece(rows=40, cols=40), 2) == 0
+    assert q(raw_piece(), 4) == -B.ERR_ARG
 
 
 # ------------------------------------------------------------------ binding marshalling
