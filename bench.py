@@ -61,6 +61,9 @@ def parse():
                     help="rows of the weight (a band-aligned sample) the oracle processes")
     ap.add_argument("--separate-scales", dest="fused", action="store_false", default=True,
                     help="run the scales and the cast as two calls instead of the fused call")
+    ap.add_argument("--single-pass", dest="single_pass", action="store_true", default=True,
+                    help="also time the writeback that quantizes whole bands in one pass")
+    ap.add_argument("--no-single-pass", dest="single_pass", action="store_false")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain device copy (the counter calibration kernel)")
     return ap.parse_args()
@@ -205,6 +208,17 @@ def main():
                 "launch_us": round(cast_launch_us, 2),
                 "alg_bytes_per_launch": int(cast_bytes_launch)}
 
+    # the same steps replayed from captured graphs (no host launch gaps)
+    def graph_step(j):
+        seq = stages_now(j % n_sets)[:-1] + [stages_now((j - 1) % n_sets)[-1]]
+        for _, fn in seq:
+            fn()
+
+    def stages_now(j):  # built at call time, so inside a capture they use its stream
+        return sets[j][2].stages()
+
+    graph_us = graph_step_us(args, [lambda j=j: graph_step(j) for j in range(n_sets)])
+
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -218,11 +232,18 @@ def main():
                                   else "scales, partial cast"),
                    "rows": rows, "cols": cols, "fragments": frags, "buffer_sets": n_sets,
                    "step_alg_bytes": step_bytes},
+        "graph_us_per_step": graph_us,
+        "graph_GBps": round(step_bytes / (graph_us * 1e-6) / 1e9, 1),
         "stage_us": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
         "stage_alg_GBps": {k: round(stage_bytes[k] / (stage_ms[k] * 1e-3) / 1e9, 1)
                            for k in stage_names},
         "roofline": roofline,
     }
+
+    if args.single_pass:
+        out["single_pass_step"] = {
+            "k_buffers": single_pass_step(args, sets, spec, frags, s_in, dev, tdt, False),
+            "shared_buffer": single_pass_step(args, sets, spec, frags, s_in, dev, tdt, True)}
 
     if args.copy_probe:
         # a plain device-to-device copy of known size (256 MiB per launch, rotating over four
@@ -254,6 +275,103 @@ def main():
         out["cpu_baseline"] = cpu_baseline(m, args.cpu_rows, s_in)
 
     print(json.dumps(out), flush=True)
+
+
+def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
+    """The same writeback with ``single_pass``: each fragment's whole 32-row bands are
+    quantized in one pass (input read once) on a side stream, overlapped with the partial
+    chain for the bands at the cuts (amax -> combine of just their entries -> scales + cast;
+    with ``shared`` the cut blocks merge atomically into one buffer and there is no combine).
+    Same outputs, fewer bytes moved.  Timed with HIP events around each whole step, eagerly
+    and replayed from a captured graph, over the rotating buffer sets."""
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
+    from mxfp8_block_scaled_partial_amd import writeback as W
+
+    plans = []
+    for x, _, _ in sets:
+        wb = W.Writeback([spec], tdt, dev, frags, shared=shared, single_pass=True)
+        plans.append(wb.plan([x[s:s + l] for s, l in frags]))
+    p0 = plans[0]
+    k = 1 if shared else len(frags)
+    rows, cols = spec.rows, spec.cols
+    packed = spec.amax_row_entries + spec.amax_col_entries
+    part = [BM.piece_bytes(rows, cols, a, b - a, s_in, True) for _, a, b in p0.partial_ranges]
+    quant = [BM.piece_bytes(rows, cols, a, b - a, s_in, True) for _, a, b in p0.quant_ranges]
+    shared_entries = 0 if shared else sum(c for _, _, c in p0.wb.combine_calls)
+    stage_bytes = {"zero": BM.zero_bytes(k, packed, s_in),
+                   "amax": sum(p["amax"] for p in part),
+                   "quantize": sum(p["quantize"] for p in quant),
+                   "scales_cast": sum(p["scales_cast"] for p in part)}
+    if not shared:
+        stage_bytes["combine"] = BM.combine_bytes(k, shared_entries, s_in)
+    total = sum(stage_bytes.values())
+
+    # one linear pass with events per stage (no overlap), for the breakdown
+    names = [n for n, _ in p0.stages()]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    stage_runs = []
+    for i in range(args.warmup + 5):
+        for j, (_, fn) in enumerate(plans[i % len(plans)].stages()):
+            ev[j].record()
+            fn()
+        ev[-1].record()
+        torch.cuda.synchronize()
+        stage_runs.append([ev[j].elapsed_time(ev[j + 1]) * 1e3 for j in range(len(names))])
+    stage_us = {n: round(statistics.median(r[j] for r in stage_runs[args.warmup:]), 2)
+                for j, n in enumerate(names)}
+
+    # the overlapped step, eager
+    for i in range(args.warmup):
+        plans[i % len(plans)].run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        plans[(args.warmup + i) % len(plans)].run()
+        e1.record()
+    torch.cuda.synchronize()
+    step_us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)
+    graph_us = graph_step_us(args, [lambda p=p: p.run() for p in plans])
+    return {"us": round(step_us, 2), "graph_us": graph_us, "alg_bytes": total,
+            "GBps": round(total / (step_us * 1e-6) / 1e9, 1),
+            "graph_GBps": round(total / (graph_us * 1e-6) / 1e9, 1),
+            "stage_us_serial": stage_us, "stage_alg_bytes": stage_bytes,
+            "quantize_pieces": p0.n_quant, "partial_pieces": p0.n_cast,
+            "combined_entries": shared_entries,
+            "note": "same outputs as the step; whole bands of each fragment go through the "
+                    "single-pass quantize (input read once) on a second stream, overlapped "
+                    "with the partial chain for the bands at the cuts"}
+
+
+def graph_step_us(args, step_fns):
+    """Median µs of one step replayed from a captured HIP graph (one graph per buffer set,
+    replayed in turn), so no host launch gap sits between the step's kernels."""
+    import torch
+
+    graphs = []
+    for fn in step_fns:
+        fn()  # outside capture first: nothing is first-touched inside the graph
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()  # the library reads torch's current stream: the capture stream here
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        graphs[i % len(graphs)].replay()
+        e1.record()
+    torch.cuda.synchronize()
+    us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    del graphs
+    return round(us, 2)
 
 
 def kernel_table(args, bf16_sets, m_default, dev, tdt_default):

@@ -15,7 +15,13 @@ Validation: mixed row-only / bidirectional batches, fragment outputs, boundaries
   * scales are computed once per weight over the range its fragments cover, and every
     piece is cast in place into caller-owned, full-size MXFP8 storage; with ``fused=True``
     each piece instead derives its scales from the combined amax inside its cast
-    (``mxfp8_scales_and_cast``), so the scales take no pass of their own.
+    (``mxfp8_scales_and_cast``), so the scales take no pass of their own;
+  * with ``single_pass=True`` the whole 32-row bands inside a piece, whose blocks no other
+    fragment touches and whose amax are therefore final without the combine, go through the
+    one-pass ``mxfp8_quantize``, which writes their amax straight into the combined buffer;
+    only the partial bands at the piece's two ends take the amax -> combine -> scales + cast
+    path, the combine covers only their entries (the single-GPU form of all-reducing just
+    the blocks that fragments share), and the two run overlapped on two streams.
 
 All arithmetic runs in the library's kernels; buffers are zero-filled with torch's fill.
 """
@@ -104,13 +110,56 @@ def split_fragment(specs, frag_start: int, frag_len: int):
     return out
 
 
+def whole_bands(spec: WeightSpec, a: int, b: int):
+    """The largest [lo, hi) inside [a, b) made of whole 32-row bands of the weight (the short
+    last band counts as whole); lo >= hi when there is none."""
+    band = 32 * spec.cols
+    lo = -(-a // band) * band
+    hi = b if b == spec.numel else (b // band) * band
+    return lo, hi
+
+
+def boundary_spans(specs, fragments, dtype=torch.float32):
+    """Packed-entry ranges [lo, hi) of the bands that a partial piece (the part of a
+    fragment's piece outside its whole bands) touches, merged: the row-wise entries of the
+    band's rows and, for bidirectional weights, the band's column-wise entries."""
+    spans = []
+    offsets = PackedAmax(specs, dtype, "meta").offsets
+    for fs, fl in fragments:
+        for (i, s, n, _) in split_fragment(specs, fs, fl):
+            spec = specs[i]
+            lo, hi = whole_bands(spec, s, s + n)
+            parts = [(s, s + n)] if lo >= hi else [(s, lo), (hi, s + n)]
+            nb, band = B.nblocks(spec.cols), 32 * spec.cols
+            for a, b in parts:
+                if a >= b:
+                    continue
+                for bd in range(a // band, (b - 1) // band + 1):
+                    r0, r1 = 32 * bd, min(32 * bd + 32, spec.rows)
+                    o = offsets[i]
+                    spans.append((o + r0 * nb, o + r1 * nb))
+                    if spec.colwise:
+                        oc = o + spec.amax_row_entries + bd * spec.cols
+                        spans.append((oc, oc + spec.cols))
+    spans.sort()
+    merged = []
+    for lo, hi in spans:
+        if merged and lo <= merged[-1][1]:
+            merged[-1][1] = max(merged[-1][1], hi)
+        else:
+            merged.append([lo, hi])
+    return [(lo, hi) for lo, hi in merged]
+
+
 class Plan:
     """Prepared C-ABI calls for one set of master fragments (pointers are baked in)."""
 
     def __init__(self, wb: "Writeback", fragments_values):
         self.wb = wb
         self.keep = list(fragments_values)       # keep the tensors alive
-        amax_pieces, cast_pieces = [], []
+        amax_pieces, cast_pieces, quant_pieces = [], [], []
+        # (weight index, start, end) of every amax / cast piece and every quantize piece
+        self.partial_ranges, self.quant_ranges = [], []
         for f, ((fs, fl), x) in enumerate(zip(wb.fragments, self.keep)):
             if x.numel() != fl or x.dtype != wb.dtype:
                 raise ValueError(f"fragment {f}: expected {fl} values of {wb.dtype}")
@@ -118,37 +167,65 @@ class Plan:
             for (i, s, n, off) in split_fragment(wb.specs, fs, fl):
                 spec, st = wb.specs[i], wb.storage[i]
                 ar, ac = packed.views(i)
-                xin = x[off:off + n]
-                amax_pieces.append(B.make_piece(spec.rows, spec.cols, s, xin, amax_row=ar,
-                                                amax_col=ac, preround=wb.preround))
-                car, cac = wb.combined.views(i) if wb.fused else (None, None)
-                cast_pieces.append(B.make_piece(
-                    spec.rows, spec.cols, s, xin, amax_row=car, amax_col=cac,
-                    scale_row=st.scale_row, scale_col=st.scale_col,
-                    data_row=st.data_row[s:s + n],
-                    data_col=st.data_col[s:s + n] if spec.colwise else None,
-                    preround=wb.preround))
+                car, cac = wb.combined.views(i)
+                ranges = [(s, s + n)]
+                if wb.single_pass:
+                    lo, hi = whole_bands(spec, s, s + n)
+                    if lo < hi:
+                        ranges = [(s, lo), (hi, s + n)]
+                        # no other fragment touches these blocks: their amax are final and go
+                        # straight into the combined buffer
+                        quant_pieces.append(self._piece(spec, st, x, off - s, lo, hi, car, cac))
+                        self.quant_ranges.append((i, lo, hi))
+                for a, b in ranges:
+                    if a == b:
+                        continue
+                    xin = x[off + a - s:off + b - s]
+                    amax_pieces.append(B.make_piece(spec.rows, spec.cols, a, xin, amax_row=ar,
+                                                    amax_col=ac, preround=wb.preround))
+                    cast_pieces.append(self._piece(spec, st, x, off - s, a, b,
+                                                   *((car, cac) if wb.fused else (None, None))))
+                    self.partial_ranges.append((i, a, b))
         self.amax = (B.Piece * len(amax_pieces))(*amax_pieces)
         self.cast = (B.Piece * len(cast_pieces))(*cast_pieces)
+        self.quant = (B.Piece * len(quant_pieces))(*quant_pieces)
         self.n_amax, self.n_cast = len(amax_pieces), len(cast_pieces)
+        self.n_quant = len(quant_pieces)
 
-    def stages(self, stream=None):
-        """The writeback as (name, callable) stages, in order: zero-fill of the packed amax,
-        partial amax, MAX-combine (only with one packed buffer per fragment), then scales and
-        cast, or one fused scales-and-cast stage."""
+    def _piece(self, spec, st, x, shift, a, b, amax_row, amax_col):
+        """Piece [a, b) of a weight whose fragment values start at x[a + shift]."""
+        return B.make_piece(
+            spec.rows, spec.cols, a, x[a + shift:b + shift], amax_row=amax_row,
+            amax_col=amax_col, scale_row=st.scale_row, scale_col=st.scale_col,
+            data_row=st.data_row[a:b], data_col=st.data_col[a:b] if spec.colwise else None,
+            preround=self.wb.preround)
+
+    def _calls(self, stream):
+        """The library calls of the writeback on torch stream ``stream``, by name."""
+        import torch
         wb = self.wb
         lib = B.lib()
-        sp = B._stream(stream)
+        code = B.dtype_code(wb.dtype)
+        sp = stream.cuda_stream
 
         def zero():
-            wb.packed_storage.zero_()
+            with torch.cuda.stream(stream):
+                wb.packed_storage.zero_()
+
+        def zero_combined():
+            with torch.cuda.stream(stream):
+                wb.packed_storage[:wb.per_buffer].zero_()
+
+        def zero_partials():
+            with torch.cuda.stream(stream):
+                wb.packed_storage[wb.per_buffer:].zero_()
 
         def amax():
             B._check(lib.mxfp8_partial_amax(self.amax, self.n_amax, sp))
 
         def combine():
-            B._check(lib.mxfp8_combine_amax(wb.combine_dst, wb.combine_srcs, len(wb.packed),
-                                            wb.combined.numel, B.dtype_code(wb.dtype), sp))
+            for dst, srcs, count in wb.combine_calls:
+                B._check(lib.mxfp8_combine_amax(dst, srcs, len(wb.packed), count, code, sp))
 
         def scales():
             B._check(lib.mxfp8_compute_scales(wb.scale_pieces, wb.n_scale, sp))
@@ -159,16 +236,55 @@ class Plan:
         def scales_cast():
             B._check(lib.mxfp8_scales_and_cast(self.cast, self.n_cast, sp))
 
-        out = [("zero", zero), ("amax", amax)]
+        def quantize():
+            B._check(lib.mxfp8_quantize(self.quant, self.n_quant, sp))
+
+        return dict(zero=zero, zero_combined=zero_combined, zero_partials=zero_partials,
+                    amax=amax, combine=combine, scales=scales, cast=cast,
+                    scales_cast=scales_cast, quantize=quantize)
+
+    def stages(self, stream=None):
+        """The writeback as (name, callable) stages in one stream, in order: zero-fill of the
+        packed amax, partial amax, the single-pass quantize of whole bands (``single_pass``
+        only), MAX-combine (only with one packed buffer per fragment), then scales and cast,
+        or one fused scales-and-cast stage.  ``stream`` is a torch stream (None: the current
+        stream when this is called)."""
+        import torch
+        wb = self.wb
+        c = self._calls(torch.cuda.current_stream() if stream is None else stream)
+        out = [("zero", c["zero"]), ("amax", c["amax"])]
+        if wb.single_pass:
+            out.append(("quantize", c["quantize"]))
         if not wb.shared and len(wb.packed) > 1:
-            out.append(("combine", combine))
+            out.append(("combine", c["combine"]))
         if wb.fused:
-            return out + [("scales_cast", scales_cast)]
-        return out + [("scales", scales), ("cast", cast)]
+            return out + [("scales_cast", c["scales_cast"])]
+        return out + [("scales", c["scales"]), ("cast", c["cast"])]
 
     def run(self, stream=None):
-        for _, fn in self.stages(stream):
-            fn()
+        """Run the writeback.  With ``single_pass`` the quantize of whole bands runs on a side
+        stream, overlapped with the partial chain (amax -> combine -> scales + cast of the
+        bands at the cuts), which touches none of its blocks; both start after the combined
+        buffer is cleared and the call returns with the caller's stream waiting on both."""
+        wb = self.wb
+        if not (wb.single_pass and self.n_quant and self.n_cast):
+            for _, fn in self.stages(stream):
+                fn()
+            return
+        import torch
+        main = torch.cuda.current_stream() if stream is None else stream
+        side = wb.side_stream
+        c, cs = self._calls(main), self._calls(side)
+        c["zero_combined"]()
+        side.wait_stream(main)
+        cs["quantize"]()
+        if len(wb.packed) > 1:
+            c["zero_partials"]()
+        c["amax"]()
+        if not wb.shared and len(wb.packed) > 1:
+            c["combine"]()
+        c["scales_cast"]()
+        main.wait_stream(side)
 
 
 class Writeback:
@@ -176,13 +292,15 @@ class Writeback:
 
     ``shared=True`` accumulates every fragment's amax in one packed buffer; ``shared=False``
     gives each fragment its own packed buffer (one per rank) and MAX-combines them.
-    ``fused=True`` computes the scales inside the cast."""
+    ``fused=True`` computes the scales inside the cast; ``single_pass=True`` (which implies
+    ``fused``) quantizes the whole bands inside each piece in one pass."""
 
     def __init__(self, specs, dtype: torch.dtype, device, fragments, shared: bool = True,
-                 preround: bool = False, fused: bool = False):
+                 preround: bool = False, fused: bool = False, single_pass: bool = False):
         self.specs = list(specs)
         self.dtype = dtype
-        self.fused = fused
+        self.single_pass = single_pass
+        self.fused = fused or single_pass
         self.fragments = [(int(s), int(l)) for s, l in fragments]
         self.shared = shared
         self.preround = preround
@@ -201,10 +319,22 @@ class Writeback:
         self.packed = [PackedAmax(self.specs, dtype, device,
                                   self.packed_storage[i * per:i * per + entries])
                        for i in range(n_bufs)]
+        self.per_buffer = per
         self.combined = self.packed[0]
+        # MAX-combine calls as (dst pointer, source pointer array, entries): the whole packed
+        # buffer, or with ``single_pass`` only the entries of bands that a partial piece
+        # touches (the others hold the single-pass quantize's final amax)
         import ctypes
-        self.combine_dst = self.combined.buffer.data_ptr()
-        self.combine_srcs = (ctypes.c_void_p * n_bufs)(*[p.buffer.data_ptr() for p in self.packed])
+        esz = torch.tensor([], dtype=dtype).element_size()
+        spans = ([(0, entries)] if not single_pass
+                 else boundary_spans(self.specs, self.fragments, dtype))
+        self.combine_calls = []
+        for lo, hi in spans:
+            srcs = (ctypes.c_void_p * n_bufs)(*[p.buffer.data_ptr() + lo * esz
+                                                  for p in self.packed])
+            self.combine_calls.append((self.combined.buffer.data_ptr() + lo * esz, srcs, hi - lo))
+        self._side = None
+        self.device = device
         # scales: one piece per weight and maximal run of adjacent fragments
         pieces = []
         for i, (spec, st) in enumerate(zip(self.specs, self.storage)):
@@ -227,6 +357,13 @@ class Writeback:
                                            scale_row=st.scale_row, scale_col=st.scale_col))
         self.scale_pieces = (B.Piece * len(pieces))(*pieces)
         self.n_scale = len(pieces)
+
+    @property
+    def side_stream(self):
+        """The second stream of the single-pass writeback (default priority)."""
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        return self._side
 
     def plan(self, fragments_values) -> Plan:
         return Plan(self, fragments_values)

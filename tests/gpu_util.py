@@ -53,11 +53,11 @@ def fragment_inputs(x_dev: torch.Tensor, fragments, mode: str):
 
 
 def run_matrix(x: np.ndarray, rows: int, cols: int, fragments, colwise=True, preround=False,
-               inputs="views", shared=True, fused=False):
+               inputs="views", shared=True, fused=False, single_pass=False):
     """The whole path on the GPU for one matrix held as ``fragments``; numpy results."""
     x_dev = to_dev(x)
     wb = W.Writeback([W.WeightSpec(rows, cols, colwise)], torch_dtype(x), DEV, fragments,
-                     shared=shared, preround=preround, fused=fused)
+                     shared=shared, preround=preround, fused=fused, single_pass=single_pass)
     wb(fragment_inputs(x_dev, fragments, inputs))
     torch.cuda.synchronize()
     ar, ac = wb.combined.views(0)

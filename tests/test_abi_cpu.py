@@ -307,3 +307,68 @@ def test_packed_amax_layout():
     assert r0.shape == (40, 3) and c0.shape == (2, 96) and r1.shape == (33, 2) and c1 is None
     assert c0.data_ptr() - r0.data_ptr() == 40 * 3 * 2
     assert r1.data_ptr() - r0.data_ptr() == (40 * 3 + 2 * 96) * 2
+
+
+def test_whole_bands_of_a_piece():
+    spec = W.WeightSpec(100, 64, True)    # bands of 2048 elements, the last one 256
+    band, n = 2048, 6400
+    assert W.whole_bands(spec, 0, n) == (0, n)
+    assert W.whole_bands(spec, 5, n) == (band, n)          # short last band counts as whole
+    assert W.whole_bands(spec, 5, 4100) == (band, 2 * band)
+    lo, hi = W.whole_bands(spec, 5, 2100)                  # no whole band inside
+    assert lo >= hi
+    assert W.whole_bands(spec, band, 3 * band) == (band, 3 * band)
+    assert W.whole_bands(spec, 3 * band + 1, n) == (4 * band, n)
+    lo, hi = W.whole_bands(spec, 3 * band + 1, n - 1)
+    assert lo >= hi
+
+
+def test_boundary_spans_cover_exactly_the_shared_entries():
+    """The single-pass combine covers the packed entries of every block that a partial piece
+    touches (brute force over the elements), and only whole bands of them."""
+    import numpy as np
+    specs = [W.WeightSpec(100, 64, True), W.WeightSpec(70, 96, False), W.WeightSpec(64, 32, True)]
+    total = sum(s.numel for s in specs)
+    g = np.random.Generator(np.random.PCG64(5))
+    for trial in range(20):
+        cuts = np.sort(g.integers(0, total + 1, 3))
+        frags = [(int(a), int(b - a)) for a, b in zip(np.r_[0, cuts], np.r_[cuts, total])]
+        spans = W.boundary_spans(specs, frags)
+        covered = set()
+        for lo, hi in spans:
+            covered |= set(range(lo, hi))
+        offs = W.PackedAmax(specs, torch.float32, "meta").offsets
+        need = set()
+        for fs, fl in frags:
+            for (i, s, n, _) in W.split_fragment(specs, fs, fl):
+                sp = specs[i]
+                lo, hi = W.whole_bands(sp, s, s + n)
+                parts = [(s, s + n)] if lo >= hi else [(s, lo), (hi, s + n)]
+                nb = (sp.cols + 31) // 32
+                for a, b in parts:
+                    for e in range(a, b):
+                        r, c = divmod(e, sp.cols)
+                        need.add(offs[i] + r * nb + c // 32)
+                        if sp.colwise:
+                            need.add(offs[i] + sp.amax_row_entries + (r // 32) * sp.cols + c)
+        assert need <= covered, trial
+        # nothing outside the bands of the partial pieces
+        bands = set()
+        for fs, fl in frags:
+            for (i, s, n, _) in W.split_fragment(specs, fs, fl):
+                sp = specs[i]
+                lo, hi = W.whole_bands(sp, s, s + n)
+                parts = [(s, s + n)] if lo >= hi else [(s, lo), (hi, s + n)]
+                for a, b in parts:
+                    for e in range(a, b):
+                        bands.add((i, e // sp.cols // 32))
+        allowed = set()
+        for i, bd in bands:
+            sp = specs[i]
+            nb = (sp.cols + 31) // 32
+            r0, r1 = 32 * bd, min(32 * bd + 32, sp.rows)
+            allowed |= set(range(offs[i] + r0 * nb, offs[i] + r1 * nb))
+            if sp.colwise:
+                oc = offs[i] + sp.amax_row_entries + bd * sp.cols
+                allowed |= set(range(oc, oc + sp.cols))
+        assert covered <= allowed, trial

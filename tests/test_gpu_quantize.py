@@ -4,7 +4,8 @@ zero-filled amax, scales, cast.  Amax and scale entries of blocks outside the fr
 their previous values.  Covers both kernels (vector and element-wise), short last bands,
 partial last tiles, several pieces in one call, the optional amax outputs, row-only calls,
 BF16 pre-rounding, inputs 2 bytes off a dword boundary, fragment-sized outputs at every byte
-offset, padded leading dimensions, and the full-size weights of the workloads."""
+offset, padded leading dimensions, and the full-size weights of the workloads; and the
+writeback that sends the whole bands inside each fragment through it (``single_pass``)."""
 import numpy as np
 import pytest
 import torch
@@ -12,8 +13,10 @@ import torch
 import oracle
 from mxfp8_block_scaled_partial_amd import binding as B
 from mxfp8_block_scaled_partial_amd import workloads as wl
+from mxfp8_block_scaled_partial_amd import writeback as W
 
-from gpu_util import DEV, bits, first_mismatch, require_gpu, to_dev, to_np, torch_dtype
+from gpu_util import (DEV, assert_same, bits, first_mismatch, require_gpu, run_matrix, to_dev,
+                      to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -275,3 +278,86 @@ def test_quantize_layer_batch_weights_in_one_call():
                 continue
             msg = first_mismatch(bits(got[k]), bits(w))
             assert not msg, f"{name} {k}: {msg}"
+
+
+# ------------------------------------------------------------------ writeback with single_pass
+
+
+def splits(n, k, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    cuts = np.sort(g.integers(0, n + 1, k - 1))
+    cuts = np.concatenate([[0], cuts, [n]])
+    return [(int(a), int(b - a)) for a, b in zip(cuts[:-1], cuts[1:])]
+
+
+@pytest.mark.parametrize("rows,cols", [(100, 64), (37, 45), (256, 96), (97, 2048), (64, 1056)])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_writeback_single_pass_matches_oracle(rows, cols, dtype):
+    x = wl.random_matrix(rows, cols, dtype, seed=rows + 5 * cols, kind="mixed")
+    n = rows * cols
+    band = 32 * cols
+    fragsets = [[(0, n)], splits(n, 3, rows), splits(n, 5, cols),
+                [(0, band + 5), (band + 5, n - band - 5)],  # one cut inside the second band
+                [(0, band), (band, n - band)]]               # a cut on a band boundary
+    for frags in fragsets:
+        if any(l < 0 for _, l in frags):
+            continue
+        for colwise in (True, False):
+            want = oracle.writeback(x, rows, cols, frags, colwise)
+            for shared in (True, False):
+                got = run_matrix(x, rows, cols, frags, colwise, inputs="own", shared=shared,
+                                 single_pass=True)
+                assert_same(got, want, rows, cols, f"{frags} colwise={colwise} shared={shared}: ")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_writeback_single_pass_large_four_fragments(dtype):
+    """The benchmark's launch configuration through the single-pass writeback."""
+    m = wl.matrix_large(dtype)
+    n = m.rows * m.cols
+    cuts = [0, n // 4 + 17, n // 2 + 17, 3 * n // 4 + 17, n]
+    four = [(cuts[i], cuts[i + 1] - cuts[i]) for i in range(4)]
+    want = oracle.writeback(m.data, m.rows, m.cols, [(0, n)], True)
+    got = run_matrix(m.data, m.rows, m.cols, four, True, inputs="views", shared=False,
+                     single_pass=True)
+    assert_same(got, want, m.rows, m.cols, "single pass, 4 fragments: ")
+    plan = got["wb"].plan([torch.empty(l, dtype=torch.bfloat16 if dtype == "bf16" else
+                                       torch.float32, device=DEV) for _, l in four])
+    assert plan.n_quant == 4 and plan.n_cast == 6  # a head and / or tail at each inner cut
+    # the combine covers only the 3 bands at the inner cuts: 32 rows of row-wise entries and
+    # one row of column-wise entries each
+    wb = got["wb"]
+    assert sum(c for _, _, c in wb.combine_calls) == 3 * (32 * m.cols // 32 + m.cols)
+
+
+def test_writeback_single_pass_rowonly_and_layer_batch():
+    r = wl.matrix_rowonly_fragments()
+    want = oracle.writeback(r.data, r.rows, r.cols, r.runs["fragments"], colwise=False)
+    got = run_matrix(r.data, r.rows, r.cols, r.runs["fragments"], False, inputs="own",
+                     shared=False, single_pass=True)
+    assert_same(got, want, r.rows, r.cols, "row-only: ")
+    batch = wl.layer_batch()
+    specs = [W.WeightSpec(rr, c, colwise) for (_, rr, c, colwise) in batch.tensors]
+    x_dev = to_dev(batch.data)
+    wb = W.Writeback(specs, torch.bfloat16, DEV, batch.fragments, shared=False, single_pass=True)
+    plan = wb.plan([x_dev[s:s + l] for s, l in batch.fragments])
+    assert [nm for nm, _ in plan.stages()] == ["zero", "amax", "quantize", "combine",
+                                                "scales_cast"]
+    plan.run()
+    torch.cuda.synchronize()
+    for i, (name, rr, c, colwise) in enumerate(batch.tensors):
+        o = batch.offsets[i]
+        pieces = []
+        for fs, fl in batch.fragments:
+            lo, hi = max(fs, o), min(fs + fl, o + rr * c)
+            if lo < hi:
+                pieces.append((lo - o, hi - lo))
+        want = oracle.writeback(batch.data[o:o + rr * c], rr, c, pieces, colwise)
+        ar, ac = wb.combined.views(i)
+        st = wb.storage[i]
+        got = {"amax_row": to_np(ar), "amax_col": to_np(ac) if colwise else None,
+               "scale_row": to_np(st.scale_row),
+               "scale_col": to_np(st.scale_col) if colwise else None,
+               "data_row": to_np(st.data_row),
+               "data_col": to_np(st.data_col) if colwise else None}
+        assert_same(got, want, rr, c, f"{name}: ")
