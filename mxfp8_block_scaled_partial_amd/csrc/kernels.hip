@@ -808,19 +808,22 @@ __device__ __forceinline__ void cast_tile_general(
   if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const int64_t o = o0 + i * p.cols;
       uint32_t q[E / 4];
       quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
       if (p.mo_row)
-        store_window<E>(p.data_row + o, q, p.mo_row, cvalid, first, last);
+        store_window<E>(p.data_row + o0 + i * p.cols, q, p.mo_row, cvalid, first, last);
       else if (cvalid)
-        store_bytes<E>(p.data_row + o, q);
-      if constexpr (kCol) {
+        store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+    }
+    if constexpr (kCol) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        uint32_t q[E / 4];
         quantize_chunk<T, kPre>(d[i], cshift, true, q);
         if (p.mo_col)
-          store_window<E>(p.data_col + o, q, p.mo_col, cvalid, first, last);
+          store_window<E>(p.data_col + o0 + i * p.cols, q, p.mo_col, cvalid, first, last);
         else if (cvalid)
-          store_bytes<E>(p.data_col + o, q);
+          store_bytes<E>(p.data_col + o0 + i * p.cols, q);
       }
     }
     return;
@@ -924,15 +927,20 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
     }
+    // all row-wise stores, then all column-wise ones: each output gets one run of stores
+    // (interleaving the two directions measured 1.4% slower)
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const int64_t o = o0 + i * p.cols;
       uint32_t q[E / 4];
       quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-      store_bytes<E>(p.data_row + o, q);
-      if constexpr (kCol) {
+      store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+    }
+    if constexpr (kCol) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        uint32_t q[E / 4];
         quantize_chunk<T, kPre>(d[i], cshift, true, q);
-        store_bytes<E>(p.data_col + o, q);
+        store_bytes<E>(p.data_col + o0 + i * p.cols, q);
       }
     }
     if constexpr (kFuse && kCol) {
@@ -1028,26 +1036,31 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
     cshift[e] = 127 - (int)csb[e];
   }
 
-  // data: direct stores when the outputs are dword aligned, else window stores
+  // data: direct stores when the outputs are dword aligned, else window stores; all
+  // row-wise stores first, then the column-wise ones
   const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
   const int64_t cend = min<int64_t>(c0 + WC, p.cols);
   const bool first = lane == 0, last = c + E == cend;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
     const bool valid = cvalid && i < nr;
-    const int64_t o = o0 + i * p.cols;
     uint32_t q[E / 4];
     quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
     if (p.mo_row)
-      store_window<E>(p.data_row + o, q, p.mo_row, valid, first, last);
+      store_window<E>(p.data_row + o0 + i * p.cols, q, p.mo_row, valid, first, last);
     else if (valid)
-      store_bytes<E>(p.data_row + o, q);
-    if constexpr (kCol) {
+      store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+  }
+  if constexpr (kCol) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const bool valid = cvalid && i < nr;
+      uint32_t q[E / 4];
       quantize_chunk<T, kPre>(d[i], cshift, true, q);
       if (p.mo_col)
-        store_window<E>(p.data_col + o, q, p.mo_col, valid, first, last);
+        store_window<E>(p.data_col + o0 + i * p.cols, q, p.mo_col, valid, first, last);
       else if (valid)
-        store_bytes<E>(p.data_col + o, q);
+        store_bytes<E>(p.data_col + o0 + i * p.cols, q);
     }
   }
 
