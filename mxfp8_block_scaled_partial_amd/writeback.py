@@ -58,17 +58,31 @@ class MXFP8Storage:
     and E8M0 scales ([rows][ceil(cols/32)] row-wise, [ceil(rows/32)][cols] column-wise).
     Allocated once; the writeback only writes into it, so its pointers never change."""
 
-    def __init__(self, spec: WeightSpec, device):
+    def __init__(self, spec: WeightSpec, device, with_data: bool = True):
         nb, nbands = B.nblocks(spec.cols), B.nblocks(spec.rows)
         self.spec = spec
-        self.data_row = torch.zeros(spec.numel, dtype=torch.uint8, device=device)
+        n = spec.numel if with_data else 0
+        self.data_row = torch.zeros(n, dtype=torch.uint8, device=device)
         self.scale_row = torch.zeros(spec.rows, nb, dtype=torch.uint8, device=device)
         if spec.colwise:
-            self.data_col = torch.zeros(spec.numel, dtype=torch.uint8, device=device)
+            self.data_col = torch.zeros(n, dtype=torch.uint8, device=device)
             self.scale_col = torch.zeros(nbands, spec.cols, dtype=torch.uint8, device=device)
         else:  # row-only: the column-wise outputs are absent (empty handles)
             self.data_col = torch.empty(0, dtype=torch.uint8, device=device)
             self.scale_col = torch.empty(0, 0, dtype=torch.uint8, device=device)
+
+
+class FragmentOutputs:
+    """E4M3 data of one fragment of the flat batch, FSDP style: byte k of ``data_row`` /
+    ``data_col`` belongs to flat element ``start + k`` of the batch.  ``data_col`` holds the
+    column-wise bytes of the bidirectional weights' elements; its bytes at row-only weights'
+    elements are not written.  Allocated once, written in place."""
+
+    def __init__(self, start: int, length: int, any_colwise: bool, device):
+        self.start, self.length = start, length
+        self.data_row = torch.zeros(length, dtype=torch.uint8, device=device)
+        self.data_col = torch.zeros(length if any_colwise else 0, dtype=torch.uint8,
+                                    device=device)
 
 
 class PackedAmax:
@@ -164,6 +178,7 @@ class Plan:
             if x.numel() != fl or x.dtype != wb.dtype:
                 raise ValueError(f"fragment {f}: expected {fl} values of {wb.dtype}")
             packed = wb.packed[f if not wb.shared else 0]
+            fo = wb.fragment_outputs[f] if wb.fragment_outputs else None
             for (i, s, n, off) in split_fragment(wb.specs, fs, fl):
                 spec, st = wb.specs[i], wb.storage[i]
                 ar, ac = packed.views(i)
@@ -175,7 +190,8 @@ class Plan:
                         ranges = [(s, lo), (hi, s + n)]
                         # no other fragment touches these blocks: their amax are final and go
                         # straight into the combined buffer
-                        quant_pieces.append(self._piece(spec, st, x, off - s, lo, hi, car, cac))
+                        quant_pieces.append(self._piece(spec, st, fo, x, off - s, lo, hi, car,
+                                                        cac))
                         self.quant_ranges.append((i, lo, hi))
                 for a, b in ranges:
                     if a == b:
@@ -183,7 +199,7 @@ class Plan:
                     xin = x[off + a - s:off + b - s]
                     amax_pieces.append(B.make_piece(spec.rows, spec.cols, a, xin, amax_row=ar,
                                                     amax_col=ac, preround=wb.preround))
-                    cast_pieces.append(self._piece(spec, st, x, off - s, a, b,
+                    cast_pieces.append(self._piece(spec, st, fo, x, off - s, a, b,
                                                    *((car, cac) if wb.fused else (None, None))))
                     self.partial_ranges.append((i, a, b))
         self.amax = (B.Piece * len(amax_pieces))(*amax_pieces)
@@ -192,13 +208,18 @@ class Plan:
         self.n_amax, self.n_cast = len(amax_pieces), len(cast_pieces)
         self.n_quant = len(quant_pieces)
 
-    def _piece(self, spec, st, x, shift, a, b, amax_row, amax_col):
-        """Piece [a, b) of a weight whose fragment values start at x[a + shift]."""
+    def _piece(self, spec, st, fo, x, shift, a, b, amax_row, amax_col):
+        """Piece [a, b) of a weight whose values sit at x[a + shift]; its data go to the
+        weight's full storage, or to the fragment's outputs ``fo`` at the same offsets as x."""
+        if fo is None:
+            dr, dc = st.data_row[a:b], st.data_col[a:b] if spec.colwise else None
+        else:
+            dr = fo.data_row[a + shift:b + shift]
+            dc = fo.data_col[a + shift:b + shift] if spec.colwise else None
         return B.make_piece(
             spec.rows, spec.cols, a, x[a + shift:b + shift], amax_row=amax_row,
             amax_col=amax_col, scale_row=st.scale_row, scale_col=st.scale_col,
-            data_row=st.data_row[a:b], data_col=st.data_col[a:b] if spec.colwise else None,
-            preround=self.wb.preround)
+            data_row=dr, data_col=dc, preround=self.wb.preround)
 
     def _calls(self, stream):
         """The library calls of the writeback on torch stream ``stream``, by name."""
@@ -293,10 +314,15 @@ class Writeback:
     ``shared=True`` accumulates every fragment's amax in one packed buffer; ``shared=False``
     gives each fragment its own packed buffer (one per rank) and MAX-combines them.
     ``fused=True`` computes the scales inside the cast; ``single_pass=True`` (which implies
-    ``fused``) quantizes the whole bands inside each piece in one pass."""
+    ``fused``) quantizes the whole bands inside each piece in one pass.
+
+    The data go in place into full-size per-weight storage (``storage[i].data_row`` ...), or
+    with ``fragment_outputs=True`` into one fragment-sized buffer per fragment and direction
+    (``fragment_outputs[f]``), the FSDP-style interface; scales are per weight either way."""
 
     def __init__(self, specs, dtype: torch.dtype, device, fragments, shared: bool = True,
-                 preround: bool = False, fused: bool = False, single_pass: bool = False):
+                 preround: bool = False, fused: bool = False, single_pass: bool = False,
+                 fragment_outputs: bool = False):
         self.specs = list(specs)
         self.dtype = dtype
         self.single_pass = single_pass
@@ -308,7 +334,11 @@ class Writeback:
         for s, l in self.fragments:
             if s < 0 or l < 0 or s + l > total:
                 raise ValueError(f"fragment [{s}, {s + l}) outside the batch of {total}")
-        self.storage = [MXFP8Storage(s, device) for s in self.specs]
+        self.storage = [MXFP8Storage(s, device, with_data=not fragment_outputs)
+                        for s in self.specs]
+        any_col = any(s.colwise for s in self.specs)
+        self.fragment_outputs = ([FragmentOutputs(s, l, any_col, device)
+                                  for s, l in self.fragments] if fragment_outputs else None)
         n_bufs = 1 if shared else max(1, len(self.fragments))
         # all packed buffers in one allocation (one zero-fill per update); each starts on a
         # 16-byte boundary so the combine can move 16-byte vectors
