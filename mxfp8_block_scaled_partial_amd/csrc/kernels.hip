@@ -1,5 +1,7 @@
 // HIP kernels for gfx950 (CDNA4): MXFP8 partial amax, amax MAX-combine, E8M0 scales and the
-// partial E4M3 cast of a contiguous fragment of a flattened 2-D weight.
+// partial E4M3 cast of a contiguous fragment of a flattened 2-D weight; the cast with the scales
+// derived in-kernel from the combined amax; and a single-pass quantize (amax, scales and cast
+// from one read) for fragments that own every block they touch.
 //
 // What is computed follows "Support row-only MXFP8 distributed master-weight casts"
 // (TransformerEngine PR 3488, sections Changes and the flow diagram of the Greptile summary)
@@ -27,9 +29,9 @@
 //    amax buffer merge correctly in any order.
 //  * Workgroup ids are remapped so consecutive tiles (one band's amax entries) land on the
 //    same XCD's L2.
-//  * Layouts the vector path cannot take (cols % 32 != 0, input - start not 16-byte aligned,
-//    unaligned fragment-relative outputs) run an element-wise kernel: one lane per column,
-//    same band tiling, same results.
+//  * Layouts the vector path cannot take (cols % 32 != 0) run an element-wise kernel: one lane
+//    per column, same band tiling, same results.  Any alignment of input and outputs stays on
+//    the vector path (dword loads with a 2-byte realign, window stores).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -361,3 +361,32 @@ def test_writeback_single_pass_rowonly_and_layer_batch():
                "data_row": to_np(st.data_row),
                "data_col": to_np(st.data_col) if colwise else None}
         assert_same(got, want, rr, c, f"{name}: ")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_many_pieces_in_one_call_fused_and_quantize(dtype):
+    """More pieces than one launch groups (16): the library splits them over launches."""
+    rows, cols = 40 * 32, 96
+    x = wl.random_matrix(rows, cols, dtype, seed=77, kind="mixed")
+    band = 32 * cols
+    frags = [(b * band, band) for b in range(40)]           # 40 band-sized pieces
+    want = expected(x, rows, cols, frags, True, False)
+    got = run_quantize(x, rows, cols, frags, True, False, "own")
+    check(got, want, rows, cols, "40 quantize pieces: ")
+    # the fused scales + cast over 37 uneven pieces, reading the amax the quantize produced
+    cuts = np.linspace(0, rows * cols, 38).astype(np.int64) + np.arange(38) % 5
+    cuts[0], cuts[-1] = 0, rows * cols
+    pieces37 = [(int(a), int(b - a)) for a, b in zip(cuts[:-1], cuts[1:])]
+    xd = to_dev(x)
+    ar, ac = amax_dev(got["amax_row"]), amax_dev(got["amax_col"])
+    sr = torch.full((rows, cols // 32), SENT_SCALE, dtype=torch.uint8, device=DEV)
+    sc = torch.full((rows // 32, cols), SENT_SCALE, dtype=torch.uint8, device=DEV)
+    dr = torch.zeros(rows * cols, dtype=torch.uint8, device=DEV)
+    dc = torch.zeros(rows * cols, dtype=torch.uint8, device=DEV)
+    B.mxfp8_scales_and_cast([B.make_piece(rows, cols, s, xd[s:s + l], amax_row=ar, amax_col=ac,
+                                          scale_row=sr, scale_col=sc, data_row=dr[s:s + l],
+                                          data_col=dc[s:s + l]) for s, l in pieces37])
+    torch.cuda.synchronize()
+    for k, t in (("scale_row", sr), ("scale_col", sc), ("data_row", dr), ("data_col", dc)):
+        msg = first_mismatch(to_np(t), want[k])
+        assert not msg, f"37 fused pieces {k}: {msg}"
