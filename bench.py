@@ -53,8 +53,8 @@ def parse():
                     help="distinct input/output sets rotate until this many GB are in use")
     ap.add_argument("--kernel-table", dest="kernel_table", action="store_true", default=True)
     ap.add_argument("--no-kernel-table", dest="kernel_table", action="store_false")
-    ap.add_argument("--kernel-calls", type=int, default=20,
-                    help="graph replays (10 calls each) per kernel-table entry")
+    ap.add_argument("--kernel-calls", type=int, default=140,
+                    help="graph replays (10 calls each) per kernel-table entry (7 rounds of 20)")
     ap.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-rows", type=int, default=16384,
@@ -171,9 +171,23 @@ def main():
             ev[-1].record()
 
     log(f"warmup {args.warmup} steps")
-    for i in range(args.warmup):
+    for i in range(max(2, args.warmup)):
         step(i)
     torch.cuda.synchronize()
+
+    # the oracle leg runs before the timed region: it times the oracle on the host and checks
+    # the warm-up steps' outputs for weight 0 (the same input and fragments) bit for bit
+    cpu = None
+    if args.cpu:
+        wb0 = sets[0][1]
+        ar0, ac0 = wb0.combined.views(0)
+        st0 = wb0.storage[0]
+        gpu0 = {"amax_row": ar0, "amax_col": ac0, "scale_row": st0.scale_row,
+                "scale_col": st0.scale_col, "data_row": st0.data_row, "data_col": st0.data_col}
+        cpu = cpu_baseline(m, args.cpu_rows, s_in, gpu0 if args.cpu_rows == rows else None)
+        for i in range(args.warmup):  # the GPU idled meanwhile: warm it up again
+            step(i)
+        torch.cuda.synchronize()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
            for _ in range(args.steps)]
@@ -272,7 +286,7 @@ def main():
         out["kernels"] = kernel_table(args, sets if args.dtype == "bf16" else None, m, dev, tdt)
 
     if args.cpu:
-        out["cpu_baseline"] = cpu_baseline(m, args.cpu_rows, s_in)
+        out["cpu_baseline"] = cpu
 
     print(json.dumps(out), flush=True)
 
@@ -489,13 +503,15 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
     return table
 
 
-def cpu_baseline(m, cpu_rows, s_in):
+def cpu_baseline(m, cpu_rows, s_in, gpu=None):
     """The oracle (plain C) over the first ``cpu_rows`` rows of the same weight, cut into 4
     fragments like the GPU step, through the whole path: once on one thread, then with the
     rows split into groups of whole 32-row bands, one group per host core (blocks never cross
     a band, so each group is an independent writeback of its rows with the cuts that fall in
     them; the oracle releases the GIL inside its C calls)."""
     from concurrent.futures import ThreadPoolExecutor
+
+    import torch
 
     import oracle
     from mxfp8_block_scaled_partial_amd import bytes_model as BM
@@ -507,8 +523,23 @@ def cpu_baseline(m, cpu_rows, s_in):
     x = m.data[:n]
     oracle.lib()
     t0 = time.perf_counter()
-    oracle.writeback(x, rows, cols, frags, colwise=True)
+    want = oracle.writeback(x, rows, cols, frags, colwise=True)
     dt = time.perf_counter() - t0
+    check = "not run (sample is not the whole weight)"
+    if gpu is not None:
+        import numpy as np
+        bad = []
+        for k, t in gpu.items():
+            g = t.detach().cpu()
+            g = g.view(torch.int16).numpy().view(np.uint16) if g.dtype == torch.bfloat16 else g.numpy()
+            w = want[k]
+            if g.dtype == np.float32:
+                g, w = g.view(np.uint32), w.view(np.uint32)
+            if not np.array_equal(g, w):
+                bad.append(f"{k}: {int(np.count_nonzero(g != w))} bytes differ")
+        check = "bit-exact" if not bad else "MISMATCH " + "; ".join(bad)
+        if bad:
+            log("GPU step outputs differ from the oracle: " + check)
     packed = rows * ((cols + 31) // 32) + ((rows + 31) // 32) * cols
     per = [BM.piece_bytes(rows, cols, s, l, s_in, True) for s, l in frags]
     total = (BM.zero_bytes(4, packed, s_in) + sum(p["amax"] + p["cast"] for p in per)
@@ -534,6 +565,7 @@ def cpu_baseline(m, cpu_rows, s_in):
               "path (amax, combine, scales, cast), C oracle")
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2), "sample": sample + ", one thread",
+            "gpu_step_vs_oracle": check,
             "all_cores": {"value": round(total / dt_all / 1e9, 3), "unit": "GB/s",
                           "cores": cores, "seconds": round(dt_all, 2),
                           "sample": sample + f", {cores} threads over groups of 32-row bands"},
