@@ -569,7 +569,17 @@ def cpu_baseline(m, cpu_rows, s_in, gpu=None):
             "all_cores": {"value": round(total / dt_all / 1e9, 3), "unit": "GB/s",
                           "cores": cores, "seconds": round(dt_all, 2),
                           "sample": sample + f", {cores} threads over groups of 32-row bands"},
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)), "host_cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

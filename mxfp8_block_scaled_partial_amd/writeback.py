@@ -401,3 +401,23 @@ class Writeback:
     def __call__(self, fragments_values, stream=None):
         self.plan(fragments_values).run(stream)
         return self
+
+
+def cast_master_fragments(fragments, weights, **options) -> Writeback:
+    """One writeback of a batch: ``fragments`` is a list of (start, values) pairs, each a
+    contiguous shard of the batch's flat master buffer (``values`` a 1-D float32 / bfloat16
+    device tensor holding elements ``start ... start + len - 1``); ``weights`` the batch's
+    ``WeightSpec`` list in buffer order.  Splits every fragment into per-weight pieces and runs
+    one partial-amax call, at most one combine, and the scale and cast calls (see
+    ``Writeback`` for ``options``).  Returns the ``Writeback``, whose storage (or fragment
+    outputs) hold the MXFP8 result; keep it to run later updates with stable pointers."""
+    fragments = list(fragments)
+    if not fragments:
+        raise ValueError("need at least one fragment")
+    values = [v for _, v in fragments]
+    dtype = values[0].dtype
+    if any(v.dtype != dtype for v in values):
+        raise ValueError("all fragments must share one dtype")
+    wb = Writeback(weights, dtype, values[0].device, [(int(s), v.numel()) for s, v in fragments],
+                   **options)
+    return wb(values)

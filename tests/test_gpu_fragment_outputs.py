@@ -136,3 +136,13 @@ def test_layer_batch_fragment_outputs():
     wb([x[s:s + l] for s, l in b.fragments])
     torch.cuda.synchronize()
     check(wb, specs, b.fragments, want, "layer batch: ")
+
+
+def test_cast_master_fragments_helper():
+    specs, flat = batch(60, "bf16")
+    frags = fragments_of(flat.size, 3, 11)
+    x = to_dev(flat)
+    wb = W.cast_master_fragments([(s, x[s:s + l].clone()) for s, l in frags], specs,
+                                 shared=False, fused=True)
+    torch.cuda.synchronize()
+    check(wb, specs, frags, expected(specs, flat, frags), "helper: ")
