@@ -163,9 +163,10 @@ const char* mxfp8_last_error(void);
 
 /* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast,
  * 2 = scales and cast, 3 = quantize (each validated as for its entry point):
- * 1 = the vectorized path (16-byte loads of row segments of whole 32-value blocks, for any
- * cols % 32 == 0, whatever the alignment of input and outputs), 0 = the element-wise path
- * (cols % 32 != 0), negative = the piece fails validation (the status code, negated).
+ * 1 = the vectorized path (16-byte loads of row segments, for rows of whole 16-byte chunks:
+ * cols % 8 == 0 for BF16, cols % 4 == 0 for FP32, whatever the alignment of input and
+ * outputs), 0 = the element-wise path (other cols), negative = the piece fails validation
+ * (the status code, negated).
  * Host-only; launches nothing.  The vectorized path may read, never write, up to 15 bytes
  * before the first and after the last input element, within the same 16-byte-aligned
  * granule (the same memory page), and ignores them. */

@@ -29,9 +29,10 @@
 //    amax buffer merge correctly in any order.
 //  * Workgroup ids are remapped so consecutive tiles (one band's amax entries) land on the
 //    same XCD's L2.
-//  * Layouts the vector path cannot take (cols % 32 != 0) run an element-wise kernel: one lane
-//    per column, same band tiling, same results.  Any alignment of input and outputs stays on
-//    the vector path (dword loads with a 2-byte realign, window stores).
+//  * Layouts the vector path cannot take (rows that are not whole 16-byte chunks: cols % 8 != 0
+//    for BF16, cols % 4 != 0 for FP32) run an element-wise kernel: one lane per column, same
+//    band tiling, same results.  Any alignment of input and outputs stays on the vector path
+//    (dword loads with a 2-byte realign, window stores).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -480,7 +481,10 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   const int i0 = wave * RW;  // this wave's first row within the band
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
-  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+  // A tile holding a row's short last block (cols % 32 != 0) takes the edge path, whose entry
+  // writes go through LDS: the interior path's per-lane writes assume whole blocks.
+  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end &&
+                        (p.cols % kBlockLen == 0 || c0 + WC <= p.cols);
 
   uint32_t col[4] = {0, 0, 0, 0};
   uint32_t d[RW][4];
@@ -1428,10 +1432,13 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
   return hipSuccess;
 }
 
-// The vector kernels take any fragment of a weight whose rows are whole 32-value blocks: the
-// input needs only its element alignment (dword loads, plus a 2-byte shift for BF16 at 2 mod
-// 4), and outputs at any byte offset are written through aligned windows.
-bool vec_common_ok(const Piece& p) { return p.cols % kBlockLen == 0; }
+// The vector kernels take any fragment of a weight whose rows are whole 16-byte chunks (cols a
+// multiple of 8 for BF16, of 4 for FP32): a chunk then never crosses a block boundary or a row
+// end, every row has the same alignment, and a row's short last block (cols % 32 != 0) is a
+// whole number of chunks.  The input needs only its element alignment (dword loads, plus a
+// 2-byte shift for BF16 at 2 mod 4), and outputs at any byte offset are written through
+// aligned windows.
+bool vec_common_ok(const Piece& p) { return p.cols % (16 / elem_size(p.dtype)) == 0; }
 
 // Pieces of one call, bucketed by kernel specialization: dtype x column-wise x pre-round x
 // vector path.

@@ -174,8 +174,8 @@ def test_quantize_needs_whole_bands():
         assert q(raw_piece(rows=100, cols=64, start=s, length=l), 3) == -B.ERR_RANGE, (s, l)
         assert "32-row bands" in B.mxfp8_last_error()
     assert call(QUANT, raw_piece(rows=100, cols=64, start=64, length=64)) == B.ERR_RANGE
-    # element-wise layout for cols % 32 != 0
-    assert q(raw_piece(rows=40, cols=40), 3) == 0
+    # element-wise layout for rows that are not whole 16-byte chunks
+    assert q(raw_piece(rows=40, cols=45), 3) == 0 and q(raw_piece(rows=40, cols=40), 3) == 1
 
 
 def test_quantize_buffers():
@@ -244,21 +244,25 @@ def test_combine_validation():
     assert L.mxfp8_combine_amax(BASE + 0x3000000, nul, 2, 16, B.BF16, None) == B.ERR_MISSING
 
 
-def test_query_path_selects_vector_kernel_for_whole_block_rows():
+def test_query_path_selects_vector_kernel_for_whole_chunk_rows():
     q = B.mxfp8_query_path
     assert q(raw_piece(), 0) == 1 and q(raw_piece(), 1) == 1
-    # any alignment of input and outputs stays on the vector path when cols % 32 == 0
+    # any alignment of input and outputs stays on the vector path
     assert q(raw_piece(start=17, length=100, input=BASE + 34,
                        data_row=BASE + 0x50000000 + 17, data_col=BASE + 0x60000000 + 17), 1) == 1
     assert q(raw_piece(start=17, length=100), 0) == 1
     p = raw_piece(start=32, length=64, input=BASE + 64, data_row=BASE + 0x50000000 + 3)
     assert q(p, 0) == 1 and q(p, 1) == 1
-    # rows that are not whole 32-value blocks -> element-wise path
-    assert q(raw_piece(rows=40, cols=40), 0) == 0
-    assert q(raw_piece(rows=40, cols=40), 1) == 0
+    # rows of whole 16-byte chunks (8 BF16 / 4 FP32 values) but not whole 32-value blocks:
+    # still the vector path; other widths: the element-wise path
+    assert q(raw_piece(rows=40, cols=40), 0) == 1 and q(raw_piece(rows=40, cols=40), 1) == 1
+    assert q(raw_piece(rows=40, cols=44), 0) == 0                   # BF16: 44 % 8 != 0
+    assert q(raw_piece(rows=40, cols=44, dtype=B.FP32), 0) == 1     # FP32: 44 % 4 == 0
+    assert q(raw_piece(rows=40, cols=45, dtype=B.FP32), 1) == 0
+    assert q(raw_piece(rows=40, cols=45), 1) == 0
     assert q(raw_piece(rows=0), 0) == -B.ERR_ARG
     assert q(raw_piece(), 5) == -B.ERR_ARG
-    assert q(raw_piece(), 2) == 1 and q(raw_piece(rows=40, cols=40), 2) == 0
+    assert q(raw_piece(), 2) == 1 and q(raw_piece(rows=40, cols=45), 2) == 0
     assert q(raw_piece(), 4) == -B.ERR_ARG
 
 

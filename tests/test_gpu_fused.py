@@ -111,7 +111,7 @@ def check(got, want, rows, cols, label):
 
 
 SHAPES = [(37, 45), (33, 40), (1, 70), (70, 1), (96, 33), (65, 96), (100, 64), (31, 4128),
-          (64, 64), (2, 32), (40, 1024), (97, 2048)]
+          (64, 64), (2, 32), (40, 1024), (97, 2048), (50, 1000), (33, 520)]
 
 
 @pytest.mark.parametrize("rows,cols", SHAPES)

@@ -86,9 +86,38 @@ def test_vector_and_element_paths_are_both_exercised():
     p_own = B.make_piece(64, 64, 17, own, amax_row=ar)
     assert B.mxfp8_query_path(p_view, 0) == 1
     assert B.mxfp8_query_path(p_own, 0) == 1
-    y = torch.zeros(40 * 40, dtype=torch.bfloat16, device=DEV)
+    y = torch.zeros(40 * 44, dtype=torch.bfloat16, device=DEV)
+    ar44 = torch.zeros(40, 2, dtype=torch.bfloat16, device=DEV)
+    assert B.mxfp8_query_path(B.make_piece(40, 44, 0, y, amax_row=ar44), 0) == 0
+    # rows of whole 16-byte chunks with a short last block stay on the vector path
     ar40 = torch.zeros(40, 2, dtype=torch.bfloat16, device=DEV)
-    assert B.mxfp8_query_path(B.make_piece(40, 40, 0, y, amax_row=ar40), 0) == 0
+    assert B.mxfp8_query_path(B.make_piece(40, 40, 0, y[:1600], amax_row=ar40), 0) == 1
+
+
+# rows of whole 16-byte chunks whose last 32-value block is short (cols % 32 != 0): the vector
+# kernels, with the short block in the last tile of each row (1028: FP32 only, BF16 takes the
+# element-wise path)
+VEC_SHORT = [(40, 4104), (33, 520), (100, 1000), (64, 72), (37, 8), (70, 1028)]
+
+
+@pytest.mark.parametrize("rows,cols", VEC_SHORT)
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_vector_path_with_short_last_block(rows, cols, dtype):
+    x = wl.random_matrix(rows, cols, dtype, seed=rows + 3 * cols, kind="mixed")
+    n = rows * cols
+    p = B.make_piece(rows, cols, 0, to_dev(x), amax_row=torch.zeros(rows, (cols + 31) // 32,
+                                                                    dtype=torch_dtype(x),
+                                                                    device=DEV))
+    esize = 2 if dtype == "bf16" else 4
+    assert B.mxfp8_query_path(p, 0) == (1 if cols % (16 // esize) == 0 else 0)
+    for frags in ([(0, n)], splits(n, 3, cols), splits(n, 6, rows), [(17, n - 17)]):
+        for colwise in (True, False):
+            want = oracle.writeback(x, rows, cols, frags, colwise)
+            for inputs in ("views", "own"):
+                for shared in (True, False):
+                    got = run_matrix(x, rows, cols, frags, colwise, inputs=inputs, shared=shared)
+                    assert_same(got, want, rows, cols,
+                                f"{frags} colwise={colwise} {inputs} shared={shared}: ")
 
 
 # ------------------------------------------------------------------ padded leading dimensions
