@@ -569,9 +569,11 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     return;
   }
 
-  // Edge tile: a fragment boundary, or the short last band, cuts it.  Every wave loads its
-  // rows masked to the fragment; the row-wise and column-wise maxima meet in LDS and all 256
-  // threads then merge the touched entries atomically, at most two of each kind per thread.
+  // Edge tile: a fragment boundary, the short last band or a row's short last block cuts it.
+  // Every wave loads its rows masked to the fragment; the row-wise and column-wise maxima meet
+  // in LDS and all 256 threads then merge the touched entries atomically, at most two of each
+  // kind per thread (all reads, then all swaps: faster than a plain read-max-write per entry
+  // even for blocks this tile owns alone).
   uint32_t em[RW];
   load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
