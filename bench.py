@@ -13,7 +13,8 @@ left in the 256 MB Infinity Cache.
 
 Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
 ``roofline`` is for the dominant kernel (the cast, fused with the scales by default), from
-HIP events recorded on the launch stream around the cast call of every fourth timed step;
+timing-only HIP events (no system-scope fence) recorded on the launch stream around the cast
+call of every fourth timed step;
 ``kernels`` is the per-call table (partial amax, partial cast and the fused scales + cast;
 full input and the quarter fragment at offset 17, BF16 and FP32); ``cpu_baseline`` times
 the oracle on the host over a band-aligned sample of the same workload.
@@ -21,6 +22,7 @@ the oracle on the host over a band-aligned sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -68,6 +70,65 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain device copy (the counter calibration kernel)")
     return ap.parse_args()
+
+
+class TimingEvent:
+    """A HIP event used for timing only, created with hipEventDisableSystemFence.
+
+    Recording a default event makes the command processor write back and invalidate the
+    caches at system scope, which lengthens the stream by a few µs at every marker; without
+    that fence the marker only takes its timestamp, so the time between two markers is close
+    to the kernel durations a profiler reports.  torch.cuda.Event cannot set the flag, so this
+    calls the HIP runtime torch has already loaded (same soname, so the same instance) and
+    records on torch's current stream, where the library launches.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in (h.hipEventCreateWithFlags, h.hipEventRecord, h.hipEventElapsedTime,
+                      h.hipEventDestroy):
+                f.restype = ctypes.c_int
+            cls._hip = h
+        return cls._hip
+
+    @staticmethod
+    def _ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def __init__(self):
+        self.ev = ctypes.c_void_p()
+        self._ok(self._rt().hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                    self.DISABLE_SYSTEM_FENCE),
+                 "hipEventCreateWithFlags")
+
+    def record(self):
+        import torch
+        self._ok(self._rt().hipEventRecord(self.ev, torch.cuda.current_stream().cuda_stream),
+                 "hipEventRecord")
+
+    def elapsed_time(self, end: "TimingEvent") -> float:
+        """Milliseconds from this event to ``end``; both must have completed."""
+        ms = ctypes.c_float()
+        self._ok(self._rt().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev),
+                 "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.ev and self._hip is not None:
+                self._hip.hipEventDestroy(self.ev)
+        except Exception:  # interpreter shutdown
+            pass
 
 
 def kernel_sha() -> str:
@@ -200,7 +261,7 @@ def main():
     # the timed steps: wall clock over all of them; HIP events around the cast launch of
     # every CAST_SAMPLE-th step (each event marker costs the stream a few µs, so sampling
     # keeps the measurement from lengthening the steps it measures)
-    cev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    cev = {i: (TimingEvent(), TimingEvent())
            for i in range(0, args.steps, CAST_SAMPLE)}
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -214,7 +275,7 @@ def main():
 
     # the stage breakdown, from a separate pass with an event before every stage
     # (informational: the markers themselves lengthen that pass's steps)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
+    evs = [[TimingEvent() for _ in range(len(stage_names) + 1)]
            for _ in range(args.steps)]
     for i in range(args.steps):
         step(args.warmup + args.steps + i, evs[i])
@@ -287,7 +348,7 @@ def main():
         for a, b in pairs:
             b.copy_(a)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = TimingEvent(), TimingEvent()
         reps = 20
         e0.record()
         for i in range(reps):
@@ -342,7 +403,7 @@ def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
 
     # one linear pass with events per stage (no overlap), for the breakdown
     names = [n for n, _ in p0.stages()]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    ev = [TimingEvent() for _ in range(len(names) + 1)]
     stage_runs = []
     for i in range(args.warmup + 5):
         for j, (_, fn) in enumerate(plans[i % len(plans)].stages()):
@@ -358,7 +419,7 @@ def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
     for i in range(args.warmup):
         plans[i % len(plans)].run()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [(TimingEvent(), TimingEvent())
            for _ in range(args.steps)]
     for i, (e0, e1) in enumerate(evs):
         e0.record()
@@ -394,7 +455,7 @@ def graph_step_us(args, step_fns):
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [(TimingEvent(), TimingEvent())
           for _ in range(args.steps)]
     for i, (e0, e1) in enumerate(ev):
         e0.record()
@@ -485,7 +546,7 @@ def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
                         fn(pieces[i % n_sets])
                 g.replay()
                 torch.cuda.synchronize()
-                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ev = [(TimingEvent(), TimingEvent())
                       for _ in range(args.kernel_calls)]
                 for e0, e1 in ev:
                     e0.record()

@@ -87,11 +87,15 @@ struct TileArgs {
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
-// numbered piece after piece, first[k] being the first tile of piece k.
+// numbered piece after piece, first[k] being the first tile of piece k.  A group with more
+// than kMaxLaunchGroups workgroups goes out as several launches, base being the tile of the
+// launch's first workgroup, so no grid comes near the 2^32 work-items a dispatch can hold.
 constexpr int kMaxGroup = 16;
+constexpr int64_t kMaxLaunchGroups = int64_t(1) << 20;
 struct GroupArgs {
   TileArgs piece[kMaxGroup];
   int64_t first[kMaxGroup + 1];
+  int64_t base;
   int32_t n;
 };
 
@@ -467,7 +471,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -868,7 +872,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -980,7 +984,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = xcd_remap(blockIdx.x, gridDim.x);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -1096,7 +1100,7 @@ constexpr int kElemTileCols = kWaveSize;  // one lane per column
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -1134,7 +1138,7 @@ __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
 template <typename T, bool kCol, bool kPre, bool kFuse>
 __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -1176,7 +1180,7 @@ __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -1236,10 +1240,11 @@ struct ScaleArgs {
   int64_t ld_sc;
   int64_t r_first, r_last;  // rows the fragment touches
   int64_t b_first, b_last;  // bands the fragment touches
+  int64_t r_lo, b_lo;       // first row / band of this launch
   uint32_t items_row;        // 8-entry items per row (row-wise part)
-  uint32_t items_row_total;  // items of the row-wise part
+  uint32_t items_row_total;  // items of this launch's row-wise part
   uint32_t items_col;        // 8-entry items per band (column-wise part)
-  uint32_t items_col_total;  // items of the column-wise part (0 when absent)
+  uint32_t items_col_total;  // items of this launch's column-wise part (0 when absent)
   int32_t row_vec, col_vec;  // rows of amax / scales aligned for 16-byte / 8-byte vectors
 };
 
@@ -1295,7 +1300,7 @@ __global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
   const uint32_t i = blockIdx.x * 256u + threadIdx.x;
   if (i < p.items_row_total) {
     const uint32_t rr = i / p.items_row;
-    const int64_t r = p.r_first + rr;
+    const int64_t r = p.r_lo + rr;
     const int64_t x0 = (int64_t)(i - rr * p.items_row) * 8;
     const int64_t nb = (p.cols + kBlockLen - 1) / kBlockLen;
     const T* a = static_cast<const T*>(p.amax_row) + r * p.ld_ar;
@@ -1314,7 +1319,7 @@ __global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
   const uint32_t j = i - p.items_row_total;
   if (j >= p.items_col_total) return;
   const uint32_t bb = j / p.items_col;
-  const int64_t b = p.b_first + bb;
+  const int64_t b = p.b_lo + bb;
   const int64_t x0 = (int64_t)(j - bb * p.items_col) * 8;
   const T* a = static_cast<const T*>(p.amax_col) + b * p.ld_ac;
   uint8_t* s = p.scale_col + b * p.ld_sc;
@@ -1418,6 +1423,7 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
     int64_t total = 0;
     for (int k = 0; k < g.n; ++k) {
+      if (ps[i0 + k].ntiles > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;  // 32-bit tile ids
       g.piece[k] = ps[i0 + k];
       g.first[k] = total;
       // element-wise tiles start on a workgroup boundary so each workgroup has one piece
@@ -1425,11 +1431,14 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     }
     g.first[g.n] = total;
     const int64_t groups = cdiv(total, tiles_per_wg);
-    if (groups > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(total < kSmallLaunchTiles ? small_kernel : kernel, dim3((unsigned)groups),
-                       dim3(kThreads), 0, s, g);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const K k = total < kSmallLaunchTiles ? small_kernel : kernel;
+    for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
+      g.base = g0 * tiles_per_wg;
+      const int64_t ng = std::min<int64_t>(kMaxLaunchGroups, groups - g0);
+      hipLaunchKernelGGL(k, dim3((unsigned)ng), dim3(kThreads), 0, s, g);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
@@ -1569,6 +1578,10 @@ hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {
   return hipSuccess;
 }
 
+// Items (threads) per scales launch beyond which a fragment's scales go out as several
+// launches of whole rows or bands, well below the 2^32 work-items a dispatch holds.
+constexpr int64_t kMaxScaleItems = int64_t(1) << 24;
+
 hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
   ScaleArgs a{};
   a.rows = p.rows;
@@ -1591,24 +1604,45 @@ hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
   const int64_t esz = elem_size(p.dtype);
   const int64_t nb = cdiv(p.cols, kBlockLen);
   const int64_t items_row = cdiv(nb, 8), items_col = cdiv(p.cols, 8);
-  const int64_t total_row = (a.r_last - a.r_first + 1) * items_row;
-  const int64_t total_col = col ? (a.b_last - a.b_first + 1) * items_col : 0;
-  if (total_row + total_col + 255 > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;
+  const int64_t nrows = a.r_last - a.r_first + 1, nbands = a.b_last - a.b_first + 1;
+  // a launch holds at least one whole row or band: at most 2^31 items (2^31 work-items)
+  constexpr int64_t kMaxRowItems = int64_t(1) << 31;
+  if (items_row > kMaxRowItems || (col && items_col > kMaxRowItems))
+    return hipErrorInvalidConfiguration;
   a.items_row = (uint32_t)items_row;
-  a.items_row_total = (uint32_t)total_row;
   a.items_col = (uint32_t)items_col;
-  a.items_col_total = (uint32_t)total_col;
   auto aligned = [](const void* q, int64_t n) { return reinterpret_cast<uintptr_t>(q) % n == 0; };
   a.row_vec = aligned(p.amax_row, 16) && (p.ld_ar * esz) % 16 == 0 && aligned(p.scale_row, 8) &&
               p.ld_sr % 8 == 0;
   a.col_vec = col && aligned(p.amax_col, 16) && (p.ld_ac * esz) % 16 == 0 &&
               aligned(p.scale_col, 8) && p.ld_sc % 8 == 0;
-  const dim3 grid((unsigned)cdiv(total_row + total_col, 256));
-  if (p.dtype == kBF16)
-    hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(scales_kernel<uint32_t>, grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  auto launch = [&](int64_t r_lo, int64_t nr, int64_t b_lo, int64_t nbd) {
+    a.r_lo = r_lo;
+    a.b_lo = b_lo;
+    a.items_row_total = (uint32_t)(nr * items_row);
+    a.items_col_total = (uint32_t)(nbd * items_col);
+    const dim3 grid((unsigned)cdiv(nr * items_row + nbd * items_col, 256));
+    if (p.dtype == kBF16)
+      hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(scales_kernel<uint32_t>, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  };
+  const int64_t ncol = col ? nbands : 0;
+  if (nrows * items_row + ncol * items_col <= kMaxScaleItems)  // the usual case: one launch
+    return launch(a.r_first, nrows, a.b_first, ncol);
+  // larger fragments: launches of whole rows, then of whole bands, each within the item limit
+  const int64_t rows_per = std::max<int64_t>(1, kMaxScaleItems / items_row);
+  for (int64_t r = a.r_first; r <= a.r_last; r += rows_per) {
+    const hipError_t e = launch(r, std::min(rows_per, a.r_last - r + 1), 0, 0);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t bands_per = std::max<int64_t>(1, kMaxScaleItems / items_col);
+  for (int64_t b = a.b_first; col && b <= a.b_last; b += bands_per) {
+    const hipError_t e = launch(0, 0, b, std::min(bands_per, a.b_last - b + 1));
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t count, int dtype,

@@ -170,3 +170,25 @@ def random_matrix(rows: int, cols: int, dtype: str, seed: int, kind: str = "mixe
     else:
         raise ValueError(kind)
     return to_dtype(x.ravel(), dtype)
+
+
+def device_matrix(rows: int, cols: int, dtype: str, seed: int, device) -> "torch.Tensor":
+    """A large weight drawn on the device, for tests past the 32-bit size limits where a
+    host-side draw would take minutes: N(0,1) times a per-row magnitude 2^U, U ~ Uniform[-20,
+    20] (the "mixed" distribution of ``random_matrix`` without its fixed blocks), from torch's
+    seeded device generator, rounded to FP32 and then, for BF16, to BF16 (both RNE).  Returns
+    the flat row-major weight as a bfloat16 or float32 device tensor."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float32
+    out = torch.empty(rows * cols, dtype=tdt, device=device)
+    mag = torch.exp2(torch.rand(rows, generator=g, device=device) * 40.0 - 20.0)
+    step = max(1, (1 << 26) // cols)  # rows per draw: about 2^26 values at a time
+    for r in range(0, rows, step):
+        n = min(step, rows - r)
+        x = torch.randn(n, cols, generator=g, device=device, dtype=torch.float32)
+        x *= mag[r:r + n, None]
+        out[r * cols:(r + n) * cols] = x.reshape(-1).to(tdt)
+    return out
