@@ -1097,81 +1097,133 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
 
 constexpr int kElemTileCols = kWaveSize;  // one lane per column
 
+// One wave per tile of a 32-row band x 64 columns, one lane per column.  All 32 rows are
+// loaded before anything is written.  Each row's two row-wise blocks are reduced over the
+// half-waves and lane 2i + h keeps block h of row i, so the tile's 64 row-wise entries are
+// merged at the end, one per lane, together with the lane's column-wise entry: no load of a
+// row waits on the entry update of the row before it.  Row addresses and the fragment's
+// bounds within each row are uniform over the wave (scalar registers); a lane adds only its
+// column.
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  // the wave index is uniform over the wave: readfirstlane lets the compiler keep the tile's
+  // indices and addresses in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
-  const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
+  const int64_t c0 = (tile % p.ntc) * kElemTileCols;
   const int64_t r0 = band * kBlockLen;
-  const bool cvalid = c < p.cols;
+  const int ncols = (int)min<int64_t>(kElemTileCols, p.cols - c0);  // lanes with a column
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
-  uint32_t cmax = 0;
-  bool ctouched = false, cfull = true;
-  const int half = lane & 32;
-  for (int i = 0; i < nrows; ++i) {
-    const int64_t r = r0 + i;
-    const int64_t g = r * p.cols + c;
-    const bool inside = cvalid && g >= p.start && g < p.end;
-    uint32_t a = 0;
-    if (inside) a = abs_bits<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
-    if constexpr (kCol) {
-      cmax = umax(cmax, a);
-      ctouched |= inside;
-      cfull &= inside || !cvalid;
-    }
-    const uint32_t m = half_wave_max(a);
-    const uint32_t in_h = (uint32_t)(__ballot(inside) >> half);
-    const uint32_t val_h = (uint32_t)(__ballot(cvalid) >> half);
-    if ((lane & 31) == 0 && in_h != 0)
-      merge_entry<T>(p.amax_row, r * p.ld_ar + (c >> 5), m, in_h == val_h);
+  const T* in_base = static_cast<const T*>(p.input);
+  uint32_t a[kBlockLen];
+  uint32_t in = 0;  // bit i: element (r0 + i, c0 + lane) lies in the fragment
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i) {
+    const int64_t g0 = (r0 + i) * p.cols + c0;  // flat index of the row's lane 0
+    const int lo = (int)max<int64_t>(0, min<int64_t>(kElemTileCols, p.start - g0));
+    const int hi = i < nrows ? (int)max<int64_t>(0, min<int64_t>(ncols, p.end - g0)) : 0;
+    const bool inside = lane >= lo && lane < hi;
+    // every lane loads (lanes outside the fragment read its first element), so no load sits
+    // in a branch that would wait for it
+    const uint32_t v = load_raw(in_base, inside ? g0 - p.start + lane : 0, (int)sizeof(T));
+    a[i] = inside ? abs_bits<T, kPre>(v) : 0u;
+    in |= (uint32_t)inside << i;
   }
+  const uint64_t valid = __ballot(lane < ncols);
+  uint32_t cmax = 0, rv = 0;
+  bool rin = false, rfull = false;
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i) {
+    if constexpr (kCol) cmax = umax(cmax, a[i]);
+    const uint32_t m = half_wave_max(a[i]);
+    const uint64_t inb = __ballot((in >> i) & 1u);
+    if (lane == 2 * i) {
+      rv = __builtin_amdgcn_readlane(m, 0);
+      rin = (uint32_t)inb != 0;
+      rfull = (uint32_t)inb == (uint32_t)valid;
+    }
+    if (lane == 2 * i + 1) {
+      rv = __builtin_amdgcn_readlane(m, 32);
+      rin = (uint32_t)(inb >> 32) != 0;
+      rfull = (uint32_t)(inb >> 32) == (uint32_t)(valid >> 32);
+    }
+  }
+  if (rin) merge_entry<T>(p.amax_row, (r0 + (lane >> 1)) * p.ld_ar + (c0 >> 5) + (lane & 1), rv, rfull);
   if constexpr (kCol) {
-    if (cvalid && ctouched) merge_entry<T>(p.amax_col, band * p.ld_ac + c, cmax, cfull);
+    const uint32_t all = nrows == kBlockLen ? ~0u : (1u << nrows) - 1u;
+    if (in != 0) merge_entry<T>(p.amax_col, band * p.ld_ac + c0 + lane, cmax, in == all);
   }
 }
 
+// Same tiling.  Lane 2i + h fetches the scale (or, fused, the amax entry) of block h of row i
+// and every lane its column's, then all 32 rows are loaded, and only then is anything
+// written; each row's two block scales reach their half-waves by readlane.
 template <typename T, bool kCol, bool kPre, bool kFuse>
 __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  // the wave index is uniform over the wave: readfirstlane lets the compiler keep the tile's
+  // indices and addresses in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
-  const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
-  if (c >= p.cols) return;
+  const int64_t c0 = (tile % p.ntc) * kElemTileCols;
   const int64_t r0 = band * kBlockLen;
+  const int ncols = (int)min<int64_t>(kElemTileCols, p.cols - c0);
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
-  int cshift = 0;
-  if constexpr (kCol) {
-    if constexpr (kFuse) {
-      const uint8_t sb = e8m0_of<T>(static_cast<const T*>(p.amax_col)[band * p.ld_ac + c]);
-      cshift = 127 - (int)sb;
-      if (col_block_touched(corners_of(p), r0, r0 + nrows - 1, c))
-        p.scale_col[band * p.ld_sc + c] = sb;
-    } else {
-      cshift = 127 - (int)p.scale_col[band * p.ld_sc + c];
+  const bool cvalid = lane < ncols;
+  const int64_t rb = r0 + (lane >> 1);                 // the lane's row-wise block: row rb,
+  const int64_t cb = c0 + kBlockLen * (lane & 1);      // columns from cb
+  const bool bvalid = (lane >> 1) < nrows && cb < p.cols;
+  // unconditional loads (lanes without a block or column read the tile's first one), so
+  // that none waits in a branch before the input loads go out
+  const int64_t rbs = bvalid ? rb : r0, cbs = bvalid ? cb : c0, ccs = c0 + (cvalid ? lane : 0);
+  const uint32_t bsc = kFuse ? e8m0_of<T>(row_amax<T>(p, rbs, cbs))
+                             : p.scale_row[rbs * p.ld_sr + (cbs >> 5)];
+  uint32_t csb = 0;
+  if constexpr (kCol)
+    csb = kFuse ? e8m0_of<T>(static_cast<const T*>(p.amax_col)[band * p.ld_ac + ccs])
+                : p.scale_col[band * p.ld_sc + ccs];
+  const T* in_base = static_cast<const T*>(p.input);
+  uint32_t raw[kBlockLen];
+  uint32_t in = 0;
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i) {
+    const int64_t g0 = (r0 + i) * p.cols + c0;
+    const int lo = (int)max<int64_t>(0, min<int64_t>(kElemTileCols, p.start - g0));
+    const int hi = i < nrows ? (int)max<int64_t>(0, min<int64_t>(ncols, p.end - g0)) : 0;
+    const bool inside = lane >= lo && lane < hi;
+    const uint32_t v = load_raw(in_base, inside ? g0 - p.start + lane : 0, (int)sizeof(T));
+    raw[i] = inside ? v : 0u;
+    in |= (uint32_t)inside << i;
+  }
+  if constexpr (kFuse) {  // the scales of the blocks the fragment touches
+    if (bvalid && row_block_touched(p, rb, cb)) p.scale_row[rb * p.ld_sr + (cb >> 5)] = (uint8_t)bsc;
+    if constexpr (kCol) {
+      if (cvalid && col_block_touched(corners_of(p), r0, r0 + nrows - 1, c0 + lane))
+        p.scale_col[band * p.ld_sc + c0 + lane] = (uint8_t)csb;
     }
   }
-  for (int i = 0; i < nrows; ++i) {
-    const int64_t r = r0 + i;
-    const int64_t g = r * p.cols + c;
-    const bool inside = g >= p.start && g < p.end;
-    // fused: the lane at the start of a row-wise block writes its scale if the block is touched
-    const bool wr = kFuse && (c & (kBlockLen - 1)) == 0 && row_block_touched(p, r, c);
-    if (!inside && !wr) continue;
-    const uint8_t sb = kFuse ? e8m0_of<T>(row_amax<T>(p, r, c)) : p.scale_row[r * p.ld_sr + (c >> 5)];
-    if (wr) p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
-    if (!inside) continue;
-    const float w = work_value<T, kPre>(load_raw(p.input, g - p.start, (int)sizeof(T)));
-    p.data_row[g - p.start] = cvt1(w, 127 - (int)sb);
-    if constexpr (kCol) p.data_col[g - p.start] = cvt1(w, cshift);
+  const int cshift = 127 - (int)csb;
+#pragma unroll
+  for (int i = 0; i < kBlockLen; ++i) {
+    const uint32_t s0 = __builtin_amdgcn_readlane(bsc, 2 * i);
+    const uint32_t s1 = __builtin_amdgcn_readlane(bsc, 2 * i + 1);
+    if ((in >> i) & 1u) {
+      const float w = work_value<T, kPre>(raw[i]);
+      const int64_t o = (r0 + i) * p.cols + c0 - p.start;  // uniform: the row's lane 0
+      p.data_row[o + lane] = cvt1(w, 127 - (int)(lane < 32 ? s0 : s1));
+      if constexpr (kCol) p.data_col[o + lane] = cvt1(w, cshift);
+    }
   }
 }
 
@@ -1180,7 +1232,8 @@ __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
 template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t gtile = ga.base + (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
   const int64_t tile = gtile - ga.first[k];
@@ -1192,10 +1245,14 @@ __global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
   const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
   uint32_t raw[kBlockLen];
 #pragma unroll
-  for (int i = 0; i < kBlockLen; ++i)
-    raw[i] = (cvalid && i < nrows)
-                 ? load_raw(p.input, (r0 + i) * p.cols + c - p.start, (int)sizeof(T))
-                 : 0u;
+  for (int i = 0; i < kBlockLen; ++i) {
+    // every lane loads (lanes without an element read the fragment's first one), so no load
+    // sits in a branch that would wait for it
+    const bool valid = cvalid && i < nrows;
+    const uint32_t v =
+        load_raw(p.input, valid ? (r0 + i) * p.cols + c - p.start : 0, (int)sizeof(T));
+    raw[i] = valid ? v : 0u;
+  }
   int cshift = 0;
   if constexpr (kCol) {
     uint32_t cmax = 0;
@@ -1210,19 +1267,21 @@ __global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
   }
 #pragma unroll
   for (int i = 0; i < kBlockLen; ++i) {
-    if (i >= nrows) break;
-    const int64_t r = r0 + i;
-    const uint32_t m = half_wave_max(abs_bits<T, kPre>(raw[i]));  // the lane's row-wise block
-    const uint8_t sb = e8m0_of<T>(m);
-    if (cvalid && (lane & 31) == 0) {
-      p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
-      if (p.amax_row) static_cast<T*>(p.amax_row)[r * p.ld_ar + (c >> 5)] = (T)m;
+    if (i < nrows) {
+      const int64_t r = r0 + i;
+      const uint32_t m = half_wave_max(abs_bits<T, kPre>(raw[i]));  // the lane's row-wise block
+      const uint8_t sb = e8m0_of<T>(m);
+      if (cvalid && (lane & 31) == 0) {
+        p.scale_row[r * p.ld_sr + (c >> 5)] = sb;
+        if (p.amax_row) static_cast<T*>(p.amax_row)[r * p.ld_ar + (c >> 5)] = (T)m;
+      }
+      if (cvalid) {
+        const float w = work_value<T, kPre>(raw[i]);
+        const int64_t o = r * p.cols + c - p.start;
+        p.data_row[o] = cvt1(w, 127 - (int)sb);
+        if constexpr (kCol) p.data_col[o] = cvt1(w, cshift);
+      }
     }
-    if (!cvalid) continue;
-    const float w = work_value<T, kPre>(raw[i]);
-    const int64_t o = r * p.cols + c - p.start;
-    p.data_row[o] = cvt1(w, 127 - (int)sb);
-    if constexpr (kCol) p.data_col[o] = cvt1(w, cshift);
   }
 }
 
