@@ -167,9 +167,10 @@ const char* mxfp8_last_error(void);
  * cols % 8 == 0 for BF16, cols % 4 == 0 for FP32, whatever the alignment of input and
  * outputs), 0 = the element-wise path (other cols), negative = the piece fails validation
  * (the status code, negated).
- * Host-only; launches nothing.  The vectorized path may read, never write, up to 15 bytes
- * before the first and after the last input element, within the same 16-byte-aligned
- * granule (the same memory page), and ignores them. */
+ * Host-only; launches nothing.  For a BF16 input 2 bytes past a 4-byte boundary the
+ * vectorized path reads, never writes, the 2 bytes that share a 4-byte word with the first
+ * and with the last input element, and ignores them; no kernel reads anything else outside
+ * the fragment. */
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel);
 
 #ifdef __cplusplus
