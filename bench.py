@@ -362,7 +362,7 @@ def main():
         del pairs
 
     if args.kernel_table:
-        out["kernels"] = kernel_table(args, sets if args.dtype == "bf16" else None, m, dev, tdt)
+        out["kernels"], out["kernels_other_shapes"] = kernel_table(args, m, dev)
 
     if args.cpu:
         out["cpu_baseline"] = cpu
@@ -467,119 +467,142 @@ def graph_step_us(args, step_fns):
     return round(us, 2)
 
 
-def kernel_table(args, bf16_sets, m_default, dev, tdt_default):
+# The matrices of the pages' per-call table ("Bidirectional kernel performance"), largest first.
+TABLE_SHAPES = [(16384, 6144), (4096, 4096), (1024, 1024), (160, 96)]
+
+
+def kernel_table(args, m_default, dev):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
-    scales + cast and (full input only) the single-pass quantize: full input and
-    the quarter fragment starting at offset 17, both directions, BF16 and FP32.  Timed like the
-    pages: HIP events around replays of a captured graph of 10 calls, median per call over the
-    replays.  Calls rotate over distinct buffer sets holding >= the footprint option in all
-    (full runs: whole matrices; partial runs: quarter-size fragments placed so that
-    input - 17 elements stays 16-byte aligned), so inputs come from HBM rather than the 256 MB
-    Infinity Cache."""
+    scales + cast and (full input only) the single-pass quantize, for every matrix of that
+    table (16384x6144, 4096x4096, 1024x1024, 160x96): full input and the quarter fragment
+    starting at offset 17, both directions, BF16 and FP32.  Timed like the pages: HIP events
+    around replays of a captured graph of 50 calls (up to 4 M elements) or 10 calls (larger),
+    median per call over the replays.  Calls rotate over distinct buffer sets, as many as
+    reach the footprint option but at most one per call of the graph (full runs: whole
+    matrices; partial runs: quarter-size fragments placed so that input - 17 elements stays
+    16-byte aligned): the two large matrices stream from HBM, the small ones stay in the 256 MB
+    Infinity Cache like any repeated small call.  Returns the 16384x6144 entries and, by
+    shape, the others."""
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import workloads as wl
+
+    table, by_shape = {}, {}
+    for rows, cols in TABLE_SHAPES:
+        for dtype in ("bf16", "fp32"):
+            if (rows, cols) == (16384, 6144):
+                if dtype == args.dtype:
+                    m = m_default
+                else:
+                    log(f"generating {rows}x{cols} {dtype} input for the kernel table")
+                    m = wl.matrix_large(dtype)
+            else:  # N(0,1) times a per-column 2^U[-8, 8], the 4096x4096 recipe
+                m = wl.matrix_square(dtype, rows=rows, cols=cols)
+            entries = time_shape(args, m, dev)
+            if (rows, cols) == (16384, 6144):
+                table.update(entries)
+            else:
+                by_shape.setdefault(f"{rows}x{cols}", {}).update(entries)
+            torch.cuda.empty_cache()
+    return table, by_shape
+
+
+def time_shape(args, m, dev):
+    """The table's entries for one matrix in one dtype (see ``kernel_table``)."""
     import numpy as np
     import torch
 
     from mxfp8_block_scaled_partial_amd import binding as B
     from mxfp8_block_scaled_partial_amd import bytes_model as BM
-    from mxfp8_block_scaled_partial_amd import workloads as wl
 
-    rows, cols = 16384, 6144
+    rows, cols, dtype = m.rows, m.cols, m.dtype
     n = rows * cols
-    nb, nbands = cols // 32, rows // 32
-    table = {}
-    for dtype in ("bf16", "fp32"):
-        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-        s_in = 2 if dtype == "bf16" else 4
-        if dtype == args.dtype:
-            m = m_default
-        else:
-            log(f"generating {rows}x{cols} {dtype} input for the kernel table")
-            m = wl.matrix_large(dtype)
-        host = m.data
-        x0 = (torch.from_numpy(host.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
-              else torch.from_numpy(host)).to(dev)
-        for run, (s, l) in (("full", (0, n)), ("partial", (17, n // 4))):
-            lead = s % 32                      # element offset that keeps input - s aligned
-            per_set = l * s_in + 2 * l + 2 * (n // 32) * (s_in + 1)
-            n_sets = max(2, int(np.ceil(args.min_footprint_gb * 1e9 / per_set)))
-            amax_p, cast_p, fused_p, keep = [], [], [], []
-            for i in range(n_sets):
-                xb = torch.empty(l + 32, dtype=tdt, device=dev)
-                xb[lead:lead + l] = x0[s:s + l]
-                x = xb[lead:lead + l]
-                ar = torch.zeros(rows, nb, dtype=tdt, device=dev)
-                ac = torch.zeros(nbands, cols, dtype=tdt, device=dev)
-                sr = torch.full((rows, nb), 120, dtype=torch.uint8, device=dev)
-                sc = torch.full((nbands, cols), 120, dtype=torch.uint8, device=dev)
-                drb = torch.empty(l + 32, dtype=torch.uint8, device=dev)
-                dcb = torch.empty(l + 32, dtype=torch.uint8, device=dev)
-                dr, dc = drb[lead:lead + l], dcb[lead:lead + l]
-                keep.append((xb, ar, ac, sr, sc, drb, dcb))
-                amax_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac))
-                cast_p.append(B.make_piece(rows, cols, s, x, scale_row=sr, scale_col=sc,
-                                           data_row=dr, data_col=dc))
-                fused_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac,
-                                            scale_row=sr, scale_col=sc, data_row=dr,
-                                            data_col=dc))
-                assert B.mxfp8_query_path(amax_p[-1], 0) == 1
-                assert B.mxfp8_query_path(cast_p[-1], 1) == 1
-                assert B.mxfp8_query_path(fused_p[-1], 2) == 1
-                assert run != "full" or B.mxfp8_query_path(fused_p[-1], 3) == 1
-            pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
-            # the amax runs first, so the fused call reads real amax entries; the single-pass
-            # quantize needs whole bands, so it runs on the full input only
-            kernels = [("amax", amax_p, B.mxfp8_partial_amax),
-                       ("cast", cast_p, B.mxfp8_partial_cast),
-                       ("scales_cast", fused_p, B.mxfp8_scales_and_cast)]
-            if run == "full":
-                kernels.append(("quantize", fused_p, B.mxfp8_quantize))
-            for kname, pieces, fn in kernels:
-                for i in range(3):
+    nb, nbands = B.nblocks(cols), B.nblocks(rows)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    s_in = 2 if dtype == "bf16" else 4
+    per_graph = 50 if n <= 4 * 1024 * 1024 else 10
+    x0 = (torch.from_numpy(m.data.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+          else torch.from_numpy(m.data)).to(dev)
+    out = {}
+    for run, (s, l) in (("full", (0, n)), ("partial", (17, n // 4))):
+        lead = s % 32                      # element offset that keeps input - s aligned
+        per_set = l * s_in + 2 * l + (rows * nb + nbands * cols) * (s_in + 1)
+        n_sets = max(2, min(per_graph, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
+        amax_p, cast_p, fused_p, keep = [], [], [], []
+        for i in range(n_sets):
+            xb = torch.empty(l + 32, dtype=tdt, device=dev)
+            xb[lead:lead + l] = x0[s:s + l]
+            x = xb[lead:lead + l]
+            ar = torch.zeros(rows, nb, dtype=tdt, device=dev)
+            ac = torch.zeros(nbands, cols, dtype=tdt, device=dev)
+            sr = torch.full((rows, nb), 120, dtype=torch.uint8, device=dev)
+            sc = torch.full((nbands, cols), 120, dtype=torch.uint8, device=dev)
+            drb = torch.empty(l + 32, dtype=torch.uint8, device=dev)
+            dcb = torch.empty(l + 32, dtype=torch.uint8, device=dev)
+            dr, dc = drb[lead:lead + l], dcb[lead:lead + l]
+            keep.append((xb, ar, ac, sr, sc, drb, dcb))
+            amax_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac))
+            cast_p.append(B.make_piece(rows, cols, s, x, scale_row=sr, scale_col=sc,
+                                       data_row=dr, data_col=dc))
+            fused_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac,
+                                        scale_row=sr, scale_col=sc, data_row=dr,
+                                        data_col=dc))
+            assert B.mxfp8_query_path(amax_p[-1], 0) == 1
+            assert B.mxfp8_query_path(cast_p[-1], 1) == 1
+            assert B.mxfp8_query_path(fused_p[-1], 2) == 1
+            assert run != "full" or B.mxfp8_query_path(fused_p[-1], 3) == 1
+        pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
+        # the amax runs first, so the fused call reads real amax entries; the single-pass
+        # quantize needs whole bands, so it runs on the full input only
+        kernels = [("amax", amax_p, B.mxfp8_partial_amax),
+                   ("cast", cast_p, B.mxfp8_partial_cast),
+                   ("scales_cast", fused_p, B.mxfp8_scales_and_cast)]
+        if run == "full":
+            kernels.append(("quantize", fused_p, B.mxfp8_quantize))
+        for kname, pieces, fn in kernels:
+            for i in range(3):
+                fn(pieces[i % n_sets])
+            torch.cuda.synchronize()
+            # the pages' method: HIP-event timing of graph replays (each call on the next
+            # buffer set), median per call over the replays
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
                     fn(pieces[i % n_sets])
-                torch.cuda.synchronize()
-                # the pages' method: HIP-event timing of graph replays, 10 calls per graph
-                # (each on the next buffer set), median per call over the replays
-                per_graph = 10
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(per_graph):
-                        fn(pieces[i % n_sets])
+            g.replay()
+            torch.cuda.synchronize()
+            ev = [(TimingEvent(), TimingEvent()) for _ in range(args.kernel_calls)]
+            for e0, e1 in ev:
+                e0.record()
                 g.replay()
-                torch.cuda.synchronize()
-                ev = [(TimingEvent(), TimingEvent())
-                      for _ in range(args.kernel_calls)]
-                for e0, e1 in ev:
-                    e0.record()
-                    g.replay()
-                    e1.record()
-                torch.cuda.synchronize()
-                us = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
-                del g
-                gbs = pb[kname] / (us * 1e-6) / 1e9
-                entry = {"us": round(us, 2), "GBps": round(gbs, 1),
-                         "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                         "alg_bytes": pb[kname], "buffer_sets": n_sets}
-                # the same call on one buffer set over and over: what stays in the 256 MB
-                # Infinity Cache between calls is not re-read from HBM (cache-resident figure)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    for i in range(per_graph):
-                        fn(pieces[0])
+                e1.record()
+            torch.cuda.synchronize()
+            us = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
+            del g
+            gbs = pb[kname] / (us * 1e-6) / 1e9
+            entry = {"us": round(us, 2), "GBps": round(gbs, 1),
+                     "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "alg_bytes": pb[kname], "buffer_sets": n_sets, "calls_per_graph": per_graph}
+            # the same call on one buffer set over and over: what stays in the 256 MB
+            # Infinity Cache between calls is not re-read from HBM (cache-resident figure)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
+                    fn(pieces[0])
+            g.replay()
+            torch.cuda.synchronize()
+            for e0, e1 in ev:
+                e0.record()
                 g.replay()
-                torch.cuda.synchronize()
-                for e0, e1 in ev:
-                    e0.record()
-                    g.replay()
-                    e1.record()
-                torch.cuda.synchronize()
-                hot = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
-                del g
-                entry["hot_us_cache_resident"] = round(hot, 2)
-                table[f"{kname}_{dtype}_{run}"] = entry
-            del keep, amax_p, cast_p, fused_p
-            torch.cuda.empty_cache()
-        del x0
-    return table
+                e1.record()
+            torch.cuda.synchronize()
+            hot = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
+            del g
+            entry["hot_us_cache_resident"] = round(hot, 2)
+            out[f"{kname}_{dtype}_{run}"] = entry
+        del keep, amax_p, cast_p, fused_p
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(m, cpu_rows, s_in, gpu=None):

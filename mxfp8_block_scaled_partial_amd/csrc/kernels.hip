@@ -37,6 +37,9 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "mxfp8_internal.h"
@@ -49,20 +52,27 @@ constexpr int kWaveSize = 64;
 constexpr int kWavesPerGroup = 4;
 constexpr int kThreads = kWaveSize * kWavesPerGroup;
 constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round-robin
-// Resident waves per SIMD the register allocator targets in the vector kernels, per kernel and
-// element type (chosen by measurement on MI355X; without a target the edge-tile path inflates
-// every wave's register budget).
-// Large amax launches run best with few, register-rich waves; small ones (a single rank's
-// fragment) need more resident waves to fill the GPU in one round, so both amax variants are
-// compiled and the launch picks one by its tile count.  The cast's register need is set by
-// its edge / unaligned-output path, so it has one variant.
+// Occupancy of the vector kernels, per kernel and element type, chosen by measurement on
+// MI355X.  kAmax / kAmaxSmall / kCast are the resident waves per SIMD the register allocator
+// must allow.  Large launches (kSmallLaunchTiles tiles or more) stream best with few resident
+// workgroups per CU (kAmaxCap / cast_cap: more only add contention, fewer starve the stream);
+// the kernels' register use would let more in, so such a launch reserves enough LDS to hold
+// residency at the cap.  Small launches (a single rank's fragment) need every resident
+// workgroup they can get to fill the GPU in one round: no cap, and the amax has a variant
+// compiled for more waves.
 template <typename T>
 struct Occupancy {
   static constexpr int kAmax = 4;
   static constexpr int kAmaxSmall = 6;
   static constexpr int kCast = sizeof(T) == 2 ? 3 : 2;
+  static constexpr int kAmaxCap = 4;
+  // cast: 3 for BF16 with both directions, else 4; cast with fused scales: 4 for FP32 with
+  // both directions, else no cap (0)
+  static constexpr int cast_cap(bool col, bool fuse) {
+    return fuse ? (sizeof(T) == 4 && col ? 4 : 0) : (sizeof(T) == 2 && col ? 3 : 4);
+  }
 };
-constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles, use kAmaxSmall
+constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-launch settings
 
 struct TileArgs {
   int64_t rows, cols, start, end;
@@ -84,6 +94,7 @@ struct TileArgs {
   int32_t row_vec;  // amax_row rows are 16-byte aligned: a tile's row entries move as vectors
   int32_t in_shift2;  // BF16 input with input - start at 2 mod 4 bytes: chunks need a 2-byte shift
   int32_t mo_row, mo_col;  // (data - start) mod 4 of each output: 0 = chunks store directly
+  int32_t sc_vec;  // scale_col rows aligned to a chunk's E bytes: a lane's scale bytes are one load
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
@@ -330,74 +341,162 @@ typedef unsigned int v2u __attribute__((ext_vector_type(2), aligned(4)));
 
 // The input is streamed once: non-temporal loads (the "nt" cache policy) keep it from
 // displacing reused lines; on MI355X they also lift a pure read stream from ~5.9 to ~6.7 TB/s.
-__device__ __forceinline__ void load16_stream(const void* p, uint32_t (&d)[4]) {
-  const v4u v = __builtin_nontemporal_load(static_cast<const v4u*>(p));
-  d[0] = v.x;
-  d[1] = v.y;
-  d[2] = v.z;
-  d[3] = v.w;
+//
+// A chunk is loaded in two steps, issue_chunk and then assemble_chunk, so that a wave issues
+// the loads of all its rows before it uses (and so waits for) any of them: a use inside the
+// branch that loads a row makes the compiler wait there, one round trip per row.
+struct RawChunk {
+  v4u v;
+  uint32_t t;
+};
+
+// The 16 bytes at p.  With shift2 (BF16 input whose input - start sits at 2 mod 4) p is 2
+// bytes past a dword boundary: the dword-aligned 16 bytes before it plus the next dword are
+// loaded instead.  The extra 2 bytes on each side lie in the same dwords as the chunk's first
+// and last element.
+__device__ __forceinline__ void issue_chunk(const void* p, bool shift2, RawChunk& r) {
+  if (shift2) {
+    const uint8_t* b = static_cast<const uint8_t*>(p) - 2;
+    r.v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(b));
+    r.t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 16));
+  } else {
+    r.v = __builtin_nontemporal_load(static_cast<const v4u*>(p));
+    r.t = 0;
+  }
 }
 
-// The 16 bytes at p, p 2 bytes past a dword boundary (BF16 input whose input - start sits at
-// 2 mod 4): the dword-aligned 16 bytes before it plus the next dword, shifted by 2 bytes.  The
-// extra 2 bytes on each side lie in the same dwords as the chunk's first and last element.
-__device__ __forceinline__ void load16_stream_shift2(const void* p, uint32_t (&d)[4]) {
-  const uint8_t* b = static_cast<const uint8_t*>(p) - 2;
-  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(b));
-  const uint32_t t = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 16));
-  d[0] = __builtin_amdgcn_alignbyte(v.y, v.x, 2);
-  d[1] = __builtin_amdgcn_alignbyte(v.z, v.y, 2);
-  d[2] = __builtin_amdgcn_alignbyte(v.w, v.z, 2);
-  d[3] = __builtin_amdgcn_alignbyte(t, v.w, 2);
+__device__ __forceinline__ void assemble_chunk(const RawChunk& r, bool shift2, uint32_t (&d)[4]) {
+  if (shift2) {
+    d[0] = __builtin_amdgcn_alignbyte(r.v.y, r.v.x, 2);
+    d[1] = __builtin_amdgcn_alignbyte(r.v.z, r.v.y, 2);
+    d[2] = __builtin_amdgcn_alignbyte(r.v.w, r.v.z, 2);
+    d[3] = __builtin_amdgcn_alignbyte(r.t, r.v.w, 2);
+  } else {
+    d[0] = r.v.x;
+    d[1] = r.v.y;
+    d[2] = r.v.z;
+    d[3] = r.v.w;
+  }
 }
 
-__device__ __forceinline__ void load_chunk(const void* p, bool shift2, uint32_t (&d)[4]) {
-  if (shift2)
-    load16_stream_shift2(p, d);
-  else
-    load16_stream(p, d);
+// Chunks src + i * cols, i < n (n <= RW; the others stay as they are): all loads are issued
+// before any is assembled.
+template <typename T, int RW>
+__device__ __forceinline__ void load_rows(const T* src, int64_t cols, bool shift2, int n,
+                                          uint32_t (&d)[RW][4]) {
+  RawChunk raw[RW];
+  if (shift2) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (i < n) issue_chunk(src + i * cols, true, raw[i]);
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (i < n) assemble_chunk(raw[i], true, d[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (i < n) issue_chunk(src + i * cols, false, raw[i]);
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      if (i < n) assemble_chunk(raw[i], false, d[i]);
+  }
 }
 
-// Chunk whose elements straddle a fragment boundary: load only the fragment's elements.
+// Chunk g whose elements a fragment boundary cuts: the fragment's elements, one load each,
+// into el (the others 0); returns the element mask.  Nothing here uses a loaded value.
 template <typename T>
-__device__ __forceinline__ uint32_t load_masked(const TileArgs& p, int64_t g, uint32_t (&d)[4]) {
+__device__ __forceinline__ uint32_t issue_masked(const TileArgs& p, int64_t g,
+                                                 uint32_t (&el)[Chunk<T>::E]) {
   constexpr int E = Chunk<T>::E;
   uint32_t mask = 0;
-  d[0] = d[1] = d[2] = d[3] = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t i = g + e;
+    el[e] = 0;
     if (i >= p.start && i < p.end) {
-      const uint32_t raw = load_raw(p.input, i - p.start, (int)sizeof(T));
-      if constexpr (sizeof(T) == 2)
-        d[e >> 1] |= raw << ((e & 1) * 16);
-      else
-        d[e] = raw;
+      el[e] = load_raw(p.input, i - p.start, (int)sizeof(T));
       mask |= 1u << e;
     }
   }
   return mask;
 }
 
-// Rows i < nrows_here of an edge tile: chunk i of the wave's rows, masked to the fragment.
-// Every load is issued before any result is used.  Returns per-row element masks in em.
+template <typename T>
+__device__ __forceinline__ void assemble_masked(const uint32_t (&el)[Chunk<T>::E],
+                                                uint32_t (&d)[4]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = el[2 * j] | (el[2 * j + 1] << 16);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[j] = el[j];
+  }
+}
+
+// Rows i < nrows_here of an edge tile: chunk i of the wave's rows, masked to the fragment, in
+// d, with per-row element masks in em.  The whole chunks' loads go out first, then the element
+// loads of the chunks a fragment boundary cuts (a lane has at most two: the fragment's start
+// and end), and only then is anything assembled.
 template <typename T, int RW>
 __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
                                                  int nrows_here, int64_t c, bool cvalid,
                                                  uint32_t (&d)[RW][4], uint32_t (&em)[RW]) {
   constexpr int E = Chunk<T>::E;
+  uint32_t full = 0;      // bit i: row i's chunk lies wholly inside the fragment
+  int cut0 = -1, cut1 = -1;  // rows whose chunk a fragment boundary cuts
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-    em[i] = 0;
     if (i < nrows_here && cvalid) {
       const int64_t g = (rfirst + i) * p.cols + c;
       if (g >= p.start && g + E <= p.end) {
-        load_chunk(src + i * p.cols, p.in_shift2, d[i]);
-        em[i] = (1u << E) - 1;
+        full |= 1u << i;
       } else if (g + E > p.start && g < p.end) {
-        em[i] = load_masked<T>(p, g, d[i]);
+        if (cut0 < 0)
+          cut0 = i;
+        else
+          cut1 = i;
       }
+    }
+  }
+  // Every lane issues every row's chunk load, rows without a whole chunk reading the
+  // fragment's first whole chunk instead (discarded): a load under a per-lane condition would
+  // make the compiler wait for it where the branches join.  That chunk starts at the first
+  // multiple of E at or after start (chunks start at multiples of E of the flat index, since
+  // cols % E == 0), so its load touches only what a whole chunk's load touches; it is not
+  // input itself, which with a 2-byte shift would read the 2 bytes before the fragment, in
+  // another dword.  A fragment without a whole chunk loads nothing.
+  RawChunk raw[RW];
+  const int64_t g_whole = (p.start + E - 1) / E * E;
+  if (g_whole + E <= p.end) {
+    const T* whole = static_cast<const T*>(p.input) + (g_whole - p.start);
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+      issue_chunk(((full >> i) & 1u) ? src + i * p.cols : whole, p.in_shift2, raw[i]);
+  }
+  uint32_t el0[E], el1[E], m0 = 0, m1 = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) el0[e] = el1[e] = 0;
+  if (cut0 >= 0) m0 = issue_masked<T>(p, (rfirst + cut0) * p.cols + c, el0);
+  if (cut1 >= 0) m1 = issue_masked<T>(p, (rfirst + cut1) * p.cols + c, el1);
+  uint32_t c0d[4], c1d[4];
+  assemble_masked<T>(el0, c0d);
+  assemble_masked<T>(el1, c1d);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const bool whole = (full >> i) & 1u;
+    assemble_chunk(raw[i], p.in_shift2, d[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d[i][j] = whole ? d[i][j] : 0u;
+    em[i] = whole ? (1u << E) - 1 : 0u;
+    if (i == cut0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[i][j] = c0d[j];
+      em[i] = m0;
+    }
+    if (i == cut1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[i][j] = c1d[j];
+      em[i] = m1;
     }
   }
 }
@@ -497,15 +596,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   if (interior) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-    if (cvalid) {
-      if (p.in_shift2) {
-#pragma unroll
-        for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
-      }
-    }
+    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
     // Entries of the tile: 32 rows x NBLK row-wise blocks (32 bytes per row) and 64*E
     // column-wise blocks.  Their old values are fetched together with the input so that no
     // memory latency remains after the reduction; wave 1 then writes the row-wise entries as
@@ -765,13 +856,42 @@ __device__ __forceinline__ void store_col_scales(const TileArgs& p, int64_t band
   store_scale_bytes<E>(p.scale_col + band * p.ld_sc + c, sb, m);
 }
 
+// Not fused: the column-wise exponent shifts of the lane's E columns, 127 minus the scale
+// bytes, read as one vector when scale_col rows are aligned to E bytes, else one by one.  The
+// values are used at once, so the caller issues this after the tile's other loads: the wait
+// then covers them all.
+template <typename T>
+__device__ __forceinline__ void col_shifts(const TileArgs& p, int64_t band, int64_t c,
+                                           int (&cshift)[Chunk<T>::E]) {
+  constexpr int E = Chunk<T>::E;
+  const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
+  uint32_t b[E];
+  if (p.sc_vec) {
+    uint32_t w[E / 4];
+    if constexpr (E == 8) {
+      const uint2 v = *reinterpret_cast<const uint2*>(sc);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(sc);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[e] = (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) b[e] = sc[e];
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)b[e];
+}
+
 // Tiles a fragment boundary or the short last band cuts, and tiles whose outputs are not
 // dword aligned: masked loads, byte stores or window stores.  The common tile (interior,
 // dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.
 template <typename T, bool kCol, bool kPre, bool kFuse>
 __device__ __forceinline__ void cast_tile_general(
     const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows, bool interior,
-    const int* cshift) {
+    int (&cshift)[Chunk<T>::E]) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
@@ -791,11 +911,13 @@ __device__ __forceinline__ void cast_tile_general(
     for (int i = 0; i < RW; ++i) {
       d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
       em[i] = cvalid ? kFull : 0u;
-      if (cvalid) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
     }
+    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
   } else {
     load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   }
+  // (not fused) the column-wise loads go out after the row-wise ones: their use then waits for
+  // every load of the tile at once
   if constexpr (kFuse) {
     // the first lane of each row-wise block writes the scale of a block the fragment
     // touches; every amax entry is loaded before the first store, so no load waits on one
@@ -805,7 +927,12 @@ __device__ __forceinline__ void cast_tile_general(
     for (int i = 0; i < RW; ++i) {
       wr[i] = (lane & (kBlockLen / E - 1)) == 0 && cvalid && i < nrows - i0 &&
               (interior || row_block_touched(p, r0 + i0 + i, c));
-      ab[i] = (em[i] || wr[i]) ? row_amax<T>(p, r0 + i0 + i, c) : 0u;
+      // unconditional (an entry the lane does not need is read at the band's first row and
+      // the tile's first column, then dropped): a load under a per-lane condition makes the
+      // compiler wait for it where the branches join
+      const bool need = em[i] || wr[i];
+      const uint32_t v = row_amax<T>(p, need ? r0 + i0 + i : r0, need ? c : c0);
+      ab[i] = need ? v : 0u;
     }
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -814,8 +941,18 @@ __device__ __forceinline__ void cast_tile_general(
       if (wr[i]) p.scale_row[(r0 + i0 + i) * p.ld_sr + (c >> 5)] = sb;
     }
   } else {
+    uint32_t sb[RW];  // every scale load goes out before the first is used (unconditional,
+                      // as the amax entries above)
 #pragma unroll
-    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)srow[i * p.ld_sr] : 0;
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t v = em[i] ? srow[i * p.ld_sr] : p.scale_row[r0 * p.ld_sr + (c0 >> 5)];
+      sb[i] = em[i] ? v : 0u;
+    }
+    if constexpr (kCol) {
+      if (cvalid) col_shifts<T>(p, band, c, cshift);
+    }
+#pragma unroll
+    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)sb[i] : 0;
   }
   if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
 #pragma unroll
@@ -889,6 +1026,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
 
+  // Column-wise shifts and (fused) scale bytes.  Fused: from the amax entries, here, before
+  // the tile's loads (measured faster than with them); otherwise from the scale bytes, loaded
+  // after the tile's other loads.
   int cshift[E];
   uint8_t csb[E];
 #pragma unroll
@@ -896,48 +1036,57 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     cshift[e] = 0;
     csb[e] = 0;
   }
-  if constexpr (kCol) {
+  if constexpr (kCol && kFuse) {
     if (cvalid) {
-      if constexpr (kFuse) {
-        col_scales<T>(p, band, c, csb);  // written after the tile's loads
+      col_scales<T>(p, band, c, csb);
 #pragma unroll
-        for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)csb[e];
-      } else {
-        const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
-#pragma unroll
-        for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)sc[e];
-      }
+      for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)csb[e];
     }
   }
 
-  if (interior && p.mo_row == 0 && p.mo_col == 0) {  // the common tile: straight-line code
+  // the common tile: interior, dword-aligned outputs and (not fused) column-wise scale bytes
+  // that move as one vector; straight-line code
+  if (interior && p.mo_row == 0 && p.mo_col == 0 && (!kCol || kFuse || p.sc_vec)) {
     if (!cvalid) return;
     const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
     const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
     const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
     uint32_t d[RW][4];
     int rshift[RW];
-    if (p.in_shift2) {
+    // Every load of the tile goes out before any value is used, and before the first store
+    // (which the compiler cannot move a load past): the input rows, the row-wise amax entries
+    // (fused) or scale bytes, then (not fused) the column-wise scale bytes.
+    uint32_t cw[2] = {0, 0};
+    load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+    uint32_t rl[RW];
 #pragma unroll
-      for (int i = 0; i < RW; ++i) load16_stream_shift2(src + i * p.cols, d[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RW; ++i) load16_stream(src + i * p.cols, d[i]);
+    for (int i = 0; i < RW; ++i)
+      rl[i] = kFuse ? row_amax<T>(p, r0 + i0 + i, c) : (uint32_t)srow[i * p.ld_sr];
+    if constexpr (kCol && !kFuse) {
+      if constexpr (E == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p.scale_col + band * p.ld_sc + c);
+        cw[0] = v.x;
+        cw[1] = v.y;
+      } else {
+        cw[0] = *reinterpret_cast<const uint32_t*>(p.scale_col + band * p.ld_sc + c);
+      }
     }
-    if constexpr (kFuse) {
-      // all amax entries are loaded before the first store, so no load waits on a store
-      uint32_t ab[RW];
+    if constexpr (kCol && !kFuse) {
 #pragma unroll
-      for (int i = 0; i < RW; ++i) ab[i] = row_amax<T>(p, r0 + i0 + i, c);
+      for (int e = 0; e < E; ++e) {
+        csb[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
+        cshift[e] = 127 - (int)csb[e];
+      }
+    }
 #pragma unroll
-      for (int i = 0; i < RW; ++i) {
-        const uint8_t sb = e8m0_of<T>(ab[i]);
+    for (int i = 0; i < RW; ++i) {
+      if constexpr (kFuse) {
+        const uint8_t sb = e8m0_of<T>(rl[i]);
         rshift[i] = 127 - (int)sb;
         if ((lane & (kBlockLen / E - 1)) == 0) p.scale_row[(r0 + i0 + i) * p.ld_sr + (c >> 5)] = sb;
+      } else {
+        rshift[i] = 127 - (int)rl[i];
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RW; ++i) rshift[i] = 127 - (int)srow[i * p.ld_sr];
     }
     // all row-wise stores, then all column-wise ones: each output gets one run of stores
     // (interleaving the two directions measured 1.4% slower)
@@ -1004,14 +1153,10 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
 #pragma unroll
   for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
   if (cvalid) {
-    if (nr >= RW) {
-#pragma unroll
-      for (int i = 0; i < RW; ++i) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < RW; ++i)
-        if (i < nr) load_chunk(src + i * p.cols, p.in_shift2, d[i]);
-    }
+    if (nr >= RW)
+      load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+    else
+      load_rows<T, RW>(src, p.cols, p.in_shift2, nr, d);
   }
 
   // amax: rows absent from a short last band, and lanes past the last column, hold zeros
@@ -1468,15 +1613,58 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   };
   a.mo_row = mis(p.data_row);
   a.mo_col = mis(p.data_col);
+  const int64_t e = 16 / esz;  // elements per 16-byte chunk
+  a.sc_vec = p.scale_col && (reinterpret_cast<uintptr_t>(p.scale_col) % e == 0) && (p.ld_sc % e == 0);
   return a;
+}
+
+// LDS bytes per CU of the current device (160 KiB on MI355X), queried once per device; 0 if
+// unknown.
+int lds_per_cu() {
+  static std::atomic<int> cache[64];  // 0: not queried yet; -1: unknown
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || v <= 0)
+      v = -1;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v > 0 ? v : 0;
+}
+
+// Dynamic LDS bytes that hold `kernel` at `cap` resident workgroups per CU (0: no cap).
+template <typename K>
+size_t cap_lds(K kernel, int cap) {
+  const int lds = lds_per_cu();
+  if (cap <= 0 || lds <= 0) return 0;
+  static std::mutex mu;  // static LDS of each kernel, from its attributes, looked up once
+  static std::unordered_map<const void*, size_t> static_lds;
+  const void* key = reinterpret_cast<const void*>(kernel);
+  size_t st;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = static_lds.find(key);
+    if (it == static_lds.end()) {
+      hipFuncAttributes a{};
+      st = hipFuncGetAttributes(&a, key) == hipSuccess ? a.sharedSizeBytes : 0;
+      static_lds.emplace(key, st);
+    } else {
+      st = it->second;
+    }
+  }
+  const size_t per = (size_t)lds / (size_t)cap;
+  return per > st ? per - st : 0;
 }
 
 // Launches `kernel` over the tiles of `ps`, kMaxGroup pieces per launch.  tiles_per_wg is 1
 // for the vector kernels (a workgroup per tile) and kWavesPerGroup for the element-wise ones
-// (a wave per tile).
+// (a wave per tile).  Launches under kSmallLaunchTiles tiles run `small_kernel`; the others
+// run `kernel`, held at `cap` resident workgroups per CU (0: no cap).
 template <typename K>
 hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>& ps,
-                          int tiles_per_wg, hipStream_t s) {
+                          int tiles_per_wg, int cap, hipStream_t s) {
   for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
     GroupArgs g{};
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
@@ -1490,11 +1678,13 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     }
     g.first[g.n] = total;
     const int64_t groups = cdiv(total, tiles_per_wg);
-    const K k = total < kSmallLaunchTiles ? small_kernel : kernel;
+    const bool small = total < kSmallLaunchTiles;
+    const K k = small ? small_kernel : kernel;
+    const size_t shm = small ? 0 : cap_lds(k, cap);
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
       g.base = g0 * tiles_per_wg;
       const int64_t ng = std::min<int64_t>(kMaxLaunchGroups, groups - g0);
-      hipLaunchKernelGGL(k, dim3((unsigned)ng), dim3(kThreads), 0, s, g);
+      hipLaunchKernelGGL(k, dim3((unsigned)ng), dim3(kThreads), shm, s, g);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
@@ -1522,10 +1712,11 @@ hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vecto
   hipError_t e = hipSuccess;
   if (!vec.empty())
     e = launch_grouped(amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmax>,
-                       amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, vec, 1, s);
+                       amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, vec, 1,
+                       Occupancy<T>::kAmaxCap, s);
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, amax_elem_kernel<T, kCol, kPre>, elem,
-                       kWavesPerGroup, s);
+                       kWavesPerGroup, 0, s);
   return e;
 }
 
@@ -1535,10 +1726,11 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
   hipError_t e = hipSuccess;
   if (!vec.empty())
     e = launch_grouped(cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>,
-                       cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1, s);
+                       cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1,
+                       Occupancy<T>::cast_cap(kCol, kFuse), s);
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
-                       elem, kWavesPerGroup, s);
+                       elem, kWavesPerGroup, 0, s);
   return e;
 }
 
@@ -1595,10 +1787,10 @@ hipError_t launch_quantize_bucket(const std::vector<TileArgs>& vec,
   hipError_t e = hipSuccess;
   if (!vec.empty())
     e = launch_grouped(quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
-                       quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, s);
+                       quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, 0, s);
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(quantize_elem_kernel<T, kCol, kPre>, quantize_elem_kernel<T, kCol, kPre>,
-                       elem, kWavesPerGroup, s);
+                       elem, kWavesPerGroup, 0, s);
   return e;
 }
 
