@@ -55,7 +55,8 @@ constexpr int kNumXcd = 8;        // MI355X: 8 XCDs, workgroups dispatched round
 // Occupancy of the vector kernels, per kernel and element type, chosen by measurement on
 // MI355X.  kAmax / kAmaxSmall / kCast are the resident waves per SIMD the register allocator
 // must allow.  Large launches (kSmallLaunchTiles tiles or more) stream best with few resident
-// workgroups per CU (kAmaxCap / cast_cap: more only add contention, fewer starve the stream);
+// workgroups per CU (kAmaxCap / cast_cap / kQuantCap: more only add contention, fewer starve
+// the stream);
 // the kernels' register use would let more in, so such a launch reserves enough LDS to hold
 // residency at the cap.  Small launches (a single rank's fragment) need every resident
 // workgroup they can get to fill the GPU in one round: no cap, and the amax has a variant
@@ -66,10 +67,11 @@ struct Occupancy {
   static constexpr int kAmaxSmall = 6;
   static constexpr int kCast = sizeof(T) == 2 ? 3 : 2;
   static constexpr int kAmaxCap = 4;
-  // cast: 3 for BF16 with both directions, else 4; cast with fused scales: 4 for FP32 with
-  // both directions, else no cap (0)
+  static constexpr int kQuantCap = 5;
+  // cast: 3 for BF16 with both directions, else 4; cast with fused scales: 5 with both
+  // directions, else no cap (0)
   static constexpr int cast_cap(bool col, bool fuse) {
-    return fuse ? (sizeof(T) == 4 && col ? 4 : 0) : (sizeof(T) == 2 && col ? 3 : 4);
+    return fuse ? (col ? 5 : 0) : (sizeof(T) == 2 && col ? 3 : 4);
   }
 };
 constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-launch settings
@@ -1787,7 +1789,8 @@ hipError_t launch_quantize_bucket(const std::vector<TileArgs>& vec,
   hipError_t e = hipSuccess;
   if (!vec.empty())
     e = launch_grouped(quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
-                       quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1, 0, s);
+                       quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1,
+                       Occupancy<T>::kQuantCap, s);
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(quantize_elem_kernel<T, kCol, kPre>, quantize_elem_kernel<T, kCol, kPre>,
                        elem, kWavesPerGroup, 0, s);
