@@ -9,13 +9,15 @@
 // include/mxfp8_partial.h.
 //
 // Design (MI355X first; no matrix cores, since nothing here is a contraction):
-//  * A wave owns a tile of one 32-row band (the height of a column-wise block) and 64 * E
-//    columns, E = elements per 16-byte chunk (8 for BF16, 4 for FP32).  Each lane streams one
-//    16-byte chunk per row down the band, so every load instruction of the wave covers 1 KiB
-//    of contiguous HBM.  Column-wise maxima stay in the lane's registers for the whole band;
-//    row-wise maxima are reduced over the 32/E lanes that share a 32-value block with DPP
-//    (quad_perm, row_half_mirror), no LDS round trip.  One read of the input feeds both
-//    directions.
+//  * A workgroup owns a tile of one 32-row band (the height of a column-wise block) and 64 * E
+//    columns, E = elements per 16-byte chunk (8 for BF16, 4 for FP32); each of its four waves
+//    takes 8 of the rows.  Each lane streams one 16-byte chunk per row, so every load
+//    instruction of a wave covers 1 KiB of contiguous HBM.  Column-wise maxima stay in the
+//    lane's registers and meet over the four waves in LDS; row-wise maxima are reduced over the
+//    32/E lanes that share a 32-value block with DPP (quad_perm, row_half_mirror), no LDS round
+//    trip.  One read of the input feeds both directions.
+//  * A wave issues all of a tile's loads before it uses any value (one memory round trip per
+//    tile), and large launches hold a measured number of resident workgroups per CU.
 //  * amax is handled as unsigned integers on |x|'s bit pattern (exact, independent of the
 //    floating-point mode); BF16 pairs use v_pk_max_u16.
 //  * The cast scales with v_ldexp_f32 (exact, denormals preserved), saturates with v_med3_f32
