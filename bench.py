@@ -3,16 +3,17 @@
 One step is the whole path over a 16384x6144 master weight (BF16 by default) held as four
 contiguous fragments whose boundaries fall inside 32-value blocks (cuts at N/4+17, N/2+17,
 3N/4+17), as four ranks would hold it: zero-fill of one packed amax buffer per fragment,
-partial amax of every fragment, MAX-combine of the four buffers, then E8M0 scales and the
-in-place partial cast of every fragment to E4M3 row-wise and column-wise data: by default in
-one fused pass per fragment (mxfp8_scales_and_cast), with ``--separate-scales`` as the
-scales call over the whole weight followed by the cast call.  Inputs are resident in HBM before timing.  Steps walk over several distinct weights
+partial amax of every fragment, MAX-combine of the four buffers, then E8M0 scales (one call
+over the whole weight) and the in-place partial cast of every fragment to E4M3 row-wise and
+column-wise data, the four calls of the pages' design; ``--fused`` derives the scales inside
+the cast instead (mxfp8_scales_and_cast, one pass per fragment).  Inputs are resident in HBM
+before timing.  Steps walk over several distinct weights
 (buffer sets, >= 1.2 GB in all) like a writeback over a model: step i runs the amax side on
 weight i and the cast of weight i - 1, so no kernel reads an input another kernel has just
 left in the 256 MB Infinity Cache.
 
 Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
-``roofline`` is for the dominant kernel (the cast, fused with the scales by default), from
+``roofline`` is for the dominant kernel (the cast, or with ``--fused`` the fused one), from
 timing-only HIP events (no system-scope fence) recorded on the launch stream around the cast
 call of every fourth timed step;
 ``kernels`` is the per-call table (partial amax, partial cast and the fused scales + cast;
@@ -62,8 +63,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false")
     ap.add_argument("--cpu-rows", type=int, default=16384,
                     help="rows of the weight (a band-aligned sample) the oracle processes")
-    ap.add_argument("--separate-scales", dest="fused", action="store_false", default=True,
-                    help="run the scales and the cast as two calls instead of the fused call")
+    ap.add_argument("--fused", dest="fused", action="store_true", default=False,
+                    help="derive the scales inside the cast (one call) instead of the scales "
+                         "call followed by the cast call")
     ap.add_argument("--single-pass", dest="single_pass", action="store_true", default=True,
                     help="also time the writeback that quantizes whole bands in one pass")
     ap.add_argument("--no-single-pass", dest="single_pass", action="store_false")
@@ -283,7 +285,7 @@ def main():
     stage_ms = {name: statistics.median(e[j].elapsed_time(e[j + 1]) for e in evs)
                 for j, name in enumerate(stage_names)}
 
-    # dominant kernel: the cast (fused with the scales by default).  The library launches
+    # dominant kernel: the cast (with --fused, the fused one).  The library launches
     # the pieces of one call that share a kernel specialization together, up to 16 per
     # launch: here the 4 fragments of the weight (all on the vector path, checked above) go
     # out as one launch.
