@@ -1631,8 +1631,11 @@ int lds_per_cu() {
   int v = cache[dev].load(std::memory_order_relaxed);
   if (v == 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
-            hipSuccess || v <= 0)
+        hipSuccess) {
+      (void)hipGetLastError();  // a failed query only drops the cap; the launch check stays clean
       v = -1;
+    }
+    if (v <= 0) v = -1;
     cache[dev].store(v, std::memory_order_relaxed);
   }
   return v > 0 ? v : 0;
@@ -1652,7 +1655,12 @@ size_t cap_lds(K kernel, int cap) {
     auto it = static_lds.find(key);
     if (it == static_lds.end()) {
       hipFuncAttributes a{};
-      st = hipFuncGetAttributes(&a, key) == hipSuccess ? a.sharedSizeBytes : 0;
+      if (hipFuncGetAttributes(&a, key) == hipSuccess) {
+        st = a.sharedSizeBytes;
+      } else {
+        (void)hipGetLastError();  // as above
+        st = 0;
+      }
       static_lds.emplace(key, st);
     } else {
       st = it->second;
