@@ -155,7 +155,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build runs the writeback on a single MI355X "
+        print("bench.py measures one GPU: the writeback runs on a single MI355X "
               "(the cross-rank MAX all-reduce is replaced by an on-device combine); "
               f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported.", file=sys.stderr)
         sys.exit(2)
