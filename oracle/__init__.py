@@ -124,7 +124,9 @@ def e4m3_code(v: float) -> int:
 
 
 def partial_amax(x_frag, rows, cols, start, amax_row, amax_col=None, preround=False):
-    """MAX-accumulate the fragment's per-block |values| into amax_row (and amax_col)."""
+    """Per-block max |value| of the fragment into amax_row (and amax_col): blocks the fragment
+    holds whole are set, blocks a fragment boundary cuts are MAX-merged with their entry,
+    untouched entries keep their value."""
     dt = dtype_of(x_frag)
     for a in (amax_row, amax_col):
         if a is not None and a.dtype != amax_np_dtype(dt):

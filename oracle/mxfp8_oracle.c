@@ -160,18 +160,44 @@ static int working_value(const void* input, int64_t k, int dtype, int preround, 
 
 /* ---------------------------------------------------------------- the four steps */
 
+/* Is the whole block, from flat index `first` to flat index `last`, inside the fragment? */
+static int block_inside(int64_t first, int64_t last, int64_t start, int64_t len) {
+  return first >= start && last < start + len;
+}
+
 /* Step 1, partial amax.  Element k of the fragment is element i = start + k of the
  * row-major flattening, at row i / cols and column i % cols.  Its row-wise block is
- * (row, col / 32) and its column-wise block is (row / 32, col).  Every touched entry
- * becomes max(entry, |w|) over the fragment's elements in that block, so entries the
- * fragment does not touch keep their value and blocks cut by a fragment boundary are
- * merged, never overwritten.  amax_col == NULL means the column-wise direction is absent. */
+ * (row, col / 32) and its column-wise block is (row / 32, col).  The amax buffers are
+ * in/out (kernel documentation in the review threads):
+ *  - a block the fragment holds whole gets the max |w| over its elements: this fragment is
+ *    the only one that touches it, and its old entry is not part of the result;
+ *  - a block a fragment boundary cuts becomes max(entry, |w|) over the fragment's elements
+ *    in it, so the pieces of several fragments that share one buffer merge;
+ *  - entries the fragment does not touch keep their value.
+ * On a zero-filled buffer, which every update starts from, both kinds of block come out as
+ * max(entry, |w|).  amax_col == NULL means the column-wise direction is absent. */
 int mxo_partial_amax(int64_t rows, int64_t cols, int64_t start, int64_t len, int dtype,
                      int preround, const void* input, void* amax_row, int64_t ld_row,
                      void* amax_col, int64_t ld_col) {
   int st = check_piece(rows, cols, start, len, dtype, preround);
   if (st) return st;
   if (ld_row < ceil_div(cols, BLOCK) || (amax_col && ld_col < cols)) return MXO_ELAYOUT;
+  /* first pass: the entry of every block the fragment holds whole starts again from 0 */
+  for (int64_t k = 0; k < len; ++k) {
+    int64_t i = start + k, r = i / cols, c = i % cols;
+    int64_t j = c / BLOCK, b = r / BLOCK;
+    int64_t row_first = r * cols + j * BLOCK;
+    int64_t row_last = r * cols + (j * BLOCK + BLOCK < cols ? j * BLOCK + BLOCK : cols) - 1;
+    if (block_inside(row_first, row_last, start, len))
+      store_value(amax_row, r * ld_row + j, dtype, 0.0);
+    if (amax_col) {
+      int64_t col_first = b * BLOCK * cols + c;
+      int64_t col_last = ((b * BLOCK + BLOCK < rows ? b * BLOCK + BLOCK : rows) - 1) * cols + c;
+      if (block_inside(col_first, col_last, start, len))
+        store_value(amax_col, b * ld_col + c, dtype, 0.0);
+    }
+  }
+  /* second pass: every touched entry takes the max with |w| of each fragment element */
   for (int64_t k = 0; k < len; ++k) {
     int64_t i = start + k, r = i / cols, c = i % cols;
     double w;

@@ -356,6 +356,46 @@ def test_untouched_entries_keep_their_value_and_cut_blocks_merge():
     assert (b["amax_col"][1:] == 0.5).all()
 
 
+@pytest.mark.parametrize("rows,cols,dtype,frag", [
+    (96, 128, "bf16", (1000, 6000)),   # whole blocks in both directions, cuts inside blocks
+    (70, 45, "fp32", (17, 70 * 45 - 17)),  # to the end: short last row blocks, short last band
+    (64, 64, "fp32", (64 * 32, 64 * 32)),  # one whole band: every touched block is whole
+    (40, 96, "bf16", (5, 20)),         # inside one row block: nothing is whole
+])
+def test_whole_blocks_are_set_and_cut_blocks_merge(rows, cols, dtype, frag):
+    """Entries start at a sentinel above every |value|.  Blocks the fragment holds whole must
+    come out as the numpy block max of the fragment's values (a merge would keep the
+    sentinel); blocks a boundary cuts and untouched blocks must keep the sentinel (setting
+    them would lower it)."""
+    x = wl.random_matrix(rows, cols, dtype, seed=rows + cols, kind="mixed")
+    dt = oracle.dtype_of(x)
+    s, l = frag
+    nb, nr = oracle.nblocks(cols), oracle.nblocks(rows)
+    xv = amax_value(x, dt) if dtype == "bf16" else x.astype(np.float64)
+    inside = np.zeros(rows * cols, bool)
+    inside[s:s + l] = True
+    # padded to whole blocks: padding is "inside" for the whole-block test and 0 for the max
+    pad = ((0, nr * 32 - rows), (0, nb * 32 - cols))
+    held = np.pad(inside.reshape(rows, cols), pad, constant_values=True)
+    vals = np.pad(np.where(inside, np.abs(xv), 0.0).reshape(rows, cols), pad)
+    row_whole = held.reshape(nr * 32, nb, 32).all(axis=2)[:rows]
+    row_max = vals.reshape(nr * 32, nb, 32).max(axis=2)[:rows]
+    col_whole = held.reshape(nr, 32, nb * 32).all(axis=1)[:, :cols]
+    col_max = vals.reshape(nr, 32, nb * 32).max(axis=1)[:, :cols]
+    big = 2.0 ** 100
+    sent = np.float32(big) if dtype == "fp32" else wl.to_dtype(np.float32([big]), "bf16")[0]
+    ar = np.full((rows, nb), sent)
+    ac = np.full((nr, cols), sent)
+    oracle.partial_amax(x[s:s + l], rows, cols, s, ar, ac)
+    np.testing.assert_array_equal(amax_value(ar, dt), np.where(row_whole, row_max, big))
+    np.testing.assert_array_equal(amax_value(ac, dt), np.where(col_whole, col_max, big))
+    # the cases hold what they claim: whole blocks (except the last), cut blocks (except
+    # the band-aligned one)
+    assert row_whole.any() == (frag != (5, 20))
+    assert (~row_whole & np.pad(inside.reshape(rows, cols), pad).reshape(
+        nr * 32, nb, 32).any(axis=2)[:rows]).any() == (frag[0] % cols != 0)
+
+
 def test_config_fragments_equal_full():
     m = wl.matrix_rowonly_fragments()
     full = oracle.writeback(m.data, m.rows, m.cols, m.runs["full"], colwise=False)
