@@ -90,13 +90,17 @@ typedef struct {
 /* Step 1 -- partial amax (first step of the flow diagram; the kernel documentation in the
  * review threads marks both amax outputs as in/out).
  * For each of the n pieces (a host array) and every block the fragment touches in a present
- * direction: amax[block] = max(amax[block], max |w| over the fragment's elements in the
- * block), w being the input value (pre-rounded to BF16 if requested).  Blocks the fragment
- * does not touch keep their entry; blocks cut by a fragment boundary are MAX-merged, so
- * pieces of one weight may share amax buffers within a call or across calls, and zero-filled
- * buffers accumulate the amax of all pieces.  The column-wise direction is computed iff
- * amax_col.ptr != NULL.  Reads: rows, cols, start, len, in_dtype, preround_bf16, input,
- * amax_row (required), amax_col. */
+ * direction, with m = max |w| over the fragment's elements in the block, w being the input
+ * value (pre-rounded to BF16 if requested):
+ *  - a block the fragment holds whole: amax[block] = m (no other fragment touches it; the
+ *    old entry is not read);
+ *  - a block a fragment boundary cuts: amax[block] = max(amax[block], m);
+ *  - blocks the fragment does not touch keep their entry.
+ * So pieces of one weight whose fragments do not overlap may share amax buffers within a
+ * call or across calls, and a zero-filled buffer accumulates the amax of all pieces (on it
+ * the result is max(entry, m) for every touched block).  The column-wise direction is
+ * computed iff amax_col.ptr != NULL.  Reads: rows, cols, start, len, in_dtype,
+ * preround_bf16, input, amax_row (required), amax_col. */
 int mxfp8_partial_amax(const mxfp8_piece* pieces, int n, void* hip_stream);
 
 /* Step 2 -- MAX-combine (section Changes keeps a single MAX all-reduce over the packed amax;

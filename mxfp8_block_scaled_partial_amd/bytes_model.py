@@ -1,15 +1,17 @@
 """Algorithmic HBM bytes of each step, the numerator of the reported bandwidths.
 
 What the method must move, each item once: the fragment's input values, the amax entries it
-touches (read and written: amax buffers are in/out and MAX-merged), the scale bytes and the
-E4M3 outputs.  Re-reads, staging and padding are excluded, so bytes / time is a lower bound
-on the bandwidth the hardware actually delivered.
+touches (written; the entry of a block the fragment holds whole is set without being read),
+the scale bytes and the E4M3 outputs.  Re-reads, staging and padding are excluded, and so are
+the reads of the entries of blocks a fragment boundary cuts (their merge reads them back: at
+most 2 row-wise and cols column-wise blocks at each end of a fragment), so bytes / time is a
+lower bound on the bandwidth the hardware actually delivered.
 
 For a fragment [start, start + len) of a rows x cols weight, with s_in = input element bytes
 (2 BF16, 4 FP32; amax entries have the same width), D = present directions, and T_row /
 T_col the row-wise / column-wise blocks the fragment touches:
 
-  partial amax    len * s_in + 2 * (T_row + T_col) * s_in
+  partial amax    len * s_in + (T_row + T_col) * s_in
   compute scales  (T_row + T_col) * (s_in + 1)
   partial cast    len * s_in + (T_row + T_col) * 1 + len * D
   scales + cast   len * s_in + (T_row + T_col) * (s_in + 1) + len * D   (fused: amax entries
@@ -65,7 +67,7 @@ def piece_bytes(rows: int, cols: int, start: int, length: int, s_in: int, colwis
     tr = touched_row_blocks(rows, cols, start, length)
     tc = touched_col_blocks(rows, cols, start, length) if colwise else 0
     d = 2 if colwise else 1
-    return {"amax": length * s_in + 2 * (tr + tc) * s_in,
+    return {"amax": length * s_in + (tr + tc) * s_in,
             "scales": (tr + tc) * (s_in + 1),
             "cast": length * s_in + (tr + tc) + length * d,
             "scales_cast": length * s_in + (tr + tc) * (s_in + 1) + length * d,

@@ -26,9 +26,10 @@
 //    a row-only call carries no column-wise code (the runtime-guard version measured on the
 //    pages cost amax 21-35%).
 //  * Tiles wholly inside the fragment run branch-free; tiles the fragment boundary cuts take
-//    an element-masked path.  Amax entries of blocks wholly inside a piece are read-max-written
-//    by their single owner; blocks a boundary cuts use an atomic max, so pieces sharing one
-//    amax buffer merge correctly in any order.
+//    an element-masked path.  The amax entry of a block wholly inside a piece is written by
+//    its single owner without being read (no other fragment touches that block); blocks a
+//    boundary cuts use an atomic max, so pieces sharing one amax buffer merge correctly in
+//    any order.
 //  * Workgroup ids are remapped so consecutive tiles (one band's amax entries) land on the
 //    same XCD's L2.
 //  * Layouts the vector path cannot take (rows that are not whole 16-byte chunks: cols % 8 != 0
@@ -174,12 +175,6 @@ __device__ __forceinline__ int piece_of(const GroupArgs& g, int64_t t) {
 
 // ------------------------------------------------------------------ amax entries
 
-__device__ __forceinline__ void merge_plain(uint16_t* p, uint32_t v) {
-  const uint32_t old = *p;
-  *p = (uint16_t)umax(old, v);
-}
-__device__ __forceinline__ void merge_plain(uint32_t* p, uint32_t v) { *p = umax(*p, v); }
-
 // Atomic max into N amax entries at once; bit i of `active` selects entry i.  Amax values are
 // non-negative, so unsigned order on the bit patterns is float order.  FP32 entries use the
 // hardware's unsigned atomic max, which returns nothing to wait for.
@@ -229,11 +224,13 @@ __device__ __forceinline__ void atomic_max_entries(uint16_t* const (&p)[N],
   }
 }
 
+// The entry of a block: set when the piece holds the whole block (`whole`: its only writer),
+// else MAX-merged atomically (a neighbouring piece may share the block).
 template <typename T>
-__device__ __forceinline__ void merge_entry(void* base, int64_t idx, uint32_t v, bool full) {
+__device__ __forceinline__ void write_entry(void* base, int64_t idx, uint32_t v, bool whole) {
   T* p = static_cast<T*>(base) + idx;
-  if (full) {
-    merge_plain(p, v);
+  if (whole) {
+    *p = (T)v;
   } else {
     T* const ps[1] = {p};
     const uint32_t vs[1] = {v};
@@ -557,8 +554,9 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 
 // A workgroup owns one tile: a 32-row band x 64*E columns.  Wave w streams rows 8w .. 8w+7
 // with all eight 16-byte loads in flight; the four waves' column-wise maxima meet in LDS.
-// Tiles wholly inside the fragment read-max-write their entries (each has a single owner);
-// edge tiles merge every touched entry atomically, since a neighbouring piece may share it.
+// Tiles wholly inside the fragment write their entries without reading them (each block has
+// a single owner); edge tiles write the entries of blocks the piece holds whole and merge
+// those of cut blocks atomically, since a neighbouring piece may share them.
 template <typename T, bool kCol, bool kPre, int kOcc>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
@@ -602,27 +600,18 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
     if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
     // Entries of the tile: 32 rows x NBLK row-wise blocks (32 bytes per row) and 64*E
-    // column-wise blocks.  Their old values are fetched together with the input so that no
-    // memory latency remains after the reduction; wave 1 then writes the row-wise entries as
-    // one 16-byte vector per lane (row lane/2, half lane%2) while wave 0 merges the
-    // column-wise ones.  Tiles whose rows are not 16-byte aligned in amax_row, or that run
-    // past the last column, let every block's owner lanes write their entries one by one.
+    // column-wise blocks, all held whole by this piece, so they are written and never read.
+    // Wave 1 writes the row-wise entries as one 16-byte vector per lane (row lane/2, half
+    // lane%2) while wave 0 combines and writes the column-wise ones.  Tiles whose rows are not
+    // 16-byte aligned in amax_row, or that run past the last column, let every block's owner
+    // lanes write their entries one by one.
     constexpr int EPV = 16 / (int)sizeof(T);  // entries per 16-byte vector (NBLK = 2 * EPV)
     const bool rvec = p.row_vec && c0 + WC <= p.cols;  // uniform
     T* ar = static_cast<T*>(p.amax_row) + (r0 + i0 + lane % LB) * p.ld_ar + (c >> 5);
     T* arv = static_cast<T*>(p.amax_row) + (r0 + (lane >> 1)) * p.ld_ar + (c0 >> 5) +
              (lane & 1) * EPV;
     T* ac = static_cast<T*>(p.amax_col) + band * p.ld_ac + c;
-    uint32_t old[NK], keep[NK], orow[4] = {0, 0, 0, 0}, ocol[4] = {0, 0, 0, 0};
-    if (rvec) {
-      if (wave == 1) load16(arv, orow);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NK; ++k) old[k] = cvalid ? (uint32_t)ar[(int64_t)k * LB * p.ld_ar] : 0u;
-    }
-    if constexpr (kCol) {
-      if (wave == 0 && cvalid && p.col_vec) load16(ac, ocol);
-    }
+    uint32_t keep[NK];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       uint32_t m = chunk_absmax<T, kCol, kPre>(d[i], col);
@@ -635,7 +624,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     }
     if (!rvec && cvalid) {
 #pragma unroll
-      for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)umax(old[k], keep[k]);
+      for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)keep[k];
     }
     if constexpr (kCol) s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
     if (rvec || kCol) __syncthreads();
@@ -649,19 +638,17 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
         else
           v[j] = s_rmax[lane >> 1][(lane & 1) * EPV + j];
       }
-      fold_col<T>(orow, make_uint4(v[0], v[1], v[2], v[3]));
-      *reinterpret_cast<uint4*>(arv) = make_uint4(orow[0], orow[1], orow[2], orow[3]);
+      *reinterpret_cast<uint4*>(arv) = make_uint4(v[0], v[1], v[2], v[3]);
     }
     if constexpr (kCol) {
       if (wave == 0 && cvalid) {
 #pragma unroll
         for (int w = 1; w < kWavesPerGroup; ++w) fold_col<T>(col, s_col[w][lane]);
         if (p.col_vec) {
-          fold_col<T>(ocol, make_uint4(col[0], col[1], col[2], col[3]));
-          *reinterpret_cast<uint4*>(ac) = make_uint4(ocol[0], ocol[1], ocol[2], ocol[3]);
+          *reinterpret_cast<uint4*>(ac) = make_uint4(col[0], col[1], col[2], col[3]);
         } else {
 #pragma unroll
-          for (int e = 0; e < E; ++e) merge_plain(ac + e, col_entry<T>(col, e));
+          for (int e = 0; e < E; ++e) ac[e] = (T)col_entry<T>(col, e);
         }
       }
     }
@@ -670,9 +657,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
 
   // Edge tile: a fragment boundary, the short last band or a row's short last block cuts it.
   // Every wave loads its rows masked to the fragment; the row-wise and column-wise maxima meet
-  // in LDS and all 256 threads then merge the touched entries atomically, at most two of each
-  // kind per thread (all reads, then all swaps: faster than a plain read-max-write per entry
-  // even for blocks this tile owns alone).
+  // in LDS and all 256 threads then write the touched entries, at most two of each kind per
+  // thread: blocks the piece holds whole are stored, blocks a fragment boundary cuts are
+  // merged atomically (all reads, then all swaps).
   uint32_t em[RW];
   load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
@@ -694,11 +681,17 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       const int e = threadIdx.x + j * kThreads;
       const int row = e / NBLK, blk = e % NBLK;
       const int64_t r = r0 + row;
-      const int64_t gb = r * p.cols + c0 + blk * kBlockLen;
+      const int64_t bc = c0 + blk * kBlockLen;  // the block's first column
+      const int64_t gb = r * p.cols + bc;
+      const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
       ptr[j] = static_cast<T*>(p.amax_row) + r * p.ld_ar + (c0 >> 5) + blk;
       v[j] = s_rmax[row][blk];
-      if (row < nrows && c0 + blk * kBlockLen < p.cols && gb < p.end && gb + kBlockLen > p.start)
-        act |= 1u << j;
+      if (row < nrows && bc < p.cols && gb < p.end && ge > p.start) {
+        if (gb >= p.start && ge <= p.end)
+          *ptr[j] = (T)v[j];  // whole block: this tile is its only writer
+        else
+          act |= 1u << j;
+      }
     }
     atomic_max_entries<kPer>(ptr, v, act);
   }
@@ -720,7 +713,14 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       }
       ptr[j] = static_cast<T*>(p.amax_col) + band * p.ld_ac + c0 + cc;
       v[j] = m;
-      if (c0 + cc < p.cols && ((t >> e) & 1u)) act |= 1u << j;
+      // the block's first and last elements decide whether the piece holds it whole
+      const int64_t gf = r0 * p.cols + c0 + cc, gl = (r0 + nrows - 1) * p.cols + c0 + cc;
+      if (c0 + cc < p.cols && ((t >> e) & 1u)) {
+        if (gf >= p.start && gl < p.end)
+          *ptr[j] = (T)m;
+        else
+          act |= 1u << j;
+      }
     }
     atomic_max_entries<kPer>(ptr, v, act);
   }
@@ -1303,10 +1303,10 @@ __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
       rfull = (uint32_t)(inb >> 32) == (uint32_t)(valid >> 32);
     }
   }
-  if (rin) merge_entry<T>(p.amax_row, (r0 + (lane >> 1)) * p.ld_ar + (c0 >> 5) + (lane & 1), rv, rfull);
+  if (rin) write_entry<T>(p.amax_row, (r0 + (lane >> 1)) * p.ld_ar + (c0 >> 5) + (lane & 1), rv, rfull);
   if constexpr (kCol) {
     const uint32_t all = nrows == kBlockLen ? ~0u : (1u << nrows) - 1u;
-    if (in != 0) merge_entry<T>(p.amax_col, band * p.ld_ac + c0 + lane, cmax, in == all);
+    if (in != 0) write_entry<T>(p.amax_col, band * p.ld_ac + c0 + lane, cmax, in == all);
   }
 }
 

@@ -31,7 +31,7 @@ def test_bytes_per_element_at_full_size():
     n = rows * cols
     b = BM.piece_bytes(rows, cols, 0, n, 2, True)
     assert b["touched_row"] == n // 32 and b["touched_col"] == n // 32
-    assert b["amax"] / n == pytest.approx(2 + 2 * 2 * 2 / 32)
+    assert b["amax"] / n == pytest.approx(2 + 2 * 2 / 32)  # input, then 2 entries per 32
     assert b["cast"] / n == pytest.approx(2 + 2 / 32 + 2)
     # fused: each element's share of its two blocks' amax entries (2 bytes) and scales (1)
     assert b["scales_cast"] / n == pytest.approx(2 + 2 * (2 + 1) / 32 + 2)

@@ -1,9 +1,9 @@
 """GPU parity on edge cases and per-kernel contracts, byte for byte against the oracle:
-ragged shapes, short last bands, tiny fragments, padded leading dimensions, the MAX-merge
-into non-zero amax entries, every BF16 code at every scale byte through the cast, scales for
-every non-negative BF16 amax, K-way combines, omitted column-wise outputs, untouched bytes
-outside the fragment, consecutive updates with stable pointers, determinism, and many
-pieces of one weight merging in a single call."""
+ragged shapes, short last bands, tiny fragments, padded leading dimensions, amax entries
+over non-zero values (set for whole blocks, MAX-merged for cut blocks), every BF16 code at
+every scale byte through the cast, scales for every non-negative BF16 amax, K-way combines,
+omitted column-wise outputs, untouched bytes outside the fragment, consecutive updates with
+stable pointers, determinism, and many pieces of one weight merging in a single call."""
 import numpy as np
 import pytest
 import torch
@@ -172,24 +172,39 @@ def test_padded_leading_dimensions_and_padding_untouched(dtype):
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("inputs", ["views", "own"])
-def test_amax_merges_into_existing_entries(dtype, inputs):
-    rows, cols = 96, 128
+@pytest.mark.parametrize("cols,frag", [
+    (128, (1000, 6000)),               # vector path: interior tiles, cut bands, cut row blocks
+    (128, (32 * 128 + 17, 96 * 128 - 32 * 128 - 22)),  # edge tiles holding whole column blocks
+    (4104, (4104 * 32 + 5, 4104 * 40)),  # vector path, short last row block in every row
+    (99, (1000, 6000)),                # element-wise path
+    (99, (32 * 99 + 17, 96 * 99 - 32 * 99 - 22)),
+])
+def test_amax_sets_whole_blocks_and_merges_cut_blocks(dtype, inputs, cols, frag):
+    """Entries start at random non-negative values, often above the block maxima: blocks the
+    fragment holds whole must come out as their max, cut blocks as the max with the entry,
+    untouched blocks unchanged (the oracle's rule), on every amax kernel path."""
+    rows = 96
     x = wl.random_matrix(rows, cols, dtype, seed=9, kind="normal")
+    nb = B.nblocks(cols)
     g = np.random.Generator(np.random.PCG64(1))
-    init = np.abs(g.standard_normal((rows, 4)) * 1.5).astype(np.float32)
+    init = np.abs(g.standard_normal((rows, nb)) * 1.5).astype(np.float32)
     initc = np.abs(g.standard_normal((3, cols)) * 1.5).astype(np.float32)
     if dtype == "bf16":
-        init, initc = wl.to_dtype(init, "bf16").reshape(rows, 4), wl.to_dtype(initc, "bf16").reshape(3, cols)
-    s, l = 1000, 6000
-    ar, ac = to_dev(init.ravel()).view(rows, 4), to_dev(initc.ravel()).view(3, cols)
+        init, initc = wl.to_dtype(init, "bf16").reshape(rows, nb), wl.to_dtype(initc, "bf16").reshape(3, cols)
+    s, l = frag
+    ar, ac = to_dev(init.ravel()).view(rows, nb), to_dev(initc.ravel()).view(3, cols)
     xd = to_dev(x)
     xs = xd[s:s + l] if inputs == "views" else xd[s:s + l].clone()
-    B.mxfp8_partial_amax(B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac))
+    piece = B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac)
+    assert B.mxfp8_query_path(piece, 0) == (1 if cols % 8 == 0 else 0)
+    B.mxfp8_partial_amax(piece)
     torch.cuda.synchronize()
     war, wac = init.copy(), initc.copy()
     oracle.partial_amax(x[s:s + l], rows, cols, s, war, wac)
     assert not first_mismatch(bits(to_np(ar)), bits(war))
     assert not first_mismatch(bits(to_np(ac)), bits(wac))
+    # the case holds blocks of every kind in both directions
+    assert (bits(war) != bits(init)).any() and (bits(wac) != bits(initc)).any()
 
 
 def test_scales_for_every_nonnegative_bf16_amax():
