@@ -381,12 +381,45 @@ __device__ __forceinline__ void assemble_chunk(const RawChunk& r, bool shift2, u
 }
 
 // Chunks src + i * cols, i < n (n <= RW; the others stay as they are): all loads are issued
-// before any is assembled.
+// before any is assembled.  With shift2 and `whole_wave` (every lane of the wave is active and
+// the 64 lanes hold consecutive chunks of each row), the dword after a lane's 16 bytes is the
+// next lane's first dword: lanes take it from their neighbour with a DPP wave shift, and only
+// lane 63's, one uniform address per row (the dword its own shifted load would read), is
+// loaded, in place of a scattered extra dword load per lane and row.
 template <typename T, int RW>
 __device__ __forceinline__ void load_rows(const T* src, int64_t cols, bool shift2, int n,
-                                          uint32_t (&d)[RW][4]) {
+                                          uint32_t (&d)[RW][4], bool whole_wave) {
   RawChunk raw[RW];
-  if (shift2) {
+  if (shift2 && whole_wave) {
+    const uint64_t a = reinterpret_cast<uint64_t>(src);
+    const uint64_t a63 =
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), kWaveSize - 1) << 32) |
+        (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, kWaveSize - 1);
+    // lane 63's next dword (p + 14 for a chunk at p = 2 mod 4: dword-aligned).  The mask keeps
+    // the compiler from folding the 14 into the instruction offset of a scalar load, whose
+    // hardware drops the two low bits of the base address before adding the offset.
+    const uint8_t* t63 = reinterpret_cast<const uint8_t*>((a63 + 14) & ~uint64_t(3));
+    uint32_t tail[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (i < n) {
+        raw[i].v = __builtin_nontemporal_load(
+            reinterpret_cast<const v4u*>(reinterpret_cast<const uint8_t*>(src + i * cols) - 2));
+        tail[i] = *reinterpret_cast<const uint32_t*>(t63 + i * cols * (int64_t)sizeof(T));
+      }
+    }
+    const bool top = (threadIdx.x & (kWaveSize - 1)) == kWaveSize - 1;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (i < n) {
+        // wave_shl:1 (DPP control 0x130): lane l reads lane l + 1; lane 63 keeps `old`
+        const uint32_t next = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)raw[i].v.x, 0x130,
+                                                                    0xF, 0xF, false);
+        raw[i].t = top ? tail[i] : next;
+        assemble_chunk(raw[i], true, d[i]);
+      }
+    }
+  } else if (shift2) {
 #pragma unroll
     for (int i = 0; i < RW; ++i)
       if (i < n) issue_chunk(src + i * cols, true, raw[i]);
@@ -598,7 +631,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   if (interior) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
-    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, c0 + WC <= p.cols);
     // Entries of the tile: 32 rows x NBLK row-wise blocks (32 bytes per row) and 64*E
     // column-wise blocks, all held whole by this piece, so they are written and never read.
     // Wave 1 writes the row-wise entries as one 16-byte vector per lane (row lane/2, half
@@ -916,7 +949,7 @@ __device__ __forceinline__ void cast_tile_general(
       d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
       em[i] = cvalid ? kFull : 0u;
     }
-    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, c0 + WC <= p.cols);
   } else {
     load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
   }
@@ -1061,7 +1094,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     // (which the compiler cannot move a load past): the input rows, the row-wise amax entries
     // (fused) or scale bytes, then (not fused) the column-wise scale bytes.
     uint32_t cw[2] = {0, 0};
-    load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+    load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, c0 + WC <= p.cols);
     uint32_t rl[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i)
@@ -1158,9 +1191,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
   for (int i = 0; i < RW; ++i) d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
   if (cvalid) {
     if (nr >= RW)
-      load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d);
+      load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, c0 + WC <= p.cols);
     else
-      load_rows<T, RW>(src, p.cols, p.in_shift2, nr, d);
+      load_rows<T, RW>(src, p.cols, p.in_shift2, nr, d, c0 + WC <= p.cols);
   }
 
   // amax: rows absent from a short last band, and lanes past the last column, hold zeros

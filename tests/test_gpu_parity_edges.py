@@ -120,6 +120,25 @@ def test_vector_path_with_short_last_block(rows, cols, dtype):
                                 f"{frags} colwise={colwise} {inputs} shared={shared}: ")
 
 
+@pytest.mark.parametrize("cols", [1536, 1544])
+@pytest.mark.parametrize("mode", ["separate", "fused", "single_pass"])
+def test_bf16_shifted_input_whole_and_partial_wave_rows(cols, mode):
+    """BF16 fragments in allocations of their own, with input - start 2 bytes off a dword
+    boundary: rows of whole 64-lane chunk runs take the dword after each lane's 16 bytes from
+    the next lane (lane 63's from one load per row), a row's short last tile (1544 columns)
+    loads it per lane.  Fragments start at odd elements, inside and on band boundaries."""
+    rows = 100
+    x = wl.random_matrix(rows, cols, "bf16", seed=cols, kind="mixed")
+    n = rows * cols
+    frags = [(0, 33 * cols + 7), (33 * cols + 7, 31 * cols), (64 * cols + 7, n - 64 * cols - 7)]
+    assert all(s % 2 == 1 for s, _ in frags[1:])
+    want = oracle.writeback(x, rows, cols, frags, True)
+    for shared in (True, False):
+        got = run_matrix(x, rows, cols, frags, True, inputs="own", shared=shared,
+                         fused=mode == "fused", single_pass=mode == "single_pass")
+        assert_same(got, want, rows, cols, f"{mode} shared={shared}: ")
+
+
 # ------------------------------------------------------------------ padded leading dimensions
 
 
