@@ -99,6 +99,7 @@ struct TileArgs {
   int32_t row_vec;  // amax_row rows are 16-byte aligned: a tile's row entries move as vectors
   int32_t in_shift2;  // BF16 input with input - start at 2 mod 4 bytes: chunks need a 2-byte shift
   int32_t mo_row, mo_col;  // (data - start) mod 4 of each output: 0 = chunks store directly
+  int32_t nt_row, nt_col;  // each output row starts on a 64-byte boundary: streaming stores
   int32_t sc_vec;  // scale_col rows aligned to a chunk's E bytes: a lane's scale bytes are one load
 };
 
@@ -781,13 +782,42 @@ __device__ __forceinline__ void quantize_chunk(const uint32_t (&d)[4], const int
   }
 }
 
-// E output bytes of a chunk, streamed out with a non-temporal store (p 4-byte aligned).
+// E output bytes of a chunk at p (4-byte aligned).  Where every output row of the piece starts
+// on a 64-byte boundary (kNT), a wave's row of stores covers whole 64-byte pieces of its lines
+// and streams out with non-temporal stores.  Otherwise the ends of each row segment share
+// 64-byte pieces with the neighbouring workgroups' segments, and ordinary stores, which the L2
+// holds and merges, cost less: 16384x6144 outputs 4 bytes off a line took the FP32 cast 152 us
+// with streaming stores and 118 us with ordinary ones (102 us aligned; 112 us with streaming
+// stores 64 bytes off a line, 118 us with ordinary ones).
+// The two kinds must stay apart where a branch selects between them: merged into one store,
+// the streaming hint is dropped.  So the ordinary store sits between two empty asm statements,
+// compiler-only memory barriers that emit no instruction.
+template <int E, bool kNT>
+__device__ __forceinline__ void store_chunk(uint8_t* p, const uint32_t* q) {
+  if constexpr (kNT) {
+    if constexpr (E == 8)
+      __builtin_nontemporal_store(v2u{q[0], q[1]}, reinterpret_cast<v2u*>(p));
+    else
+      __builtin_nontemporal_store(q[0], reinterpret_cast<uint32_t*>(p));
+  } else {
+    asm volatile("" ::: "memory");
+    if constexpr (E == 8)
+      *reinterpret_cast<v2u*>(p) = v2u{q[0], q[1]};
+    else
+      *reinterpret_cast<uint32_t*>(p) = q[0];
+    asm volatile("" ::: "memory");
+  }
+}
+
+// The same with the choice made at run time, one chunk at a time: the general and edge tiles
+// of the cast.  The common cast tile takes only outputs whose rows start on lines and streams;
+// the single-pass quantize always streams.
 template <int E>
-__device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q) {
-  if constexpr (E == 8)
-    __builtin_nontemporal_store(v2u{q[0], q[1]}, reinterpret_cast<v2u*>(p));
+__device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q, bool nt) {
+  if (nt)
+    store_chunk<E, true>(p, q);
   else
-    __builtin_nontemporal_store(q[0], reinterpret_cast<uint32_t*>(p));
+    store_chunk<E, false>(p, q);
 }
 
 template <int E>
@@ -797,37 +827,84 @@ __device__ __forceinline__ void store_masked(uint8_t* p, const uint32_t* q, uint
     if ((mask >> e) & 1u) p[e] = (uint8_t)(q[e >> 2] >> ((e & 3) * 8));
 }
 
-// Chunk outputs at p, mo = p mod 4 != 0 (fragment-relative outputs not dword aligned).  Each
-// lane writes the dword-aligned window [p - mo, p - mo + E): the last mo bytes of the lane to
-// its left (same row, contiguous in memory) and its own first E - mo bytes.  The first lane of
-// a row segment writes its own first E - mo bytes one by one instead (the window's head belongs
-// to another workgroup), and the last lane adds its trailing mo bytes.  Every lane of the wave
-// must call this (it exchanges registers with __shfl_up).
+// Bytes [lo, hi) of the word w into the dword at the 4-byte-aligned address a, with at most
+// one byte store and one 2-byte store (lo == hi: nothing).  Used for the partial dwords at the
+// two ends of a row segment whose outputs are not dword aligned, where the dword's other
+// bytes belong to a neighbouring segment; every range that occurs is [mo, 4) or [0, mo).
+__device__ __forceinline__ void store_partial(uint8_t* a, uint32_t w, int lo, int hi) {
+  const int len = hi - lo;
+  if (len & 1) {
+    const int b = (lo & 1) ? lo : hi - 1;
+    a[b] = (uint8_t)(w >> (8 * b));
+  }
+  if (len >= 2) {
+    const int h = (lo & 1) ? lo + 1 : lo;
+    *reinterpret_cast<uint16_t*>(a + h) = (uint16_t)(w >> (8 * h));
+  }
+}
+
+// Chunk outputs at p, mo = p mod 4 != 0 (fragment-relative outputs not dword aligned); the
+// lanes of a row segment hold consecutive chunks, `first` the segment's first lane and `last`
+// its last.  Each lane writes the dword-aligned window [p - mo, p - mo + E): the last mo bytes
+// of the lane to its left and its own first E - mo bytes.  The first lane's window would start
+// with another segment's bytes: with E = 8 it writes [p - mo + 4, p - mo + 12) instead, its own
+// bytes there followed by the next lane's first 4 - mo (the same bytes that lane writes), so
+// one 8-byte store instruction serves every lane.  What is left are the partial dwords at the
+// segment's two ends, the first lane's leading 4 - mo bytes and the last lane's trailing mo
+// bytes, which share one byte and one 2-byte store instruction.  Neighbour words move by DPP
+// wave shifts, so every lane of the wave must call this.
 template <int E>
 __device__ __forceinline__ void store_window(uint8_t* p, const uint32_t* q, int mo, bool valid,
                                              bool first, bool last) {
   uint32_t prev[E / 4];
 #pragma unroll
-  for (int j = 0; j < E / 4; ++j) prev[j] = (uint32_t)__shfl_up((int)q[j], 1);
+  for (int j = 0; j < E / 4; ++j)  // wave_shr:1 (DPP 0x138): lane l reads lane l - 1
+    prev[j] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q[j], 0x138, 0xF, 0xF, false);
+  // wave_shl:1 (DPP 0x130): lane l reads lane l + 1
+  const uint32_t next0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)q[0], 0x130, 0xF, 0xF, false);
   if (!valid) return;
   const int sh = 8 * mo;
-  if (!first) {
-    uint32_t w[E / 4];
-    // window bytes = bytes [E - mo, 2E - mo) of prev || own, little-endian
-    if constexpr (E == 8) {
-      const uint64_t own = ((uint64_t)q[1] << 32) | q[0];
+  uint8_t* a = p - mo;  // dword aligned
+  uint32_t head, tail;  // the partial dwords' words: [mo, 4) of head at a, [0, mo) of tail
+  if constexpr (E == 8) {
+    const uint64_t own = ((uint64_t)q[1] << 32) | q[0];
+    if (!first) {
       const uint64_t pv = ((uint64_t)prev[1] << 32) | prev[0];
       const uint64_t win = (own << sh) | (pv >> (64 - sh));
-      w[0] = (uint32_t)win;
-      w[1] = (uint32_t)(win >> 32);
+      __builtin_nontemporal_store(v2u{(uint32_t)win, (uint32_t)(win >> 32)},
+                                  reinterpret_cast<v2u*>(a));
+    } else if (!last) {
+      const uint64_t win = (own >> (32 - sh)) | ((uint64_t)next0 << (32 + sh));
+      __builtin_nontemporal_store(v2u{(uint32_t)win, (uint32_t)(win >> 32)},
+                                  reinterpret_cast<v2u*>(a + 4));
     } else {
-      w[0] = (q[0] << sh) | (prev[0] >> (32 - sh));
+      __builtin_nontemporal_store((uint32_t)(own >> (32 - sh)),
+                                  reinterpret_cast<uint32_t*>(a + 4));
     }
-    store_bytes<E>(p - mo, w);
+    head = (uint32_t)(own << sh);
+    tail = (uint32_t)(own >> (64 - sh));
   } else {
-    store_masked<E>(p, q, (1u << (E - mo)) - 1);
+    if (!first)
+      __builtin_nontemporal_store((q[0] << sh) | (prev[0] >> (32 - sh)),
+                                  reinterpret_cast<uint32_t*>(a));
+    head = q[0] << sh;
+    tail = q[0] >> (32 - sh);
   }
-  if (last) store_masked<E>(p, q, ((1u << E) - 1) & ~((1u << (E - mo)) - 1));
+  // one byte and one 2-byte store instruction for the first lane's head and the last lane's
+  // tail; a lone lane that is both writes its tail after
+  int lo = 0, hi = 0;
+  uint8_t* pa = a;
+  uint32_t pw = head;
+  if (first) {
+    lo = mo;
+    hi = 4;
+  } else if (last) {
+    hi = mo;
+    pa = a + E;
+    pw = tail;
+  }
+  store_partial(pa, pw, lo, hi);
+  if (first && last) store_partial(a + E, tail, 0, mo);
 }
 
 // Fused scales: the E8M0 bytes of the lane's E column-wise blocks, from their amax entries.
@@ -999,7 +1076,7 @@ __device__ __forceinline__ void cast_tile_general(
       if (p.mo_row)
         store_window<E>(p.data_row + o0 + i * p.cols, q, p.mo_row, cvalid, first, last);
       else if (cvalid)
-        store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+        store_bytes<E>(p.data_row + o0 + i * p.cols, q, p.nt_row);
     }
     if constexpr (kCol) {
 #pragma unroll
@@ -1009,7 +1086,7 @@ __device__ __forceinline__ void cast_tile_general(
         if (p.mo_col)
           store_window<E>(p.data_col + o0 + i * p.cols, q, p.mo_col, cvalid, first, last);
         else if (cvalid)
-          store_bytes<E>(p.data_col + o0 + i * p.cols, q);
+          store_bytes<E>(p.data_col + o0 + i * p.cols, q, p.nt_col);
       }
     }
     return;
@@ -1022,13 +1099,13 @@ __device__ __forceinline__ void cast_tile_general(
     uint32_t q[E / 4];
     quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
     if (em[i] == kFull && p.mo_row == 0)
-      store_bytes<E>(p.data_row + o, q);
+      store_bytes<E>(p.data_row + o, q, p.nt_row);
     else
       store_masked<E>(p.data_row + o, q, em[i]);
     if constexpr (kCol) {
       quantize_chunk<T, kPre>(d[i], cshift, true, q);
       if (em[i] == kFull && p.mo_col == 0)
-        store_bytes<E>(p.data_col + o, q);
+        store_bytes<E>(p.data_col + o, q, p.nt_col);
       else
         store_masked<E>(p.data_col + o, q, em[i]);
     }
@@ -1081,9 +1158,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     }
   }
 
-  // the common tile: interior, dword-aligned outputs and (not fused) column-wise scale bytes
-  // that move as one vector; straight-line code
-  if (interior && p.mo_row == 0 && p.mo_col == 0 && (!kCol || kFuse || p.sc_vec)) {
+  // the common tile: interior, outputs whose rows start on 64-byte boundaries (streaming stores)
+  // and (not fused) column-wise scale bytes that move as one vector; straight-line code
+  if (interior && p.nt_row && (!kCol || p.nt_col) && (!kCol || kFuse || p.sc_vec)) {
     if (!cvalid) return;
     const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
     const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
@@ -1131,14 +1208,14 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     for (int i = 0; i < RW; ++i) {
       uint32_t q[E / 4];
       quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-      store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+      store_chunk<E, true>(p.data_row + o0 + i * p.cols, q);
     }
     if constexpr (kCol) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         uint32_t q[E / 4];
         quantize_chunk<T, kPre>(d[i], cshift, true, q);
-        store_bytes<E>(p.data_col + o0 + i * p.cols, q);
+        store_chunk<E, true>(p.data_col + o0 + i * p.cols, q);
       }
     }
     if constexpr (kFuse && kCol) {
@@ -1243,7 +1320,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
     if (p.mo_row)
       store_window<E>(p.data_row + o0 + i * p.cols, q, p.mo_row, valid, first, last);
     else if (valid)
-      store_bytes<E>(p.data_row + o0 + i * p.cols, q);
+      store_chunk<E, true>(p.data_row + o0 + i * p.cols, q);
   }
   if constexpr (kCol) {
 #pragma unroll
@@ -1254,7 +1331,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
       if (p.mo_col)
         store_window<E>(p.data_col + o0 + i * p.cols, q, p.mo_col, valid, first, last);
       else if (valid)
-        store_bytes<E>(p.data_col + o0 + i * p.cols, q);
+        store_chunk<E, true>(p.data_col + o0 + i * p.cols, q);
     }
   }
 
@@ -1650,6 +1727,12 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   };
   a.mo_row = mis(p.data_row);
   a.mo_col = mis(p.data_col);
+  auto lines = [&](const uint8_t* d) {
+    return (int32_t)(d && (reinterpret_cast<uintptr_t>(d) - (uintptr_t)p.start) % 64 == 0 &&
+                     p.cols % 64 == 0);
+  };
+  a.nt_row = lines(p.data_row);
+  a.nt_col = lines(p.data_col);
   const int64_t e = 16 / esz;  // elements per 16-byte chunk
   a.sc_vec = p.scale_col && (reinterpret_cast<uintptr_t>(p.scale_col) % e == 0) && (p.ld_sc % e == 0);
   return a;
