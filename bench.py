@@ -17,7 +17,9 @@ Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time 
 timing-only HIP events (no system-scope fence) recorded on the launch stream around the cast
 call of every fourth timed step;
 ``kernels`` is the per-call table (partial amax, partial cast and the fused scales + cast;
-full input and the quarter fragment at offset 17, BF16 and FP32); ``cpu_baseline`` times
+full input and the quarter fragment at offset 17, BF16 and FP32; at 16384x6144 also the quarter
+fragment in one rank's own buffers, ``*_partial_own``: input and fragment-sized outputs in
+allocations of their own); ``cpu_baseline`` times
 the oracle on the host over a band-aligned sample of the same workload.
 """
 from __future__ import annotations
@@ -526,8 +528,15 @@ def time_shape(args, m, dev):
     x0 = (torch.from_numpy(m.data.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
           else torch.from_numpy(m.data)).to(dev)
     out = {}
-    for run, (s, l) in (("full", (0, n)), ("partial", (17, n // 4))):
-        lead = s % 32                      # element offset that keeps input - s aligned
+    runs = [("full", (0, n)), ("partial", (17, n // 4))]
+    if (rows, cols) == (16384, 6144):
+        # one rank's own buffers: the quarter fragment's input and its fragment-sized E4M3
+        # outputs in allocations of their own, so input - 17 and data - 17 lose their alignment
+        # (BF16 input 2 bytes off a dword, outputs 1 byte off: shifted loads, window stores)
+        runs.append(("partial_own", (17, n // 4)))
+    for run, (s, l) in runs:
+        # element offset that keeps input - s (and data - s) aligned; 0 for a rank's own buffers
+        lead = 0 if run == "partial_own" else s % 32
         per_set = l * s_in + 2 * l + (rows * nb + nbands * cols) * (s_in + 1)
         n_sets = max(2, min(per_graph, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
         amax_p, cast_p, fused_p, keep = [], [], [], []
@@ -557,8 +566,9 @@ def time_shape(args, m, dev):
         # the amax runs first, so the fused call reads real amax entries; the single-pass
         # quantize needs whole bands, so it runs on the full input only
         kernels = [("amax", amax_p, B.mxfp8_partial_amax),
-                   ("cast", cast_p, B.mxfp8_partial_cast),
-                   ("scales_cast", fused_p, B.mxfp8_scales_and_cast)]
+                   ("cast", cast_p, B.mxfp8_partial_cast)]
+        if run != "partial_own":
+            kernels.append(("scales_cast", fused_p, B.mxfp8_scales_and_cast))
         if run == "full":
             kernels.append(("quantize", fused_p, B.mxfp8_quantize))
         for kname, pieces, fn in kernels:
