@@ -810,8 +810,8 @@ __device__ __forceinline__ void store_chunk(uint8_t* p, const uint32_t* q) {
 }
 
 // The same with the choice made at run time, one chunk at a time: the general and edge tiles
-// of the cast.  The common cast tile takes only outputs whose rows start on lines and streams;
-// the single-pass quantize always streams.
+// of the cast.  The common cast tile takes only outputs whose rows start on 64-byte boundaries
+// and streams; the single-pass quantize always streams.
 template <int E>
 __device__ __forceinline__ void store_bytes(uint8_t* p, const uint32_t* q, bool nt) {
   if (nt)
