@@ -139,6 +139,47 @@ def test_bf16_shifted_input_whole_and_partial_wave_rows(cols, mode):
         assert_same(got, want, rows, cols, f"{mode} shared={shared}: ")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("offset", [0, 4, 36, 5, 64 + 2])
+@pytest.mark.parametrize("fused", [False, True])
+def test_fragment_outputs_on_and_off_64_byte_boundaries(dtype, offset, fused):
+    """Fragment-sized outputs (fresh allocations) of fragments starting `offset` elements
+    past a band boundary, on a weight with several tiles per row: data - start sits on a
+    64-byte boundary (0: the common tile, streaming stores), off one but dword aligned (4, 36:
+    the general tile, ordinary stores) or off a dword (5, 66: window stores)."""
+    rows, cols = 96, 1536
+    x = wl.random_matrix(rows, cols, dtype, seed=offset + 11, kind="mixed")
+    n = rows * cols
+    s = 32 * cols + offset
+    l = 48 * cols - 2 * offset
+    tdt = torch_dtype(x)
+    xd = to_dev(x)
+    nb, nbands = cols // 32, rows // 32
+    ar = torch.zeros(rows, nb, dtype=tdt, device=DEV)
+    ac = torch.zeros(nbands, cols, dtype=tdt, device=DEV)
+    sr = torch.zeros(rows, nb, dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(nbands, cols, dtype=torch.uint8, device=DEV)
+    dr = torch.full((l,), 0xA5, dtype=torch.uint8, device=DEV)
+    dc = torch.full((l,), 0xA5, dtype=torch.uint8, device=DEV)
+    assert (dr.data_ptr() - s) % 64 == (-offset) % 64
+    xs = xd[s:s + l]
+    B.mxfp8_partial_amax(B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac))
+    if fused:
+        B.mxfp8_scales_and_cast(B.make_piece(rows, cols, s, xs, amax_row=ar, amax_col=ac,
+                                             scale_row=sr, scale_col=sc, data_row=dr,
+                                             data_col=dc))
+    else:
+        B.mxfp8_compute_scales(B.make_piece(rows, cols, s, None, length=l, in_dtype=tdt,
+                                            amax_row=ar, amax_col=ac, scale_row=sr,
+                                            scale_col=sc))
+        B.mxfp8_partial_cast(B.make_piece(rows, cols, s, xs, scale_row=sr, scale_col=sc,
+                                          data_row=dr, data_col=dc))
+    torch.cuda.synchronize()
+    want = oracle.writeback(x, rows, cols, [(s, l)], True)
+    assert not first_mismatch(to_np(dr), want["data_row"][s:s + l])
+    assert not first_mismatch(to_np(dc), want["data_col"][s:s + l])
+
+
 # ------------------------------------------------------------------ padded leading dimensions
 
 
