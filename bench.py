@@ -71,8 +71,10 @@ def parse():
     ap.add_argument("--single-pass", dest="single_pass", action="store_true", default=True,
                     help="also time the writeback that quantizes whole bands in one pass")
     ap.add_argument("--no-single-pass", dest="single_pass", action="store_false")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also time a plain device copy (the counter calibration kernel)")
+    ap.add_argument("--copy-probe", dest="copy_probe", action="store_true", default=True,
+                    help="also time a plain device copy (the achievable read + write ceiling, "
+                         "and the counter calibration kernel); on by default")
+    ap.add_argument("--no-copy-probe", dest="copy_probe", action="store_false")
     return ap.parse_args()
 
 
