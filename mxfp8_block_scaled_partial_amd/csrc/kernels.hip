@@ -79,6 +79,13 @@ struct Occupancy {
 };
 constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-launch settings
 
+// The runtime-guard ablation library (built with MXFP8_RUNTIME_GUARDS=1 by build.py
+// --ablation) runs the amax and the plain cast of rows of whole chunks through one kernel per
+// dtype for row-only and bidirectional calls, the column-wise work selected at run time by a
+// test of the column-wise pointer: the kernels the pages measured before the compile-time
+// specialization.  The product library (MXFP8_RUNTIME_GUARDS=0) never instantiates them.
+constexpr bool kRuntimeGuards = MXFP8_RUNTIME_GUARDS != 0;
+
 struct TileArgs {
   int64_t rows, cols, start, end;
   const void* input;
@@ -101,6 +108,7 @@ struct TileArgs {
   int32_t mo_row, mo_col;  // (data - start) mod 4 of each output: 0 = chunks store directly
   int32_t nt_row, nt_col;  // each output row starts on a 64-byte boundary: streaming stores
   int32_t sc_vec;  // scale_col rows aligned to a chunk's E bytes: a lane's scale bytes are one load
+  int32_t shift;   // line-owned cast tiles: flat offset of every tile column (0 elsewhere)
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
@@ -471,7 +479,8 @@ __device__ __forceinline__ void assemble_masked(const uint32_t (&el)[Chunk<T>::E
 // Rows i < nrows_here of an edge tile: chunk i of the wave's rows, masked to the fragment, in
 // d, with per-row element masks in em.  The whole chunks' loads go out first, then the element
 // loads of the chunks a fragment boundary cuts (a lane has at most two: the fragment's start
-// and end), and only then is anything assembled.
+// and end), and only then is anything assembled.  Chunks start at flat indices congruent to
+// p.shift modulo E (0 except in the line-owned cast tiles); c may then pass the row's end.
 template <typename T, int RW>
 __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
                                                  int nrows_here, int64_t c, bool cvalid,
@@ -496,12 +505,12 @@ __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src
   // Every lane issues every row's chunk load, rows without a whole chunk reading the
   // fragment's first whole chunk instead (discarded): a load under a per-lane condition would
   // make the compiler wait for it where the branches join.  That chunk starts at the first
-  // multiple of E at or after start (chunks start at multiples of E of the flat index, since
+  // chunk start at or after start (chunks start on one grid of the flat index, since
   // cols % E == 0), so its load touches only what a whole chunk's load touches; it is not
   // input itself, which with a 2-byte shift would read the 2 bytes before the fragment, in
   // another dword.  A fragment without a whole chunk loads nothing.
   RawChunk raw[RW];
-  const int64_t g_whole = (p.start + E - 1) / E * E;
+  const int64_t g_whole = p.start + ((((int64_t)p.shift - p.start) % E) + E) % E;
   if (g_whole + E <= p.end) {
     const T* whole = static_cast<const T*>(p.input) + (g_whole - p.start);
 #pragma unroll
@@ -591,7 +600,9 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // Tiles wholly inside the fragment write their entries without reading them (each block has
 // a single owner); edge tiles write the entries of blocks the piece holds whole and merge
 // those of cut blocks atomically, since a neighbouring piece may share them.
-template <typename T, bool kCol, bool kPre, int kOcc>
+// kGuard (the runtime-guard ablation library only, with kCol = true): one kernel for both
+// kinds of call, its column-wise work selected at run time by the column-wise pointer.
+template <typename T, bool kCol, bool kPre, int kOcc, bool kGuard = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -624,6 +635,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   // writes go through LDS: the interior path's per-lane writes assume whole blocks.
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end &&
                         (p.cols % kBlockLen == 0 || c0 + WC <= p.cols);
+  const bool colw = kCol && (!kGuard || p.amax_col != nullptr);  // column-wise entries
 
   uint32_t col[4] = {0, 0, 0, 0};
   uint32_t d[RW][4];
@@ -660,8 +672,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
 #pragma unroll
       for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)keep[k];
     }
-    if constexpr (kCol) s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
-    if (rvec || kCol) __syncthreads();
+    if (colw) s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    if (rvec || colw) __syncthreads();
     if (rvec && wave == 1) {
       uint32_t v[4];
 #pragma unroll
@@ -674,7 +686,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       }
       *reinterpret_cast<uint4*>(arv) = make_uint4(v[0], v[1], v[2], v[3]);
     }
-    if constexpr (kCol) {
+    if (colw) {
       if (wave == 0 && cvalid) {
 #pragma unroll
         for (int w = 1; w < kWavesPerGroup; ++w) fold_col<T>(col, s_col[w][lane]);
@@ -729,7 +741,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     }
     atomic_max_entries<kPer>(ptr, v, act);
   }
-  if constexpr (kCol) {
+  if (colw) {
     constexpr int kPer = WC / kThreads;  // columns per thread (2 or 1)
     T* ptr[kPer];
     uint32_t v[kPer], act = 0;
@@ -1005,7 +1017,7 @@ __device__ __forceinline__ void col_shifts(const TileArgs& p, int64_t band, int6
 template <typename T, bool kCol, bool kPre, bool kFuse>
 __device__ __forceinline__ void cast_tile_general(
     const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows, bool interior,
-    int (&cshift)[Chunk<T>::E]) {
+    int (&cshift)[Chunk<T>::E], bool colw) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
@@ -1062,7 +1074,7 @@ __device__ __forceinline__ void cast_tile_general(
       const uint32_t v = em[i] ? srow[i * p.ld_sr] : p.scale_row[r0 * p.ld_sr + (c0 >> 5)];
       sb[i] = em[i] ? v : 0u;
     }
-    if constexpr (kCol) {
+    if (colw) {
       if (cvalid) col_shifts<T>(p, band, c, cshift);
     }
 #pragma unroll
@@ -1078,7 +1090,7 @@ __device__ __forceinline__ void cast_tile_general(
       else if (cvalid)
         store_bytes<E>(p.data_row + o0 + i * p.cols, q, p.nt_row);
     }
-    if constexpr (kCol) {
+    if (colw) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         uint32_t q[E / 4];
@@ -1102,7 +1114,7 @@ __device__ __forceinline__ void cast_tile_general(
       store_bytes<E>(p.data_row + o, q, p.nt_row);
     else
       store_masked<E>(p.data_row + o, q, em[i]);
-    if constexpr (kCol) {
+    if (colw) {
       quantize_chunk<T, kPre>(d[i], cshift, true, q);
       if (em[i] == kFull && p.mo_col == 0)
         store_bytes<E>(p.data_col + o, q, p.nt_col);
@@ -1113,8 +1125,9 @@ __device__ __forceinline__ void cast_tile_general(
 }
 
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
-// with all loads in flight.
-template <typename T, bool kCol, bool kPre, bool kFuse, int kOcc>
+// with all loads in flight.  kGuard as for the amax (not fused): the column-wise work
+// follows a run-time test of data_col.
+template <typename T, bool kCol, bool kPre, bool kFuse, int kOcc, bool kGuard = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -1139,6 +1152,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+  static_assert(!(kGuard && kFuse), "the runtime-guard ablation covers the plain cast");
+  const bool colw = kCol && (!kGuard || p.data_col != nullptr);  // column-wise output
 
   // Column-wise shifts and (fused) scale bytes.  Fused: from the amax entries, here, before
   // the tile's loads (measured faster than with them); otherwise from the scale bytes, loaded
@@ -1160,7 +1175,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 
   // the common tile: interior, outputs whose rows start on 64-byte boundaries (streaming stores)
   // and (not fused) column-wise scale bytes that move as one vector; straight-line code
-  if (interior && p.nt_row && (!kCol || p.nt_col) && (!kCol || kFuse || p.sc_vec)) {
+  if (interior && p.nt_row && (!colw || p.nt_col) && (!colw || kFuse || p.sc_vec)) {
     if (!cvalid) return;
     const T* src = static_cast<const T*>(p.input) + ((r0 + i0) * p.cols + c - p.start);
     const uint8_t* srow = p.scale_row + (r0 + i0) * p.ld_sr + (c >> 5);
@@ -1176,7 +1191,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 #pragma unroll
     for (int i = 0; i < RW; ++i)
       rl[i] = kFuse ? row_amax<T>(p, r0 + i0 + i, c) : (uint32_t)srow[i * p.ld_sr];
-    if constexpr (kCol && !kFuse) {
+    if (colw && !kFuse) {
       if constexpr (E == 8) {
         const uint2 v = *reinterpret_cast<const uint2*>(p.scale_col + band * p.ld_sc + c);
         cw[0] = v.x;
@@ -1185,7 +1200,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
         cw[0] = *reinterpret_cast<const uint32_t*>(p.scale_col + band * p.ld_sc + c);
       }
     }
-    if constexpr (kCol && !kFuse) {
+    if (colw && !kFuse) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         csb[e] = (uint8_t)(cw[e >> 2] >> (8 * (e & 3)));
@@ -1210,7 +1225,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
       quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
       store_chunk<E, true>(p.data_row + o0 + i * p.cols, q);
     }
-    if constexpr (kCol) {
+    if (colw) {
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         uint32_t q[E / 4];
@@ -1223,9 +1238,177 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     }
     return;
   }
-  cast_tile_general<T, kCol, kPre, kFuse>(p, band, c0, c, i0, nrows, interior, cshift);
+  cast_tile_general<T, kCol, kPre, kFuse>(p, band, c0, c, i0, nrows, interior, cshift, colw);
   if constexpr (kFuse && kCol) {
     if (wave == 0 && cvalid) store_col_scales<T>(p, band, c, nrows, interior, csb);
+  }
+}
+
+// ------------------------------------------------------------------ partial cast, line-owned tiles
+
+// Fragment-sized outputs (each rank's E4M3 bytes in buffers of the fragment's own size) put
+// data - start at an arbitrary byte offset, so the standard tiles' output row segments begin
+// and end inside 128-byte lines that two workgroups write at different times.  These tiles
+// are laid out in output-address space instead.  With delta = (-(data_row - start)) mod 128
+// (kLineBytes) and cols a multiple of 128, tile (virtual band B, column tile j) covers, for
+// each virtual row v of [32 B, 32 B + 32), the contiguous flat range
+//   [v cols + delta + 64 E j,  v cols + delta + min(64 E (j + 1), cols)),
+// which starts on a line of the row-wise output.  A virtual row holds columns delta .. cols-1
+// of row v and then columns 0 .. delta-1 of row v + 1, so the tiles still cover every element
+// once, every workgroup writes whole lines of both outputs (the column-wise output has the
+// same offset), and the input is streamed exactly as in the standard tiles: a virtual row is
+// contiguous in memory.  The price is in the scale lookups: a lane's chunk can hold elements
+// of two row-wise blocks or of two rows, so its row-wise scale comes per element from two
+// scale bytes per row, and its column-wise scales from one or two byte windows of scale_col.
+// The n (1 <= n <= 4 W) bytes at any byte address a, little-endian in W dwords (bytes past n
+// are unspecified): the dwords that hold them, joined by byte funnel shifts.  Only dwords that
+// hold one of the n bytes are read.
+template <int W>
+__device__ __forceinline__ void load_window(const uint8_t* a, int n, uint32_t (&w)[W]) {
+  const uintptr_t ai = reinterpret_cast<uintptr_t>(a);
+  const uint32_t* d = reinterpret_cast<const uint32_t*>(ai & ~uintptr_t(3));
+  const int last = (int)(((ai + (uintptr_t)n - 1) >> 2) - (ai >> 2));  // last dword to read
+  const int sh = (int)(ai & 3);
+  uint32_t x[W + 1];
+#pragma unroll
+  for (int j = 0; j <= W; ++j) x[j] = d[j < last ? j : last];
+#pragma unroll
+  for (int j = 0; j < W; ++j) w[j] = __builtin_amdgcn_alignbyte(x[j + 1], x[j], sh);
+}
+
+// Column-wise scale bytes of a lane's E elements, packed little-endian: elements e < eC are
+// column cA + e of band bandA, the others (a chunk that runs past the row's end) column
+// e - eC of band bandB.  Issues its loads and uses them, so the caller calls it after the
+// tile's input loads.  Kept packed (E / 4 registers), the bytes become shifts at each use.
+template <int E>
+__device__ __forceinline__ uint64_t lines_col_scales(const TileArgs& p, int64_t bandA,
+                                                     int64_t bandB, int64_t cA, int eC) {
+  constexpr int W = E / 4;
+  uint32_t a[W], b[W];
+  load_window<W>(p.scale_col + bandA * p.ld_sc + cA, eC, a);
+  load_window<W>(p.scale_col + bandB * p.ld_sc, eC < E ? E - eC : 1, b);
+  uint64_t av = a[0], bv = b[0];
+  if constexpr (W == 2) {
+    av |= (uint64_t)a[1] << 32;
+    bv |= (uint64_t)b[1] << 32;
+  }
+  bv = eC < E ? bv << (8 * eC) : 0;  // byte e of bv: column e - eC of band bandB
+  const uint64_t lo = eC < 8 ? (uint64_t(1) << (8 * eC)) - 1 : ~uint64_t(0);  // bytes e < eC
+  return (av & lo) | (bv & ~lo);
+}
+
+// Exponent shifts from packed scale bytes.
+template <int E>
+__device__ __forceinline__ void unpack_shifts(uint64_t packed, int (&sh)[E]) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) sh[e] = 127 - (int)((packed >> (8 * e)) & 0xFFu);
+}
+
+template <typename T, bool kCol, bool kPre, int kOcc>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) {
+  constexpr int E = Chunk<T>::E;
+  constexpr int WC = kWaveSize * E;
+  constexpr int RW = kRowsPerWave;
+  constexpr uint32_t kFull = (1u << E) - 1;
+
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x >> 6;
+  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
+  const int k = piece_of(ga, gtile);
+  const TileArgs& p = ga.piece[k];
+  const int64_t tile = gtile - ga.first[k];
+  if (tile >= p.ntiles) return;  // uniform over the workgroup
+  const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
+  const int64_t vband = p.band0 + bq;  // virtual band; -1 holds row 0's first delta columns
+  const int64_t u0 = (int64_t)(t32 - bq * n32) * WC;
+  const bool cvalid = u0 + lane * E < p.cols;
+  const int64_t u = cvalid ? u0 + lane * E : 0;  // the lane's virtual column
+  const int64_t v0 = vband * kBlockLen;
+  const int i0 = wave * RW;
+  const int64_t cu = u + p.shift;
+  const int64_t tile_first = v0 * p.cols + p.shift + u0;
+  const int64_t tile_last = (v0 + kBlockLen - 1) * p.cols + p.shift + min<int64_t>(u0 + WC, p.cols) - 1;
+  const bool interior = tile_first >= p.start && tile_last < p.end;
+  const bool last_tc = u0 + WC >= p.cols;  // the column tile whose chunks reach the next row
+
+  // Where the lane's chunk lies, the same for every row: wholly in the next row (wrap), across
+  // the row's end (strad), or inside row v, where it may still cross a row-wise block boundary.
+  const bool wrap = cu >= p.cols;
+  const int64_t cA = wrap ? cu - p.cols : cu;  // real column of the chunk's first element
+  const bool strad = !wrap && cu + E > p.cols;
+  const int eC = strad ? (int)(p.cols - cA) : E;  // elements in the first element's row
+  const int eS = strad ? eC : min(E, kBlockLen - (int)(cA & (kBlockLen - 1)));  // ... and block
+  const int offA = wrap ? 1 : 0, offB = (wrap || strad) ? 1 : 0;  // rows after v
+  const int64_t kA = cA >> 5, kB = strad ? 0 : (cA + E - 1) >> 5;  // the two row-wise blocks
+  const int64_t last_row = p.rows - 1, last_band = (p.rows - 1) / kBlockLen;
+  auto clamp_row = [&](int64_t r) { return r < 0 ? 0 : (r > last_row ? last_row : r); };
+  auto clamp_band = [&](int64_t b) { return b < 0 ? 0 : (b > last_band ? last_band : b); };
+
+  const T* src = static_cast<const T*>(p.input) + ((v0 + i0) * p.cols + cu - p.start);
+  const int64_t o0 = (v0 + i0) * p.cols + cu - p.start;
+  uint32_t d[RW][4], em[RW];
+  if (interior) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
+      em[i] = cvalid ? kFull : 0u;
+    }
+    if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, u0 + WC <= p.cols);
+  } else {
+    load_rows_masked<T, RW>(p, src, v0 + i0, RW, cu, cvalid, d, em);
+  }
+  // the two row-wise scale bytes of every row (rows outside the weight read a clamped row;
+  // their elements are outside the fragment)
+  uint32_t sa[RW], sb[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    sa[i] = p.scale_row[clamp_row(v0 + i0 + i + offA) * p.ld_sr + kA];
+    sb[i] = p.scale_row[clamp_row(v0 + i0 + i + offB) * p.ld_sr + kB];
+  }
+  // column-wise scale bytes: every row of the tile uses band B, except the next-row elements
+  // of the last virtual row (wave 3, row 7), which belong to band B + 1
+  uint64_t csp = 0, csp7 = 0;
+  if constexpr (kCol) {
+    const int64_t bm = clamp_band(vband);
+    csp = lines_col_scales<E>(p, bm, bm, cA, eC);
+    csp7 = csp;
+    if (wave == kWavesPerGroup - 1 && last_tc)
+      csp7 = lines_col_scales<E>(p, clamp_band(vband + offA), clamp_band(vband + offB), cA, eC);
+  }
+
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if (!em[i]) continue;
+    int rs[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) rs[e] = 127 - (int)(e < eS ? sa[i] : sb[i]);
+    uint32_t q[E / 4];
+    quantize_chunk<T, kPre>(d[i], rs, true, q);
+    uint8_t* out = p.data_row + o0 + i * p.cols;
+    if (interior)
+      store_chunk<E, true>(out, q);
+    else if (em[i] == kFull)
+      store_chunk<E, false>(out, q);
+    else
+      store_masked<E>(out, q, em[i]);
+  }
+  if constexpr (kCol) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      if (!em[i]) continue;
+      int cs[E];
+      unpack_shifts<E>(i == RW - 1 ? csp7 : csp, cs);
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d[i], cs, true, q);
+      uint8_t* out = p.data_col + o0 + i * p.cols;
+      if (interior)
+        store_chunk<E, true>(out, q);
+      else if (em[i] == kFull)
+        store_chunk<E, false>(out, q);
+      else
+        store_masked<E>(out, q, em[i]);
+    }
   }
 }
 
@@ -1566,6 +1749,14 @@ struct ScaleArgs {
   int32_t row_vec, col_vec;  // rows of amax / scales aligned for 16-byte / 8-byte vectors
 };
 
+// One launch covers the scale items of up to kMaxGroup pieces (or parts of pieces) of one
+// dtype: workgroups first[k] .. first[k + 1] - 1 belong to part k.
+struct ScaleGroup {
+  ScaleArgs part[kMaxGroup];
+  uint32_t first[kMaxGroup + 1];
+  int32_t n;
+};
+
 
 // Whether column-wise block (b, c) holds an element of [start, end).
 __device__ __forceinline__ bool col_block_touched(const ScaleArgs& p, int64_t b, int64_t c) {
@@ -1614,8 +1805,11 @@ __device__ __forceinline__ void scale_segment(const T* a, uint8_t* s, int64_t x0
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void scales_kernel(ScaleArgs p) {
-  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+__global__ __launch_bounds__(256) void scales_kernel(ScaleGroup g) {
+  int k = 0;  // the part this workgroup serves (uniform: a scalar loop)
+  while (k + 1 < g.n && blockIdx.x >= g.first[k + 1]) ++k;
+  const ScaleArgs& p = g.part[k];
+  const uint32_t i = (blockIdx.x - g.first[k]) * 256u + threadIdx.x;
   if (i < p.items_row_total) {
     const uint32_t rr = i / p.items_row;
     const int64_t r = p.r_lo + rr;
@@ -1738,6 +1932,24 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
   return a;
 }
 
+inline int64_t floor_div(int64_t a, int64_t b) { return a >= 0 ? a / b : -((-a + b - 1) / b); }
+
+// Tile arguments of the line-owned cast tiles (see cast_lines_kernel): virtual rows
+// v = floor((g - shift) / cols) from the fragment's first to its last element, in bands of 32.
+TileArgs tile_args_lines(const Piece& p, int64_t tile_cols, int64_t shift) {
+  TileArgs a = tile_args(p, tile_cols);
+  const int64_t end = p.start + p.len;
+  const int64_t b0 = floor_div(floor_div(p.start - shift, p.cols), kBlockLen);
+  const int64_t b1 = floor_div(floor_div(end - 1 - shift, p.cols), kBlockLen);
+  a.shift = (int32_t)shift;
+  a.band0 = b0;
+  a.ntiles = (b1 - b0 + 1) * a.ntc;
+  const int64_t esz = elem_size(p.dtype);
+  const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
+  a.in_shift2 = ((virt + (uintptr_t)(shift * esz)) % 4) == 2;
+  return a;
+}
+
 // LDS bytes per CU of the current device (160 KiB on MI355X), queried once per device; 0 if
 // unknown.
 int lds_per_cu() {
@@ -1820,19 +2032,19 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
   return hipSuccess;
 }
 
-// The vector kernels take any fragment of a weight whose rows are whole 16-byte chunks (cols a
-// multiple of 8 for BF16, of 4 for FP32): a chunk then never crosses a block boundary or a row
-// end, every row has the same alignment, and a row's short last block (cols % 32 != 0) is a
-// whole number of chunks.  The input needs only its element alignment (dword loads, plus a
-// 2-byte shift for BF16 at 2 mod 4), and outputs at any byte offset are written through
-// aligned windows.
-bool vec_common_ok(const Piece& p) { return p.cols % (16 / elem_size(p.dtype)) == 0; }
 
 // Pieces of one call, bucketed by kernel specialization: dtype x column-wise x pre-round x
 // vector path.
 struct Buckets {
   std::vector<TileArgs> b[2][2][2][2];  // [bf16][col][pre][vec]
 };
+
+// The vector-path pieces of both directions, for one kernel with run-time guards.
+inline std::vector<TileArgs> both_directions(const Buckets& bk, int bf16, int pre) {
+  std::vector<TileArgs> v = bk.b[bf16][1][pre][1];
+  v.insert(v.end(), bk.b[bf16][0][pre][1].begin(), bk.b[bf16][0][pre][1].end());
+  return v;
+}
 
 template <typename T, bool kCol, bool kPre>
 hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
@@ -1862,33 +2074,103 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
   return e;
 }
 
+template <typename T, bool kCol, bool kPre>
+hipError_t launch_lines_bucket(const std::vector<TileArgs>& ps, hipStream_t s) {
+  if (ps.empty()) return hipSuccess;
+  return launch_grouped(cast_lines_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
+                        cast_lines_kernel<T, kCol, kPre, Occupancy<T>::kCast>, ps, 1,
+                        Occupancy<T>::cast_cap(kCol, false), s);
+}
+
+template <typename T, bool kPre>
+hipError_t launch_cast_guarded(const Buckets& bk, hipStream_t s) {
+  const int bf16 = sizeof(T) == 2, pre = kPre;
+  const std::vector<TileArgs> v = both_directions(bk, bf16, pre);
+  hipError_t e = hipSuccess;
+  if (!v.empty())
+    e = launch_grouped(cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true>,
+                       cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true>, v, 1,
+                       Occupancy<T>::cast_cap(true, false), s);
+  const std::vector<TileArgs> none;
+  if (e == hipSuccess) e = launch_cast_bucket<T, true, kPre, false>(none, bk.b[bf16][1][pre][0], s);
+  if (e == hipSuccess) e = launch_cast_bucket<T, false, kPre, false>(none, bk.b[bf16][0][pre][0], s);
+  return e;
+}
+
 template <bool kFuse>
 hipError_t launch_cast_pieces(const Piece* ps, int n, hipStream_t s) {
-  Buckets bk;
+  Buckets bk, lines;  // lines: pieces of the plain cast that take the line-owned tiles
   for (int i = 0; i < n; ++i) {
     const Piece& p = ps[i];
     const bool vec = vec_common_ok(p);
     const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
-    bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
+    const int64_t shift = kFuse ? 0 : line_shift(p);
+    if (shift)
+      lines.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][1].push_back(
+          tile_args_lines(p, width, shift));
+    else
+      bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
   }
-  hipError_t e = hipSuccess;
-  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  run(launch_cast_bucket<uint16_t, true, false, kFuse>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
-  run(launch_cast_bucket<uint16_t, false, false, kFuse>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
-  run(launch_cast_bucket<uint32_t, true, false, kFuse>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
-  run(launch_cast_bucket<uint32_t, false, false, kFuse>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
-  run(launch_cast_bucket<uint32_t, true, true, kFuse>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
-  run(launch_cast_bucket<uint32_t, false, true, kFuse>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
+  hipError_t e = hipSuccess;  // each launch only if everything before it went out
+  if constexpr (kRuntimeGuards && !kFuse) {
+    if (e == hipSuccess) e = launch_cast_guarded<uint16_t, false>(bk, s);
+    if (e == hipSuccess) e = launch_cast_guarded<uint32_t, false>(bk, s);
+    if (e == hipSuccess) e = launch_cast_guarded<uint32_t, true>(bk, s);
+  } else {
+    if (e == hipSuccess) e = launch_cast_bucket<uint16_t, true, false, kFuse>(bk.b[1][1][0][1], bk.b[1][1][0][0], s);
+    if (e == hipSuccess) e = launch_cast_bucket<uint16_t, false, false, kFuse>(bk.b[1][0][0][1], bk.b[1][0][0][0], s);
+    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, true, false, kFuse>(bk.b[0][1][0][1], bk.b[0][1][0][0], s);
+    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, false, false, kFuse>(bk.b[0][0][0][1], bk.b[0][0][0][0], s);
+    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, true, true, kFuse>(bk.b[0][1][1][1], bk.b[0][1][1][0], s);
+    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, false, true, kFuse>(bk.b[0][0][1][1], bk.b[0][0][1][0], s);
+  }
+  if constexpr (!kFuse) {
+    if (e == hipSuccess) e = launch_lines_bucket<uint16_t, true, false>(lines.b[1][1][0][1], s);
+    if (e == hipSuccess) e = launch_lines_bucket<uint16_t, false, false>(lines.b[1][0][0][1], s);
+    if (e == hipSuccess) e = launch_lines_bucket<uint32_t, true, false>(lines.b[0][1][0][1], s);
+    if (e == hipSuccess) e = launch_lines_bucket<uint32_t, false, false>(lines.b[0][0][0][1], s);
+    if (e == hipSuccess) e = launch_lines_bucket<uint32_t, true, true>(lines.b[0][1][1][1], s);
+    if (e == hipSuccess) e = launch_lines_bucket<uint32_t, false, true>(lines.b[0][0][1][1], s);
+  }
   return e;
 }
 
 }  // namespace
 
-bool amax_fast_ok(const Piece& p) { return vec_common_ok(p); }
+template <typename T, bool kPre>
+hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
+  const int bf16 = sizeof(T) == 2, pre = kPre;
+  const std::vector<TileArgs> v = both_directions(bk, bf16, pre);
+  hipError_t e = hipSuccess;
+  if (!v.empty())
+    e = launch_grouped(amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmax, true>,
+                       amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true>, v, 1,
+                       Occupancy<T>::kAmaxCap, s);
+  // the element-wise kernels keep their compile-time specializations
+  const std::vector<TileArgs> none;
+  if (e == hipSuccess) e = launch_amax_bucket<T, true, kPre>(none, bk.b[bf16][1][pre][0], s);
+  if (e == hipSuccess) e = launch_amax_bucket<T, false, kPre>(none, bk.b[bf16][0][pre][0], s);
+  return e;
+}
 
-bool cast_fast_ok(const Piece& p) { return vec_common_ok(p); }
-
-hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s);
+template <bool kGuards>
+hipError_t launch_amax_buckets(const Buckets& bk, hipStream_t s) {
+  hipError_t e = hipSuccess;  // each launch only if everything before it went out
+  if constexpr (kGuards) {
+    if (e == hipSuccess) e = launch_amax_guarded<uint16_t, false>(bk, s);
+    if (e == hipSuccess) e = launch_amax_guarded<uint32_t, false>(bk, s);
+    if (e == hipSuccess) e = launch_amax_guarded<uint32_t, true>(bk, s);
+    return e;
+  } else {
+    if (e == hipSuccess) e = launch_amax_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s);
+    if (e == hipSuccess) e = launch_amax_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s);
+    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s);
+    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s);
+    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s);
+    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s);
+    return e;
+  }
+}
 
 hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
   Buckets bk;
@@ -1898,15 +2180,7 @@ hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
     const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
     bk.b[p.dtype == kBF16][p.amax_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
   }
-  hipError_t e = hipSuccess;
-  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  run(launch_amax_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
-  run(launch_amax_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
-  run(launch_amax_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
-  run(launch_amax_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
-  run(launch_amax_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
-  run(launch_amax_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
-  return e;
+  return launch_amax_buckets<kRuntimeGuards>(bk, s);
 }
 
 template <typename T, bool kCol, bool kPre>
@@ -1931,14 +2205,13 @@ hipError_t launch_quantize(const Piece* ps, int n, hipStream_t s) {
     const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
     bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
   }
-  hipError_t e = hipSuccess;
-  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  run(launch_quantize_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s));
-  run(launch_quantize_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s));
-  run(launch_quantize_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s));
-  run(launch_quantize_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s));
-  run(launch_quantize_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s));
-  run(launch_quantize_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s));
+  hipError_t e = hipSuccess;  // each launch only if everything before it went out
+  if (e == hipSuccess) e = launch_quantize_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s);
+  if (e == hipSuccess) e = launch_quantize_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s);
+  if (e == hipSuccess) e = launch_quantize_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s);
+  if (e == hipSuccess) e = launch_quantize_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s);
+  if (e == hipSuccess) e = launch_quantize_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s);
+  if (e == hipSuccess) e = launch_quantize_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s);
   return e;
 }
 
@@ -1950,19 +2223,13 @@ hipError_t launch_scales_and_cast(const Piece* ps, int n, hipStream_t s) {
   return launch_cast_pieces<true>(ps, n, s);
 }
 
-hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {
-  for (int i = 0; i < n; ++i) {
-    const hipError_t e = launch_compute_scales_one(ps[i], s);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-// Items (threads) per scales launch beyond which a fragment's scales go out as several
-// launches of whole rows or bands, well below the 2^32 work-items a dispatch holds.
+// Items (threads) per part of a scales launch beyond which a fragment's scales are split into
+// parts of whole rows, then whole bands, well below the 2^32 work-items a dispatch holds.
 constexpr int64_t kMaxScaleItems = int64_t(1) << 24;
 
-hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
+// The scale parts of one piece: usually one; larger fragments are split into parts of whole
+// rows and of whole bands, each within kMaxScaleItems.
+hipError_t scale_parts(const Piece& p, std::vector<ScaleArgs>& out) {
   ScaleArgs a{};
   a.rows = p.rows;
   a.cols = p.cols;
@@ -1985,7 +2252,7 @@ hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
   const int64_t nb = cdiv(p.cols, kBlockLen);
   const int64_t items_row = cdiv(nb, 8), items_col = cdiv(p.cols, 8);
   const int64_t nrows = a.r_last - a.r_first + 1, nbands = a.b_last - a.b_first + 1;
-  // a launch holds at least one whole row or band: at most 2^31 items (2^31 work-items)
+  // a part holds at least one whole row or band: at most 2^31 items
   constexpr int64_t kMaxRowItems = int64_t(1) << 31;
   if (items_row > kMaxRowItems || (col && items_col > kMaxRowItems))
     return hipErrorInvalidConfiguration;
@@ -1996,31 +2263,58 @@ hipError_t launch_compute_scales_one(const Piece& p, hipStream_t s) {
               p.ld_sr % 8 == 0;
   a.col_vec = col && aligned(p.amax_col, 16) && (p.ld_ac * esz) % 16 == 0 &&
               aligned(p.scale_col, 8) && p.ld_sc % 8 == 0;
-  auto launch = [&](int64_t r_lo, int64_t nr, int64_t b_lo, int64_t nbd) {
+  auto part = [&](int64_t r_lo, int64_t nr, int64_t b_lo, int64_t nbd) {
     a.r_lo = r_lo;
     a.b_lo = b_lo;
     a.items_row_total = (uint32_t)(nr * items_row);
     a.items_col_total = (uint32_t)(nbd * items_col);
-    const dim3 grid((unsigned)cdiv(nr * items_row + nbd * items_col, 256));
-    if (p.dtype == kBF16)
-      hipLaunchKernelGGL(scales_kernel<uint16_t>, grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(scales_kernel<uint32_t>, grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+    out.push_back(a);
   };
   const int64_t ncol = col ? nbands : 0;
-  if (nrows * items_row + ncol * items_col <= kMaxScaleItems)  // the usual case: one launch
-    return launch(a.r_first, nrows, a.b_first, ncol);
-  // larger fragments: launches of whole rows, then of whole bands, each within the item limit
+  if (nrows * items_row + ncol * items_col <= kMaxScaleItems) {  // the usual case: one part
+    part(a.r_first, nrows, a.b_first, ncol);
+    return hipSuccess;
+  }
   const int64_t rows_per = std::max<int64_t>(1, kMaxScaleItems / items_row);
-  for (int64_t r = a.r_first; r <= a.r_last; r += rows_per) {
-    const hipError_t e = launch(r, std::min(rows_per, a.r_last - r + 1), 0, 0);
+  for (int64_t r = a.r_first; r <= a.r_last; r += rows_per)
+    part(r, std::min(rows_per, a.r_last - r + 1), 0, 0);
+  const int64_t bands_per = std::max<int64_t>(1, kMaxScaleItems / items_col);
+  for (int64_t b = a.b_first; col && b <= a.b_last; b += bands_per)
+    part(0, 0, b, std::min(bands_per, a.b_last - b + 1));
+  return hipSuccess;
+}
+
+// The scales of every piece of a call: one launch per dtype for up to kMaxGroup parts.
+hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {
+  std::vector<ScaleArgs> parts[2];  // [bf16]
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = scale_parts(ps[i], parts[ps[i].dtype == kBF16]);
     if (e != hipSuccess) return e;
   }
-  const int64_t bands_per = std::max<int64_t>(1, kMaxScaleItems / items_col);
-  for (int64_t b = a.b_first; col && b <= a.b_last; b += bands_per) {
-    const hipError_t e = launch(0, 0, b, std::min(bands_per, a.b_last - b + 1));
-    if (e != hipSuccess) return e;
+  // a launch stays within 2^23 workgroups (2^31 work-items); one part alone is at most 2^31
+  // items (a single row or band of the widest weights), so it always fits
+  constexpr int64_t kMaxScaleLaunchGroups = int64_t(1) << 23;
+  for (int bf16 = 1; bf16 >= 0; --bf16) {
+    const std::vector<ScaleArgs>& v = parts[bf16];
+    for (size_t i0 = 0; i0 < v.size();) {
+      ScaleGroup g{};
+      int64_t wg = 0;
+      while (g.n < kMaxGroup && i0 < v.size()) {
+        const int64_t w = cdiv((int64_t)v[i0].items_row_total + v[i0].items_col_total, 256);
+        if (g.n > 0 && wg + w > kMaxScaleLaunchGroups) break;
+        g.part[g.n] = v[i0++];
+        g.first[g.n++] = (uint32_t)wg;
+        wg += w;
+      }
+      g.first[g.n] = (uint32_t)wg;
+      if (wg == 0) continue;
+      if (bf16)
+        hipLaunchKernelGGL(scales_kernel<uint16_t>, dim3(wg), dim3(256), 0, s, g);
+      else
+        hipLaunchKernelGGL(scales_kernel<uint32_t>, dim3(wg), dim3(256), 0, s, g);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }

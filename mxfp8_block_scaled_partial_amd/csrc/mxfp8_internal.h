@@ -2,7 +2,7 @@
 // (kernels.hip).  Not installed; the public interface is include/mxfp8_partial.h.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace mxfp8 {
@@ -29,9 +29,18 @@ struct Piece {
 
 inline int64_t elem_size(int dtype) { return dtype == kBF16 ? 2 : 4; }
 
+// Kernel-path selection (host only; paths.cpp).
+constexpr int kLineBytes = 128;  // the output lines the cast's line-owned tiles start on
+// The vector kernels take any fragment of a weight whose rows are whole 16-byte chunks.
+bool vec_common_ok(const Piece& p);
+// Offset of the line-owned cast tiles (1 .. kLineBytes - 1 elements), or 0 for the standard
+// tiles.
+int64_t line_shift(const Piece& p);
 // Whether the vectorized kernels apply (see mxfp8_query_path in the public header).
 bool amax_fast_ok(const Piece& p);
 bool cast_fast_ok(const Piece& p);
+// Whether the plain cast takes the line-owned tiles.
+bool cast_lines_ok(const Piece& p);
 
 // Pieces sharing a kernel specialization go out in as few launches as possible.
 hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s);
