@@ -33,8 +33,12 @@
  *    fragment-sized output buffer passes its own pointer.
  *  - Errors: every check runs on the host before anything is enqueued; a call returns a
  *    status code and never aborts or throws.  mxfp8_last_error() gives a message for the
- *    calling thread's last non-OK status.  A HIP launch failure returns MXFP8_ERR_HIP; pieces
- *    enqueued before the failing one stay enqueued.
+ *    calling thread's last non-OK status.  A HIP launch failure returns MXFP8_ERR_HIP: the
+ *    launches issued before the failing one stay enqueued, and no launch follows it.
+ *  - Across the pieces of one call, a buffer that one piece writes must not overlap any
+ *    buffer of another piece (MXFP8_ERR_LAYOUT), except that pieces may share an amax or
+ *    scale array: the same pointer, leading dimension and shape in the same role, which is
+ *    how the pieces of one weight merge the blocks their fragments cut.
  *  - len == 0 (an empty master shard on a participating rank) is a valid no-op; input and
  *    outputs may then be NULL.
  *  - Precondition, not checked (device data): inputs are finite, and pre-rounding (below)
@@ -165,12 +169,23 @@ int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream);
 /* Message for the calling thread's last non-OK status (static storage, thread-local). */
 const char* mxfp8_last_error(void);
 
+/* Validates a whole call of entry point kernel = 0 (mxfp8_partial_amax), 1
+ * (mxfp8_partial_cast), 2 (mxfp8_scales_and_cast), 3 (mxfp8_quantize) or 4
+ * (mxfp8_compute_scales) exactly as that entry point does, every piece and the pieces
+ * against each other, and returns the status it would return before launching anything
+ * (MXFP8_OK if it would launch).  Host-only; launches nothing.  For callers that validate a
+ * fixed plan once and replay it. */
+int mxfp8_check_call(const mxfp8_piece* pieces, int n, int kernel);
+
 /* Which kernel variant a piece would use for kernel 0 = partial amax, 1 = partial cast,
  * 2 = scales and cast, 3 = quantize (each validated as for its entry point):
  * 1 = the vectorized path (16-byte loads of row segments, for rows of whole 16-byte chunks:
  * cols % 8 == 0 for BF16, cols % 4 == 0 for FP32, whatever the alignment of input and
- * outputs), 0 = the element-wise path (other cols), negative = the piece fails validation
- * (the status code, negated).
+ * outputs), 2 (partial cast only) = the vectorized path in tiles that own whole 128-byte
+ * lines of the outputs, taken when the outputs' rows do not start on a 128-byte line (such
+ * as fragment-sized outputs) while cols is a multiple of 128 and both outputs share their
+ * offset within a line, 0 = the element-wise path (other cols), negative = the piece fails
+ * validation (the status code, negated).
  * Host-only; launches nothing.  For a BF16 input 2 bytes past a 4-byte boundary the
  * vectorized path reads, never writes, the 2 bytes that share a 4-byte word with the first
  * and with the last input element, and ignores them; no kernel reads anything else outside

@@ -14,7 +14,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmxfp8partial.so")
+# the in-tree build; MXFP8_PARTIAL_LIB names another build of the same sources (the host-code
+# sanitizer build of the CPU tests loads this way)
+LIB_PATH = os.environ.get("MXFP8_PARTIAL_LIB") or os.path.join(HERE, "libmxfp8partial.so")
 
 FP32 = 0
 BF16 = 1
@@ -26,7 +28,10 @@ STATUS_NAMES = {OK: "OK", ERR_ARG: "ERR_ARG", ERR_RANGE: "ERR_RANGE", ERR_DTYPE:
 # every entry point declared in include/mxfp8_partial.h
 EXPORTS = ("mxfp8_partial_amax", "mxfp8_combine_amax", "mxfp8_compute_scales",
            "mxfp8_partial_cast", "mxfp8_scales_and_cast", "mxfp8_quantize", "mxfp8_last_error",
-           "mxfp8_query_path")
+           "mxfp8_check_call", "mxfp8_query_path")
+
+# kernel numbers of mxfp8_check_call / mxfp8_query_path
+K_AMAX, K_CAST, K_SCALES_CAST, K_QUANTIZE, K_SCALES = range(5)
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -59,29 +64,36 @@ def lib():
     """Load libmxfp8partial.so (built in-tree by ``mxfp8_block_scaled_partial_amd.build``)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise LibraryNotBuilt(f"{LIB_PATH} is not built; run "
-                                  "`python -m mxfp8_block_scaled_partial_amd.build`")
-        try:
-            L = ctypes.CDLL(LIB_PATH)
-        except OSError as e:
-            raise LibraryNotBuilt(f"cannot load {LIB_PATH}: {e}") from e
-        PP = ctypes.POINTER(Piece)
-        for name in ("mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast",
-                     "mxfp8_scales_and_cast", "mxfp8_quantize"):
-            f = getattr(L, name)
-            f.argtypes = [PP, ctypes.c_int, ctypes.c_void_p]
-            f.restype = ctypes.c_int
-        L.mxfp8_combine_amax.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
-                                         ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
-                                         ctypes.c_void_p]
-        L.mxfp8_combine_amax.restype = ctypes.c_int
-        L.mxfp8_last_error.argtypes = []
-        L.mxfp8_last_error.restype = ctypes.c_char_p
-        L.mxfp8_query_path.argtypes = [PP, ctypes.c_int]
-        L.mxfp8_query_path.restype = ctypes.c_int
-        _lib = L
+        _lib = load_library(LIB_PATH)
     return _lib
+
+
+def load_library(path: str):
+    """A build of the library at ``path`` with the C ABI's argument and result types set."""
+    if not os.path.exists(path):
+        raise LibraryNotBuilt(f"{path} is not built; run "
+                              "`python -m mxfp8_block_scaled_partial_amd.build`")
+    try:
+        L = ctypes.CDLL(path)
+    except OSError as e:
+        raise LibraryNotBuilt(f"cannot load {path}: {e}") from e
+    PP = ctypes.POINTER(Piece)
+    for name in ("mxfp8_partial_amax", "mxfp8_compute_scales", "mxfp8_partial_cast",
+                 "mxfp8_scales_and_cast", "mxfp8_quantize"):
+        f = getattr(L, name)
+        f.argtypes = [PP, ctypes.c_int, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+    L.mxfp8_combine_amax.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                     ctypes.c_int, ctypes.c_int64, ctypes.c_int32,
+                                     ctypes.c_void_p]
+    L.mxfp8_combine_amax.restype = ctypes.c_int
+    L.mxfp8_last_error.argtypes = []
+    L.mxfp8_last_error.restype = ctypes.c_char_p
+    L.mxfp8_check_call.argtypes = [PP, ctypes.c_int, ctypes.c_int]
+    L.mxfp8_check_call.restype = ctypes.c_int
+    L.mxfp8_query_path.argtypes = [PP, ctypes.c_int]
+    L.mxfp8_query_path.restype = ctypes.c_int
+    return L
 
 
 def _check(status: int) -> None:
@@ -242,6 +254,13 @@ def mxfp8_quantize(pieces, stream=None) -> None:
     """amax, scales and cast in one pass, for fragments made of whole 32-row bands."""
     arr, n = _array(pieces)
     _check(lib().mxfp8_quantize(arr, n, _stream(stream)))
+
+
+def mxfp8_check_call(pieces, kernel: int) -> int:
+    """The status the entry point numbered ``kernel`` would return for these pieces before
+    launching (host-only validation; launches nothing)."""
+    arr, n = _array(pieces)
+    return lib().mxfp8_check_call(arr, n, kernel)
 
 
 def mxfp8_query_path(piece: Piece, kernel: int) -> int:

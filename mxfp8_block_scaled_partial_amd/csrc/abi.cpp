@@ -11,6 +11,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <limits>
 #include <vector>
 
@@ -218,8 +219,82 @@ int check_piece(const mxfp8_piece& q, Kind kind, int idx, mxfp8::Piece* out, boo
   return MXFP8_OK;
 }
 
-template <typename Launch>
-int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch launch) {
+// A buffer one piece of a call uses: its bytes, what it is, and whether the call writes it.
+struct Use {
+  uintptr_t lo, hi;
+  int64_t ld;
+  int role;      // index into kRoleName
+  bool write;
+  int piece;     // first piece using it
+  bool shared;   // more than one piece uses this very array
+};
+const char* kRoleName[] = {"input", "amax_row", "amax_col", "scale_row", "scale_col", "data_row",
+                           "data_col"};
+
+// The buffers of validated piece p for entry point `kind` (absent ones are left out).
+void uses_of(const mxfp8::Piece& p, Kind kind, int idx, std::vector<Use>& out) {
+  const int64_t esz = mxfp8::elem_size(p.dtype);
+  const int64_t nb = nblk(p.cols), nbands = nblk(p.rows);
+  const bool amax_w = kind == kAmax || kind == kQuant;
+  const bool scale_w = kind == kScales || kind == kFused || kind == kQuant;
+  auto add = [&](const void* ptr, Span sp, int64_t ld, int role, bool w) {
+    if (ptr && sp.hi > sp.lo) out.push_back({sp.lo, sp.hi, ld, role, w, idx, false});
+  };
+  add(p.input, span1d(p.input, p.len * esz), 0, 0, false);
+  add(p.amax_row, span2d(p.amax_row, p.rows, p.ld_ar, nb, esz), p.ld_ar, 1, amax_w);
+  add(p.amax_col, span2d(p.amax_col, nbands, p.ld_ac, p.cols, esz), p.ld_ac, 2, amax_w);
+  add(p.scale_row, span2d(p.scale_row, p.rows, p.ld_sr, nb, 1), p.ld_sr, 3, scale_w);
+  add(p.scale_col, span2d(p.scale_col, nbands, p.ld_sc, p.cols, 1), p.ld_sc, 4, scale_w);
+  add(p.data_row, span1d(p.data_row, p.len), 0, 5, true);
+  add(p.data_col, span1d(p.data_col, p.len), 0, 6, true);
+}
+
+// Across the pieces of one call, a buffer that one piece writes must not overlap a buffer of
+// another piece, except that pieces may share an amax or scale array (the same pointer,
+// leading dimension and extent in the same role): that is how the pieces of one weight merge
+// their blocks.  Within a piece, check_piece has already ruled out overlaps.
+int check_across(const std::vector<mxfp8::Piece>& ps, const std::vector<int>& idx, Kind kind) {
+  const char* fn = kKindName[kind];
+  std::vector<Use> u;
+  for (size_t i = 0; i < ps.size(); ++i) uses_of(ps[i], kind, idx[i], u);
+  // one entry per shared array
+  std::sort(u.begin(), u.end(), [](const Use& a, const Use& b) {
+    if (a.lo != b.lo) return a.lo < b.lo;
+    if (a.hi != b.hi) return a.hi < b.hi;
+    if (a.role != b.role) return a.role < b.role;
+    if (a.ld != b.ld) return a.ld < b.ld;
+    return a.piece < b.piece;
+  });
+  std::vector<Use> v;
+  for (const Use& x : u) {
+    if (!v.empty() && x.role >= 1 && x.role <= 4 && v.back().role == x.role &&
+        v.back().lo == x.lo && v.back().hi == x.hi && v.back().ld == x.ld) {
+      if (v.back().piece != x.piece) v.back().shared = true;
+      continue;
+    }
+    v.push_back(x);
+  }
+  // sweep in address order; `active` holds the buffers that reach past the current start
+  std::vector<const Use*> active;
+  for (const Use& x : v) {
+    size_t keep = 0;
+    for (const Use* a : active)
+      if (a->hi > x.lo) active[keep++] = a;
+    active.resize(keep);
+    for (const Use* a : active) {
+      if (!(a->write || x.write)) continue;
+      if (!a->shared && !x.shared && a->piece == x.piece) continue;  // one piece: checked
+      return fail(MXFP8_ERR_LAYOUT, "%s: piece %d's %s overlaps piece %d's %s", fn, x.piece,
+                  kRoleName[x.role], a->piece, kRoleName[a->role]);
+    }
+    active.push_back(&x);
+  }
+  return MXFP8_OK;
+}
+
+// Validates a whole call (every piece, then the pieces against each other); fills `todo` with
+// the pieces that have work.
+int validate_call(const mxfp8_piece* pieces, int n, Kind kind, std::vector<mxfp8::Piece>& todo) {
   const char* fn = kKindName[kind];
   if (n < 0) return fail(MXFP8_ERR_ARG, "%s: n = %d < 0", fn, n);
   if (n > 0 && !pieces) return fail(MXFP8_ERR_ARG, "%s: pieces is NULL", fn);
@@ -230,14 +305,29 @@ int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch
     const int st = check_piece(pieces[i], kind, i, &p, &skip);
     if (st) return st;
   }
-  std::vector<mxfp8::Piece> todo;
+  todo.clear();
+  std::vector<int> idx;  // each one's index in the caller's array
   todo.reserve(n);
+  idx.reserve(n);
   for (int i = 0; i < n; ++i) {
     mxfp8::Piece p;
     bool skip;
     check_piece(pieces[i], kind, i, &p, &skip);
-    if (!skip) todo.push_back(p);
+    if (!skip) {
+      todo.push_back(p);
+      idx.push_back(i);
+    }
   }
+  if (todo.size() > 1) return check_across(todo, idx, kind);
+  return MXFP8_OK;
+}
+
+template <typename Launch>
+int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch launch) {
+  const char* fn = kKindName[kind];
+  std::vector<mxfp8::Piece> todo;
+  const int st = validate_call(pieces, n, kind, todo);
+  if (st) return st;
   if (todo.empty()) return MXFP8_OK;
   const hipError_t e = launch(todo.data(), (int)todo.size(), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MXFP8_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
@@ -298,6 +388,15 @@ int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
 
 const char* mxfp8_last_error(void) { return g_err; }
 
+int mxfp8_check_call(const mxfp8_piece* pieces, int n, int kernel) {
+  if (kernel < 0 || kernel > 4)
+    return fail(MXFP8_ERR_ARG, "mxfp8_check_call: kernel must be 0 (amax), 1 (cast), 2 "
+                               "(scales and cast), 3 (quantize) or 4 (scales)");
+  const Kind kinds[5] = {kAmax, kCast, kFused, kQuant, kScales};
+  std::vector<mxfp8::Piece> todo;
+  return validate_call(pieces, n, kinds[kernel], todo);
+}
+
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel) {
   if (!piece) return -fail(MXFP8_ERR_ARG, "mxfp8_query_path: piece is NULL");
   if (kernel < 0 || kernel > 3)
@@ -309,7 +408,9 @@ int mxfp8_query_path(const mxfp8_piece* piece, int kernel) {
   const int st = check_piece(*piece, kinds[kernel], 0, &p, &skip);
   if (st) return -st;
   if (skip) return 0;
-  return kernel == 0 ? (int)mxfp8::amax_fast_ok(p) : (int)mxfp8::cast_fast_ok(p);
+  if (kernel == 0) return (int)mxfp8::amax_fast_ok(p);
+  if (kernel == 1 && mxfp8::cast_lines_ok(p)) return 2;
+  return (int)mxfp8::cast_fast_ok(p);
 }
 
 }  // extern "C"

@@ -376,3 +376,89 @@ def test_boundary_spans_cover_exactly_the_shared_entries():
                 oc = offs[i] + sp.amax_row_entries + bd * sp.cols
                 allowed |= set(range(oc, oc + sp.cols))
         assert covered <= allowed, trial
+
+
+# ------------------------------------------------------------------ whole-call validation
+
+def piece_at(start, length, rows=64, cols=64, dtype=B.BF16, k=0, **bufs):
+    """A piece whose input and fragment-relative outputs live in slot k of their own regions,
+    sharing the weight's amax and scale arrays (as the pieces of one weight do)."""
+    esz = 2 if dtype == B.BF16 else 4
+    d = {"input": BASE + 0x08000000 * k + start * esz,
+         "data_row": BASE + 0x50000000 + start, "data_col": BASE + 0x60000000 + start}
+    d.update(bufs)
+    return raw_piece(rows=rows, cols=cols, start=start, length=length, dtype=dtype, **d)
+
+
+@pytest.mark.parametrize("kernel", [B.K_AMAX, B.K_CAST, B.K_SCALES_CAST, B.K_SCALES])
+def test_pieces_of_one_weight_may_share_amax_and_scale_arrays(kernel):
+    ps = [piece_at(0, 1000, k=0), piece_at(1000, 2000, k=1), piece_at(3000, 1096, k=2)]
+    assert B.mxfp8_check_call(ps, kernel) == B.OK, B.mxfp8_last_error()
+
+
+def test_whole_call_validation_matches_the_entry_points():
+    bad = [piece_at(0, 1000), piece_at(1000, 100, rows=0)]
+    assert B.mxfp8_check_call(bad, B.K_CAST) == B.ERR_ARG
+    assert "piece 1" in B.mxfp8_last_error()
+    assert call(CAST, *bad) == B.ERR_ARG
+    assert B.mxfp8_check_call(bad[:1], 9) == B.ERR_ARG
+    # empty pieces are skipped, as by the entry points
+    empty = B.Piece(64, 64, 17, 0, B.BF16, 0, None, B.Buf(None, 0), B.Buf(None, 0),
+                    B.Buf(None, 0), B.Buf(None, 0), None, None)
+    assert B.mxfp8_check_call([empty, empty], B.K_QUANTIZE) == B.OK
+
+
+@pytest.mark.parametrize("kernel", [B.K_CAST, B.K_SCALES_CAST])
+def test_overlap_across_pieces_is_rejected(kernel):
+    good = [piece_at(0, 1000, k=0), piece_at(1000, 2000, k=1)]
+    assert B.mxfp8_check_call(good, kernel) == B.OK
+    # piece 1's row-wise output overlaps piece 0's
+    p1 = piece_at(1000, 2000, k=1, data_row=BASE + 0x50000000 + 900)
+    assert B.mxfp8_check_call([good[0], p1], kernel) == B.ERR_LAYOUT
+    assert "piece 1's data_row overlaps piece 0's data_row" in B.mxfp8_last_error() or \
+        "piece 0's data_row overlaps piece 1's data_row" in B.mxfp8_last_error()
+    # piece 1's column-wise output written over piece 0's input
+    p1 = piece_at(1000, 2000, k=1, data_col=BASE + 10)
+    assert B.mxfp8_check_call([good[0], p1], kernel) == B.ERR_LAYOUT
+    assert "overlaps" in B.mxfp8_last_error()
+    # the same through the entry point: nothing is launched
+    assert call(CAST, good[0], p1) == B.ERR_LAYOUT
+
+
+def test_overlap_of_a_written_array_with_another_pieces_array_is_rejected():
+    # two weights: the second's amax_row partly over the first's (not the same array)
+    a = piece_at(0, 4096, k=0)
+    b = piece_at(0, 4096, k=1, amax_row=B.Buf(BASE + 0x10000000 + 64, 2),
+                 amax_col=B.Buf(BASE + 0x28000000, 64), data_row=BASE + 0x58000000,
+                 data_col=BASE + 0x68000000)
+    assert B.mxfp8_check_call([a, b], B.K_AMAX) == B.ERR_LAYOUT
+    assert "amax_row" in B.mxfp8_last_error()
+    # the same array with another leading dimension is not shared either
+    b = piece_at(0, 4096, k=1, amax_row=B.Buf(BASE + 0x10000000, 3),
+                 amax_col=B.Buf(BASE + 0x28000000, 64))
+    assert B.mxfp8_check_call([a, b], B.K_AMAX) == B.ERR_LAYOUT
+    # a read-only array shared by the cast pieces may overlap another piece's read-only one
+    c = piece_at(0, 4096, k=1, scale_row=B.Buf(BASE + 0x30000000 + 5, 2),
+                 data_row=BASE + 0x58000000, data_col=BASE + 0x68000000)
+    assert B.mxfp8_check_call([a, c], B.K_CAST) == B.OK
+    # ... but not one the call writes
+    assert B.mxfp8_check_call([a, c], B.K_SCALES) == B.ERR_LAYOUT
+
+
+def test_query_path_reports_line_owned_cast_tiles():
+    q = B.mxfp8_query_path
+    # rows of whole 128-byte lines, outputs off a line: line-owned tiles for the cast only
+    p = raw_piece(rows=64, cols=256, start=17, length=1000, input=BASE + 34,
+                  data_row=BASE + 0x50000000, data_col=BASE + 0x60000000)
+    assert q(p, 1) == 2 and q(p, 0) == 1 and q(p, 2) == 1
+    # outputs on a line, or the two outputs at different offsets: the standard tiles
+    assert q(raw_piece(rows=64, cols=256, start=17, length=1000, data_row=BASE + 0x50000000 + 17,
+                       data_col=BASE + 0x60000000 + 17), 1) == 1
+    assert q(raw_piece(rows=64, cols=256, start=17, length=1000, data_row=BASE + 0x50000000,
+                       data_col=BASE + 0x60000000 + 1), 1) == 1
+    # row-only: only the row-wise output counts
+    assert q(raw_piece(rows=64, cols=256, start=17, length=1000, data_row=BASE + 0x50000000,
+                       data_col=None), 1) == 2
+    # rows that are not whole lines
+    assert q(raw_piece(rows=64, cols=192, start=17, length=1000, data_row=BASE + 0x50000000,
+                       data_col=BASE + 0x60000000), 1) == 1
