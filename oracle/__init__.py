@@ -27,7 +27,9 @@ BF16 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "mxfp8_oracle.c")
-_LIB = os.path.join(_HERE, "libmxfp8_oracle.so")
+# MXFP8_ORACLE_LIB names another build of mxfp8_oracle.c (the sanitizer build of the CPU
+# tests loads this way)
+_LIB = os.environ.get("MXFP8_ORACLE_LIB") or os.path.join(_HERE, "libmxfp8_oracle.so")
 
 _ERRORS = {1: "bad argument", 2: "fragment out of range", 3: "bad dtype", 4: "bad layout",
            5: "non-finite working value", 6: "scale byte 255"}
