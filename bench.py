@@ -59,6 +59,8 @@ def parse():
                     help="distinct input/output sets rotate until this many GB are in use")
     ap.add_argument("--kernel-table", dest="kernel_table", action="store_true", default=True)
     ap.add_argument("--no-kernel-table", dest="kernel_table", action="store_false")
+    ap.add_argument("--table-shapes", default="16384x6144,4096x4096,1024x1024,160x96",
+                    help="matrices of the per-call table, comma-separated ROWSxCOLS")
     ap.add_argument("--kernel-calls", type=int, default=140,
                     help="graph replays (10 calls each) per kernel-table entry (7 rounds of 20)")
     ap.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
@@ -71,11 +73,42 @@ def parse():
     ap.add_argument("--single-pass", dest="single_pass", action="store_true", default=True,
                     help="also time the writeback that quantizes whole bands in one pass")
     ap.add_argument("--no-single-pass", dest="single_pass", action="store_false")
+    ap.add_argument("--layer-batch", dest="layer_batch", action="store_true", default=True,
+                    help="also time the transformer-layer batch (4 weights, 8 fragments): the "
+                         "whole writeback with one shared packed buffer and with 8 buffers + "
+                         "combine, and one rank's fragment")
+    ap.add_argument("--no-layer-batch", dest="layer_batch", action="store_false")
     ap.add_argument("--copy-probe", dest="copy_probe", action="store_true", default=True,
                     help="also time a plain device copy (the achievable read + write ceiling, "
                          "and the counter calibration kernel); on by default")
     ap.add_argument("--no-copy-probe", dest="copy_probe", action="store_false")
     return ap.parse_args()
+
+
+def hip_runtime_path() -> str:
+    """Path of the HIP runtime library this process has loaded (torch maps its own at import,
+    and the library resolves to it), read from /proc/self/maps, so the benchmark talks to the
+    same runtime instance whatever its file name or soname."""
+    import torch  # noqa: F401
+
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1] if len(line.split()) >= 6 else ""
+            if os.path.basename(path).startswith("libamdhip64.so"):
+                return path
+    raise RuntimeError("the HIP runtime (libamdhip64) is not loaded in this process")
+
+
+def hip_event_flag(name: str, fallback: int) -> int:
+    """Value of a hipEvent* flag macro from the HIP headers of the ROCm install, if present
+    (the documented value otherwise)."""
+    for root in (os.environ.get("ROCM_PATH"), "/opt/rocm"):
+        hdr = os.path.join(root or "", "include", "hip", "hip_runtime_api.h")
+        if root and os.path.exists(hdr):
+            m = re.search(r"#define\s+" + name + r"\s+(0x[0-9a-fA-F]+|\d+)", open(hdr).read())
+            if m:
+                return int(m.group(1), 0)
+    return fallback
 
 
 class TimingEvent:
@@ -85,16 +118,17 @@ class TimingEvent:
     caches at system scope, which lengthens the stream by a few µs at every marker; without
     that fence the marker only takes its timestamp, so the time between two markers is close
     to the kernel durations a profiler reports.  torch.cuda.Event cannot set the flag, so this
-    calls the HIP runtime torch has already loaded (same soname, so the same instance) and
-    records on torch's current stream, where the library launches.
+    calls the HIP runtime torch has already loaded (found in the process's mappings, so the
+    same instance) and records on torch's current stream, where the library launches.
     """
-    DISABLE_SYSTEM_FENCE = 0x20000000
     _hip = None
+    _flag = None
 
     @classmethod
     def _rt(cls):
         if cls._hip is None:
-            h = ctypes.CDLL("libamdhip64.so.7")
+            cls._flag = hip_event_flag("hipEventDisableSystemFence", 0x20000000)
+            h = ctypes.CDLL(hip_runtime_path())
             h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
             h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
             h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
@@ -113,8 +147,7 @@ class TimingEvent:
 
     def __init__(self):
         self.ev = ctypes.c_void_p()
-        self._ok(self._rt().hipEventCreateWithFlags(ctypes.byref(self.ev),
-                                                    self.DISABLE_SYSTEM_FENCE),
+        self._ok(self._rt().hipEventCreateWithFlags(ctypes.byref(self.ev), self._flag),
                  "hipEventCreateWithFlags")
 
     def record(self):
@@ -369,6 +402,18 @@ def main():
 
     if args.kernel_table:
         out["kernels"], out["kernels_other_shapes"] = kernel_table(args, m, dev)
+        # the bar: partial amax and partial cast each at >= 70% of HBM peak on the full
+        # 16384x6144 input, BF16 and FP32 (per-call table, graph replays)
+        k = out["kernels"]
+        names = ("amax_bf16_full", "cast_bf16_full", "amax_fp32_full", "cast_fp32_full")
+        if all(nm in k for nm in names):
+            roofline["bar"] = {nm: {"us": k[nm]["us"], "frac": k[nm]["frac_of_peak"]}
+                               for nm in names}
+            roofline["bar"]["target_frac"] = 0.70
+            roofline["bar"]["all_met"] = all(k[nm]["frac_of_peak"] >= 0.70 for nm in names)
+
+    if args.layer_batch:
+        out["layer_batch"] = layer_batch(args, dev)
 
     if args.cpu:
         out["cpu_baseline"] = cpu
@@ -445,6 +490,173 @@ def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
                     "with the partial chain for the bands at the cuts"}
 
 
+def layer_batch(args, dev):
+    """The transformer-layer batch: QKV 4096x12288 (bidirectional), out-proj 4096x4096
+    (row-only), up 4096x14336 (bidirectional), down 14336x4096 (row-only), BF16, end to end in
+    one flat buffer of 184 549 376 elements cut into 8 equal fragments (fragments 2 and 5 span
+    weight boundaries).
+
+    ``steps``: the whole writeback per step, with one packed buffer per fragment + a K = 8
+    MAX-combine (as 8 ranks would hold them), and with one shared packed buffer whose cut
+    blocks merge atomically (no combine).  Two buffer sets; step i runs the amax side on set i
+    and the cast of set i - 1, as in the main step.  Timed with events around each whole step
+    (eager) and from graph replays; a separate pass with a marker before every stage gives
+    each stage's µs and its GB/s / fraction of peak on the stage's algorithmic bytes.
+
+    ``rank_fragment``: one rank's share, fragment 2 (its pieces of QKV, out-proj and up), per
+    call like the kernel table (graph replays of 10 calls over rotating buffer sets): its
+    partial amax, and its cast in place and into fragment-sized outputs."""
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import binding as B
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
+    from mxfp8_block_scaled_partial_amd import workloads as wl
+    from mxfp8_block_scaled_partial_amd import writeback as W
+
+    log("generating the layer batch")
+    b = wl.layer_batch()
+    specs = [W.WeightSpec(r, c, cw) for _, r, c, cw in b.tensors]
+    frags = b.fragments
+    x0 = torch.from_numpy(b.data.view(np.int16)).view(torch.bfloat16).to(dev)
+    del b
+    packed = sum(sp.amax_row_entries + sp.amax_col_entries for sp in specs)
+
+    def piece_sum(frag_list, key):
+        tot = 0
+        for fs, fl in frag_list:
+            for (i, st, n, _) in W.split_fragment(specs, fs, fl):
+                tot += BM.piece_bytes(specs[i].rows, specs[i].cols, st, n, 2,
+                                      specs[i].colwise)[key]
+        return tot
+
+    scale_bytes = sum(BM.piece_bytes(sp.rows, sp.cols, 0, sp.numel, 2, sp.colwise)["scales"]
+                      for sp in specs)
+    res = {"workload": "QKV 4096x12288 bi, out 4096x4096 row, up 4096x14336 bi, down "
+                       "14336x4096 row; BF16; 184549376 elements in 8 fragments",
+           "packed_entries": packed}
+    xs = [x0, x0.clone()]
+    for mode, shared in (("k_buffers", False), ("shared_buffer", True)):
+        k = 1 if shared else len(frags)
+        stage_bytes = {"zero": BM.zero_bytes(k, packed, 2), "amax": piece_sum(frags, "amax")}
+        if not shared:
+            stage_bytes["combine"] = BM.combine_bytes(k, packed, 2)
+        stage_bytes["scales"] = scale_bytes
+        stage_bytes["cast"] = piece_sum(frags, "cast")
+        total = sum(stage_bytes.values())
+        plans = []
+        for x in xs:
+            wb = W.Writeback(specs, torch.bfloat16, dev, frags, shared=shared)
+            plans.append(wb.plan([x[s:s + l] for s, l in frags]))
+        names = [nm for nm, _ in plans[0].stages()]
+        assert names[-1] == "cast" and list(stage_bytes) == names, names
+
+        def step(i, ev=None):
+            seq = plans[i % 2].stages()[:-1] + [plans[(i - 1) % 2].stages()[-1]]
+            for j, (_, fn) in enumerate(seq):
+                if ev is not None:
+                    ev[j].record()
+                fn()
+            if ev is not None:
+                ev[-1].record()
+
+        for i in range(max(2, args.warmup)):
+            step(i)
+        torch.cuda.synchronize()
+        steps = max(4, args.steps // 2)
+        tev = [(TimingEvent(), TimingEvent()) for _ in range(steps)]
+        for i, (e0, e1) in enumerate(tev):
+            e0.record()
+            step(i)
+            e1.record()
+        torch.cuda.synchronize()
+        step_us = statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in tev)
+        evs = [[TimingEvent() for _ in range(len(names) + 1)] for _ in range(steps)]
+        for i in range(steps):
+            step(i, evs[i])
+        torch.cuda.synchronize()
+        stage_us = {nm: statistics.median(e[j].elapsed_time(e[j + 1]) * 1e3 for e in evs)
+                    for j, nm in enumerate(names)}
+
+        def graph_fn(j):
+            def fn():
+                for _, f in (plans[j % 2].stages()[:-1] + [plans[(j - 1) % 2].stages()[-1]]):
+                    f()
+            return fn
+
+        graph_us = graph_step_us(args, [graph_fn(0), graph_fn(1)])
+        res[mode] = {
+            "us": round(step_us, 2), "graph_us": graph_us, "alg_bytes": total,
+            "GBps": round(total / (step_us * 1e-6) / 1e9, 1),
+            "stages": {nm: {"us": round(stage_us[nm], 2), "alg_bytes": stage_bytes[nm],
+                            "GBps": round(stage_bytes[nm] / (stage_us[nm] * 1e-6) / 1e9, 1),
+                            "frac_of_peak": round(stage_bytes[nm] / (stage_us[nm] * 1e-6) / 1e9
+                                                  / HBM_PEAK_GBS, 4)}
+                       for nm in names},
+            "launches": {"amax": plans[0].n_amax, "cast": plans[0].n_cast},
+            "note": "stage times from a pass with a marker before every stage"}
+        del plans
+        torch.cuda.empty_cache()
+
+    # one rank's fragment, per call
+    f = 2
+    fs, fl = frags[f]
+    rank = {"fragment": [fs, fl], "pieces": [[i, st, n] for (i, st, n, _) in
+                                              W.split_fragment(specs, fs, fl)]}
+    per_set = fl * 2 * 2 + 2 * packed * 3
+    n_sets = max(2, min(10, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
+    for name, fo in (("in_place", False), ("fragment_outputs", True)):
+        plans = []
+        for i in range(n_sets):
+            x = x0[fs:fs + fl].clone()  # the rank's shard in an allocation of its own
+            wb = W.Writeback(specs, torch.bfloat16, dev, [(fs, fl)], shared=True,
+                             fragment_outputs=fo)
+            plans.append(wb.plan([x]))
+        lib = B.lib()
+        calls = [("cast", lambda p, sp: lib.mxfp8_partial_cast(p.cast, p.n_cast, sp))]
+        if not fo:
+            calls.insert(0, ("amax", lambda p, sp: lib.mxfp8_partial_amax(p.amax, p.n_amax, sp)))
+        for kname, call in calls:
+            def fn(i, call=call):
+                assert call(plans[i % n_sets], torch.cuda.current_stream().cuda_stream) == 0
+            us = per_call_us(args, fn, 10)
+            nb = piece_sum([(fs, fl)], kname)
+            rank[f"{kname}_{name}"] = {"us": round(us, 2), "alg_bytes": nb,
+                                       "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+                                       "frac_of_peak": round(nb / (us * 1e-6) / 1e9
+                                                             / HBM_PEAK_GBS, 4),
+                                       "launches": 1, "buffer_sets": n_sets}
+        del plans
+        torch.cuda.empty_cache()
+    res["rank_fragment"] = rank
+    return res
+
+
+def per_call_us(args, fn, per_graph):
+    """Median µs per call of ``fn(i)`` (call i on buffer set i), from HIP events around
+    replays of a captured graph of ``per_graph`` calls, as in the per-call table."""
+    import torch
+
+    for i in range(3):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(TimingEvent(), TimingEvent()) for _ in range(args.kernel_calls)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    us = statistics.median(e0.elapsed_time(e1) * 1e3 / per_graph for e0, e1 in ev)
+    del g
+    return us
+
+
 def graph_step_us(args, step_fns):
     """Median µs of one step replayed from a captured HIP graph (one graph per buffer set,
     replayed in turn), so no host launch gap sits between the step's kernels."""
@@ -473,10 +685,6 @@ def graph_step_us(args, step_fns):
     return round(us, 2)
 
 
-# The matrices of the pages' per-call table ("Bidirectional kernel performance"), largest first.
-TABLE_SHAPES = [(16384, 6144), (4096, 4096), (1024, 1024), (160, 96)]
-
-
 def kernel_table(args, m_default, dev):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
     scales + cast and (full input only) the single-pass quantize, for every matrix of that
@@ -494,7 +702,8 @@ def kernel_table(args, m_default, dev):
     from mxfp8_block_scaled_partial_amd import workloads as wl
 
     table, by_shape = {}, {}
-    for rows, cols in TABLE_SHAPES:
+    shapes = [tuple(int(v) for v in t.split("x")) for t in args.table_shapes.split(",") if t]
+    for rows, cols in shapes:
         for dtype in ("bf16", "fp32"):
             if (rows, cols) == (16384, 6144):
                 if dtype == args.dtype:
@@ -534,9 +743,13 @@ def time_shape(args, m, dev):
     if (rows, cols) == (16384, 6144):
         # one rank's own buffers: the quarter fragment's input and its fragment-sized E4M3
         # outputs in allocations of their own, so input - 17 and data - 17 lose their alignment
-        # (BF16 input 2 bytes off a dword, outputs 1 byte off: shifted loads, window stores)
+        # (BF16 input 2 bytes off a dword; outputs off their 128-byte lines: the cast's
+        # line-owned tiles)
         runs.append(("partial_own", (17, n // 4)))
+        # row-only (column-wise outputs absent: the kColwise = false kernels), full input
+        runs.append(("full_rowonly", (0, n)))
     for run, (s, l) in runs:
+        colwise = run != "full_rowonly"
         # element offset that keeps input - s (and data - s) aligned; 0 for a rank's own buffers
         lead = 0 if run == "partial_own" else s % 32
         per_set = l * s_in + 2 * l + (rows * nb + nbands * cols) * (s_in + 1)
@@ -554,6 +767,8 @@ def time_shape(args, m, dev):
             dcb = torch.empty(l + 32, dtype=torch.uint8, device=dev)
             dr, dc = drb[lead:lead + l], dcb[lead:lead + l]
             keep.append((xb, ar, ac, sr, sc, drb, dcb))
+            if not colwise:  # empty handles for the absent direction
+                ac = dc = None
             amax_p.append(B.make_piece(rows, cols, s, x, amax_row=ar, amax_col=ac))
             cast_p.append(B.make_piece(rows, cols, s, x, scale_row=sr, scale_col=sc,
                                        data_row=dr, data_col=dc))
@@ -561,15 +776,16 @@ def time_shape(args, m, dev):
                                         scale_row=sr, scale_col=sc, data_row=dr,
                                         data_col=dc))
             assert B.mxfp8_query_path(amax_p[-1], 0) == 1
-            assert B.mxfp8_query_path(cast_p[-1], 1) == 1
+            # a rank's own output buffers sit off the 128-byte lines: line-owned cast tiles
+            assert B.mxfp8_query_path(cast_p[-1], 1) == (2 if run == "partial_own" else 1)
             assert B.mxfp8_query_path(fused_p[-1], 2) == 1
             assert run != "full" or B.mxfp8_query_path(fused_p[-1], 3) == 1
-        pb = BM.piece_bytes(rows, cols, s, l, s_in, True)
+        pb = BM.piece_bytes(rows, cols, s, l, s_in, colwise)
         # the amax runs first, so the fused call reads real amax entries; the single-pass
         # quantize needs whole bands, so it runs on the full input only
         kernels = [("amax", amax_p, B.mxfp8_partial_amax),
                    ("cast", cast_p, B.mxfp8_partial_cast)]
-        if run != "partial_own":
+        if run in ("full", "partial"):
             kernels.append(("scales_cast", fused_p, B.mxfp8_scales_and_cast))
         if run == "full":
             kernels.append(("quantize", fused_p, B.mxfp8_quantize))

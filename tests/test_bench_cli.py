@@ -21,3 +21,15 @@ def test_world_size_above_one_is_refused():
                        text=True, timeout=120, env=env)
     assert r.returncode == 2
     assert "WORLD_SIZE 4" in r.stderr
+
+
+def test_timing_events_find_the_loaded_hip_runtime():
+    """The benchmark's timing events use the HIP runtime already mapped into the process (no
+    library name is assumed) and read the fence-free event flag from the HIP headers."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    path = bench.hip_runtime_path()
+    assert os.path.basename(path).startswith("libamdhip64.so") and os.path.exists(path)
+    assert bench.hip_event_flag("hipEventDisableSystemFence", 0) == 0x20000000
+    assert bench.hip_event_flag("noSuchFlagAnywhere", 7) == 7
