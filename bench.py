@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--no-kernel-table", dest="kernel_table", action="store_false")
     ap.add_argument("--table-shapes", default="16384x6144,4096x4096,1024x1024,160x96",
                     help="matrices of the per-call table, comma-separated ROWSxCOLS")
+    ap.add_argument("--table-runs", default="full,partial,partial_own,full_rowonly",
+                    help="runs of the per-call table: full, partial (quarter at offset 17), "
+                         "partial_own (the quarter in a rank's own buffers, 16384x6144 only), "
+                         "full_rowonly (16384x6144 only)")
     ap.add_argument("--kernel-calls", type=int, default=140,
                     help="graph replays (10 calls each) per kernel-table entry (7 rounds of 20)")
     ap.add_argument("--cpu-baseline", dest="cpu", action="store_true", default=True)
@@ -78,6 +82,11 @@ def parse():
                          "whole writeback with one shared packed buffer and with 8 buffers + "
                          "combine, and one rank's fragment")
     ap.add_argument("--no-layer-batch", dest="layer_batch", action="store_false")
+    ap.add_argument("--ablation", action="store_true", default=False,
+                    help="also time the runtime-guard ablation library (build.py --ablation) "
+                         "against the product's compile-time specialization: amax and cast, "
+                         "row-only and bidirectional, full input and quarter fragment, BF16 and "
+                         "FP32 at 16384x6144")
     ap.add_argument("--copy-probe", dest="copy_probe", action="store_true", default=True,
                     help="also time a plain device copy (the achievable read + write ceiling, "
                          "and the counter calibration kernel); on by default")
@@ -406,7 +415,7 @@ def main():
         # 16384x6144 input, BF16 and FP32 (per-call table, graph replays)
         k = out["kernels"]
         names = ("amax_bf16_full", "cast_bf16_full", "amax_fp32_full", "cast_fp32_full")
-        if all(nm in k for nm in names):
+        if all(nm in k for nm in names) and roofline is not None:
             roofline["bar"] = {nm: {"us": k[nm]["us"], "frac": k[nm]["frac_of_peak"]}
                                for nm in names}
             roofline["bar"]["target_frac"] = 0.70
@@ -414,6 +423,9 @@ def main():
 
     if args.layer_batch:
         out["layer_batch"] = layer_batch(args, dev)
+
+    if args.ablation:
+        out["ablation"] = ablation(args, dev)
 
     if args.cpu:
         out["cpu_baseline"] = cpu
@@ -632,6 +644,93 @@ def layer_batch(args, dev):
     return res
 
 
+def ablation(args, dev, rounds=3):
+    """The PR page's one design measurement ("Bidirectional kernel performance": an earlier
+    version whose amax selected the column-wise work with runtime pointer guards was 21-35%
+    slower) redone on MI355X with the current kernels: the product's compile-time
+    specialization (one kernel per direction) against libmxfp8partial_guards.so (one kernel per
+    dtype for both, the column-wise work selected at run time by the column-wise pointer).
+    16384x6144 BF16 and FP32, full input and the quarter fragment at offset 17, row-only and
+    bidirectional, amax and cast; per call from graph replays of 10 calls over rotating buffer
+    sets, the two builds interleaved over ``rounds`` rounds (median).  Each case also checks
+    that the two builds write the same bytes."""
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_partial_amd import binding as B
+    from mxfp8_block_scaled_partial_amd import build as hip_build
+    from mxfp8_block_scaled_partial_amd import workloads as wl
+
+    libs = {"compile_time": B.lib(), "runtime_guard": B.load_library(hip_build.GUARDS_LIB)}
+    out = {"note": "µs per call; ratio = runtime_guard / compile_time"}
+    for dtype in ("bf16", "fp32"):
+        log(f"ablation: {dtype}")
+        m = wl.matrix_large(dtype)
+        rows, cols = m.rows, m.cols
+        n = rows * cols
+        nb, nbands = B.nblocks(cols), B.nblocks(rows)
+        tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+        s_in = 2 if dtype == "bf16" else 4
+        x0 = (torch.from_numpy(m.data.view(np.int16)).view(torch.bfloat16) if dtype == "bf16"
+              else torch.from_numpy(m.data)).to(dev)
+        for run, (s, l) in (("full", (0, n)), ("quarter", (17, n // 4))):
+            lead = s % 32  # input - s and data - s stay aligned, as in the per-call table
+            per_set = l * s_in + 2 * l + (rows * nb + nbands * cols) * (s_in + 1)
+            n_sets = max(2, min(10, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
+            sets = []
+            for i in range(n_sets):
+                xb = torch.empty(l + 32, dtype=tdt, device=dev)
+                xb[lead:lead + l] = x0[s:s + l]
+                bufs = dict(x=xb[lead:lead + l], xb=xb,
+                            ar=torch.zeros(rows, nb, dtype=tdt, device=dev),
+                            ac=torch.zeros(nbands, cols, dtype=tdt, device=dev),
+                            sr=torch.full((rows, nb), 120, dtype=torch.uint8, device=dev),
+                            sc=torch.full((nbands, cols), 120, dtype=torch.uint8, device=dev),
+                            drb=torch.zeros(l + 32, dtype=torch.uint8, device=dev),
+                            dcb=torch.zeros(l + 32, dtype=torch.uint8, device=dev))
+                sets.append(bufs)
+            for colwise in (True, False):
+                arrs = {"amax": [], "cast": []}
+                for b in sets:
+                    dr, dc = b["drb"][lead:lead + l], b["dcb"][lead:lead + l]
+                    arrs["amax"].append(B._array([B.make_piece(
+                        rows, cols, s, b["x"], amax_row=b["ar"],
+                        amax_col=b["ac"] if colwise else None)])[0])
+                    arrs["cast"].append(B._array([B.make_piece(
+                        rows, cols, s, b["x"], scale_row=b["sr"], scale_col=b["sc"],
+                        data_row=dr, data_col=dc if colwise else None)])[0])
+                for kname in ("amax", "cast"):
+                    # same bytes from both builds (set 0, outputs cleared before each)
+                    outs = []
+                    for name, L in libs.items():
+                        b = sets[0]
+                        for t in (b["ar"], b["ac"], b["drb"], b["dcb"]):
+                            t.zero_()
+                        f = getattr(L, f"mxfp8_partial_{kname}")
+                        assert f(arrs[kname][0], 1, torch.cuda.current_stream().cuda_stream) == 0
+                        torch.cuda.synchronize()
+                        outs.append([t.clone() for t in (b["ar"], b["ac"], b["drb"], b["dcb"])])
+                    same = all(torch.equal(a, c) for a, c in zip(*outs))
+                    times = {name: [] for name in libs}
+                    for _ in range(rounds):
+                        for name, L in libs.items():
+                            f = getattr(L, f"mxfp8_partial_{kname}")
+
+                            def fn(i, f=f, a=arrs[kname]):
+                                assert f(a[i % n_sets], 1,
+                                         torch.cuda.current_stream().cuda_stream) == 0
+                            times[name].append(per_call_us(args, fn, 10))
+                    ct = statistics.median(times["compile_time"])
+                    rg = statistics.median(times["runtime_guard"])
+                    key = f"{kname}_{dtype}_{run}_{'bidirectional' if colwise else 'rowonly'}"
+                    out[key] = {"compile_time_us": round(ct, 2), "runtime_guard_us": round(rg, 2),
+                                "ratio": round(rg / ct, 3), "same_bytes": same,
+                                "buffer_sets": n_sets}
+            del sets
+            torch.cuda.empty_cache()
+    return out
+
+
 def per_call_us(args, fn, per_graph):
     """Median µs per call of ``fn(i)`` (call i on buffer set i), from HIP events around
     replays of a captured graph of ``per_graph`` calls, as in the per-call table."""
@@ -748,7 +847,10 @@ def time_shape(args, m, dev):
         runs.append(("partial_own", (17, n // 4)))
         # row-only (column-wise outputs absent: the kColwise = false kernels), full input
         runs.append(("full_rowonly", (0, n)))
+    keep_runs = set(args.table_runs.split(","))
     for run, (s, l) in runs:
+        if run not in keep_runs:
+            continue
         colwise = run != "full_rowonly"
         # element offset that keeps input - s (and data - s) aligned; 0 for a rank's own buffers
         lead = 0 if run == "partial_own" else s % 32

@@ -109,6 +109,8 @@ struct TileArgs {
   int32_t nt_row, nt_col;  // each output row starts on a 64-byte boundary: streaming stores
   int32_t sc_vec;  // scale_col rows aligned to a chunk's E bytes: a lane's scale bytes are one load
   int32_t shift;   // line-owned cast tiles: flat offset of every tile column (0 elsewhere)
+  int32_t row_pair, col_pair;  // BF16 amax rows start on 4-byte boundaries: entries 2k, 2k + 1
+                               // share an aligned 32-bit word
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
@@ -230,6 +232,39 @@ __device__ __forceinline__ void atomic_max_entries(uint16_t* const (&p)[N],
       else
         old[i] = prev[i];
     }
+  }
+}
+
+// Two BF16 entries sharing the aligned 32-bit word w (v: the low entry's value in bits 0-15, the
+// high one's in 16-31).  Half h takes its value when its mode is 1 (the piece holds the block
+// whole: set) or the max of its value and the word's when 2 (a block a fragment boundary cuts:
+// merged); mode 0 leaves it alone.  Without a merge the halves are stored.  With one, a single
+// thread owns the word, so no swap of this tile races another of its own; amax buffers are
+// zero-filled before an update, so the first swap assumes a zero word, and any other value
+// costs one retry with the word it found.
+__device__ __forceinline__ void update_entry_pair(uint32_t* w, uint32_t v, int m0, int m1) {
+  if (m0 != 2 && m1 != 2) {
+    if (m0 && m1)
+      *w = v;
+    else if (m0)
+      *reinterpret_cast<uint16_t*>(w) = (uint16_t)v;
+    else if (m1)
+      *(reinterpret_cast<uint16_t*>(w) + 1) = (uint16_t)(v >> 16);
+    return;
+  }
+  uint32_t old = 0;
+  bool known = false;  // old is the word's value, not the zero-fill guess
+  for (;;) {
+    const uint32_t lo = old & 0xFFFFu, hi = old >> 16;
+    const uint32_t vl = v & 0xFFFFu, vh = v >> 16;
+    const uint32_t nl = m0 == 1 ? vl : (m0 == 2 ? umax(lo, vl) : lo);
+    const uint32_t nh = m1 == 1 ? vh : (m1 == 2 ? umax(hi, vh) : hi);
+    const uint32_t nw = nl | (nh << 16);
+    if (known && nw == old) return;
+    const uint32_t prev = atomicCAS(w, old, nw);
+    if (prev == old) return;
+    old = prev;
+    known = true;
   }
 }
 
@@ -718,7 +753,27 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
   s_touch[wave][lane] = touched;
   __syncthreads();
-  {
+  // BF16 entries whose rows start on 4-byte boundaries: one thread per aligned word of two
+  // entries (row-wise: blocks 2k, 2k + 1 of a row; column-wise: columns 2t, 2t + 1)
+  constexpr bool kPairs = sizeof(T) == 2;
+  if (kPairs && p.row_pair) {
+    constexpr int PR = NBLK / 2;  // word pairs per row of the tile (8)
+    const int row = threadIdx.x / PR, k2 = 2 * (threadIdx.x % PR);
+    const int64_t r = r0 + row;
+    int mode[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t bc = c0 + (k2 + h) * kBlockLen;  // the block's first column
+      const int64_t gb = r * p.cols + bc;
+      const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
+      if (row < nrows && bc < p.cols && gb < p.end && ge > p.start)
+        mode[h] = (gb >= p.start && ge <= p.end) ? 1 : 2;
+    }
+    if (mode[0] | mode[1])
+      update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_row) + r * p.ld_ar +
+                                                    (c0 >> 5) + k2),
+                        s_rmax[row][k2] | (s_rmax[row][k2 + 1] << 16), mode[0], mode[1]);
+  } else {
     constexpr int kPer = kBlockLen * NBLK / kThreads;  // row entries per thread (2 or 1)
     T* ptr[kPer];
     uint32_t v[kPer], act = 0;
@@ -741,7 +796,30 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     }
     atomic_max_entries<kPer>(ptr, v, act);
   }
-  if (colw) {
+  if (colw && kPairs && p.col_pair) {
+    const int cc = 2 * threadIdx.x;        // columns cc, cc + 1 within the tile (WC = 512)
+    const int ln = cc / E, q = (cc % E) / 2;  // lane and dword of s_col holding both
+    uint32_t m = 0, t = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerGroup; ++w) {
+      const uint4 o = s_col[w][ln];
+      const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+      m = pk_max_u16(m, ov[q]);
+      t |= s_touch[w][ln];
+    }
+    int mode[2] = {0, 0};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t cg = c0 + cc + h;
+      // the block's first and last elements decide whether the piece holds it whole
+      const int64_t gf = r0 * p.cols + cg, gl = (r0 + nrows - 1) * p.cols + cg;
+      if (cg < p.cols && ((t >> (2 * q + h)) & 1u)) mode[h] = (gf >= p.start && gl < p.end) ? 1 : 2;
+    }
+    if (mode[0] | mode[1])
+      update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_col) + band * p.ld_ac +
+                                                    c0 + cc),
+                        m, mode[0], mode[1]);
+  } else if (colw) {
     constexpr int kPer = WC / kThreads;  // columns per thread (2 or 1)
     T* ptr[kPer];
     uint32_t v[kPer], act = 0;
@@ -1914,6 +1992,10 @@ TileArgs tile_args(const Piece& p, int64_t tile_cols) {
               ((p.ld_ac * esz) % 16 == 0);
   a.row_vec = p.amax_row && (reinterpret_cast<uintptr_t>(p.amax_row) % 16 == 0) &&
               ((p.ld_ar * esz) % 16 == 0);
+  a.row_pair = p.amax_row && (reinterpret_cast<uintptr_t>(p.amax_row) % 4 == 0) &&
+               ((p.ld_ar * esz) % 4 == 0);
+  a.col_pair = p.amax_col && (reinterpret_cast<uintptr_t>(p.amax_col) % 4 == 0) &&
+               ((p.ld_ac * esz) % 4 == 0);
   const uintptr_t virt = reinterpret_cast<uintptr_t>(p.input) - (uintptr_t)(p.start * esz);
   a.in_shift2 = (virt % 4) == 2;
   auto mis = [&](const uint8_t* d) {
