@@ -1391,7 +1391,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
   constexpr uint32_t kFull = (1u << E) - 1;
 
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = threadIdx.x >> 6;
+  // uniform over the wave: row addresses stay in scalar registers, a lane adds its offset
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
   const int k = piece_of(ga, gtile);
   const TileArgs& p = ga.piece[k];
@@ -1436,13 +1437,26 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
   } else {
     load_rows_masked<T, RW>(p, src, v0 + i0, RW, cu, cvalid, d, em);
   }
-  // the two row-wise scale bytes of every row (rows outside the weight read a clamped row;
-  // their elements are outside the fragment)
+  // The two row-wise scale bytes of every row.  In an interior tile every row exists: each is
+  // at a fixed lane offset from the row's first scale byte, a scalar address (the host keeps
+  // the offsets below 2^31).  Edge tiles clamp the rows (rows outside the weight hold no
+  // element of the fragment).
   uint32_t sa[RW], sb[RW];
+  if (interior) {
+    const uint32_t oa = (uint32_t)(offA * p.ld_sr + kA), ob = (uint32_t)(offB * p.ld_sr + kB);
+    const uint8_t* rb = p.scale_row + (v0 + i0) * p.ld_sr;
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    sa[i] = p.scale_row[clamp_row(v0 + i0 + i + offA) * p.ld_sr + kA];
-    sb[i] = p.scale_row[clamp_row(v0 + i0 + i + offB) * p.ld_sr + kB];
+    for (int i = 0; i < RW; ++i) {
+      sa[i] = rb[oa];
+      sb[i] = rb[ob];
+      rb += p.ld_sr;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      sa[i] = p.scale_row[clamp_row(v0 + i0 + i + offA) * p.ld_sr + kA];
+      sb[i] = p.scale_row[clamp_row(v0 + i0 + i + offB) * p.ld_sr + kB];
+    }
   }
   // column-wise scale bytes: every row of the tile uses band B, except the next-row elements
   // of the last virtual row (wave 3, row 7), which belong to band B + 1
@@ -1472,11 +1486,12 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
       store_masked<E>(out, q, em[i]);
   }
   if constexpr (kCol) {
+    int cs[E];
+    unpack_shifts<E>(csp, cs);
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
+      if (i == RW - 1 && wave == kWavesPerGroup - 1 && last_tc) unpack_shifts<E>(csp7, cs);
       if (!em[i]) continue;
-      int cs[E];
-      unpack_shifts<E>(i == RW - 1 ? csp7 : csp, cs);
       uint32_t q[E / 4];
       quantize_chunk<T, kPre>(d[i], cs, true, q);
       uint8_t* out = p.data_col + o0 + i * p.cols;

@@ -18,6 +18,8 @@ bool vec_common_ok(const Piece& p) { return p.cols % (16 / elem_size(p.dtype)) =
 // on a line, and a column-wise output (if any) at the same offset within its lines.
 int64_t line_shift(const Piece& p) {
   if (p.cols % kLineBytes != 0 || !vec_common_ok(p)) return 0;
+  // the tiles address a row's scale bytes by 32-bit lane offsets up to one row further
+  if (p.ld_sr >= (int64_t(1) << 30)) return 0;
   const uintptr_t dr = (reinterpret_cast<uintptr_t>(p.data_row) - (uintptr_t)p.start) % kLineBytes;
   if (dr == 0) return 0;
   if (p.data_col &&
