@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import glob
 import hashlib
 import json
 import os
@@ -42,7 +43,7 @@ HBM_PEAK_GBS = 8000.0
 CAST_SAMPLE = 4  # timed steps per cast-duration sample
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for partial amax + cast"
 KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_partial_amd", "csrc", "kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "writeback_step_bf16_16384x6144_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
@@ -91,6 +92,19 @@ def parse():
                     help="also time a plain device copy (the achievable read + write ceiling, "
                          "and the counter calibration kernel); on by default")
     ap.add_argument("--no-copy-probe", dest="copy_probe", action="store_false")
+    ap.add_argument("--counter-pass", metavar="MANIFEST", default=None,
+                    help="run for a rocprofv3 counter pass: every launch of the step "
+                         "(--warmup + --steps steps) and of the per-call table (--counter-calls "
+                         "eager calls per entry) with no timing, plus the copy probe; writes "
+                         "the launch order (labels, calls, algorithmic bytes) to MANIFEST")
+    ap.add_argument("--counter-calls", type=int, default=4,
+                    help="eager calls per table entry in --counter-pass")
+    ap.add_argument("--summarize-counters", metavar="RUN", default=None,
+                    help="(no GPU) summarize the rocprofv3 passes of --counter-pass runs as "
+                         "markdown: RUN_fetch/ (FETCH_SIZE) and RUN_write/ (WRITE_SIZE), "
+                         "optionally RUN_wrreq/ (TCC_EA0_WRREQ_sum, TCC_EA0_WRREQ_64B_sum), "
+                         "each with its manifest RUN_<pass>.json; to --out")
+    ap.add_argument("--out", default=None)
     return ap.parse_args()
 
 
@@ -183,22 +197,204 @@ def kernel_sha() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def traffic_from_counters(kernel: str):
-    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; None otherwise."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    m = re.search(r"```json\n(.*?)\n```", open(TRAFFIC_FILE).read(), re.S)
+def counter_blocks():
+    """The JSON blocks of the committed rocprofv3 counter summaries (profiles/*_counters.md)."""
+    out = []
+    for f in sorted(glob.glob(os.path.join(PROFILES, "*_counters.md"))):
+        m = re.search(r"```json\n(.*?)\n```", open(f).read(), re.S)
+        if m:
+            out.append(json.loads(m.group(1)))
+    return out
+
+
+def traffic_from_counters(dtype: str, fused: bool, label: str):
+    """Calibrated HBM bytes per launch of the step stage ``label`` (e.g. ``step_cast``) from the
+    committed counter summary of the same step (dtype, fused), if it was taken on the current
+    kernel source; None otherwise."""
+    sha = kernel_sha()
+    for d in counter_blocks():
+        if (d.get("dtype"), d.get("fused")) == (dtype, fused) and \
+                d.get("kernel_source_sha256_16") == sha and label in d.get("hbm_bytes_per_launch", {}):
+            return d["hbm_bytes_per_launch"][label]
+    return None
+
+
+def _counter_dispatches(d):
+    """The dispatches of one rocprofv3 --pmc run (output directory ``d``), in dispatch order:
+    kernel name, grid, workgroup and the summed value of each counter."""
+    import csv
+
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {files}")
+    disp = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            e = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                        "grid": int(r["Grid_Size"]),
+                                                        "wg": int(r["Workgroup_Size"]), "c": {}})
+            e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return [disp[k] for k in sorted(disp)]
+
+
+def _short_kernel(name: str) -> str:
+    m = re.search(r"(\w+_kernel)<([^()]*)>", name)
     if not m:
-        return None
-    d = json.loads(m.group(1))
-    if d.get("kernel_source_sha256_16") != kernel_sha():
-        return None
-    return d.get("hbm_bytes_per_launch", {}).get(kernel)
+        return name.split("(")[0][-60:]
+    a = [x.strip() for x in m.group(2).split(",")]
+    t = {"unsigned short": "bf16", "unsigned int": "fp32"}.get(a[0], a[0])
+    rest = ", ".join(a[1:])
+    return f"{m.group(1)}<{t}{', ' + rest if rest else ''}>"
+
+
+def _attribute(man, disp):
+    """Splits the library's dispatches (namespace mxfp8) into the manifest's items (runs of
+    consecutive dispatches of one kernel) and finds the copy probe's launches; checks the
+    counts."""
+    runs = []
+    for i, d in enumerate(disp):
+        if "mxfp8::" not in d["name"]:
+            continue
+        if runs and runs[-1][-1] == i - 1 and disp[i - 1]["name"] == d["name"]:
+            runs[-1].append(i)
+        else:
+            runs.append([i])
+    items = man["items"]
+    if len(runs) != len(items):
+        raise SystemExit(f"{len(runs)} runs of library launches, {len(items)} manifest items")
+    for it, r in zip(items, runs):
+        if len(r) % it["calls"]:
+            raise SystemExit(f"{it['label']}: {len(r)} launches for {it['calls']} calls")
+    # the copy probe: the first copy launches after the step's last launch, back to back
+    n_step = sum(1 for it in items if it["label"].startswith("step_"))
+    lo = runs[n_step - 1][-1]
+    hi = runs[n_step][0] if n_step < len(runs) else len(disp)
+    cp = [i for i in range(lo + 1, hi) if "copyBuffer" in disp[i]["name"]]
+    probe = cp[:man["copy_probe"]["launches"]]
+    if len(probe) != man["copy_probe"]["launches"] or probe[-1] - probe[0] != len(probe) - 1 or \
+            len({(disp[i]["grid"], disp[i]["wg"]) for i in probe}) != 1:
+        raise SystemExit("copy probe: expected "
+                         f"{man['copy_probe']['launches']} consecutive copies of one shape")
+    return runs, probe
+
+
+COUNTER_PASSES = (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
+                  ("wrreq", "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum"))
+
+
+def summarize_counters(args):
+    """Markdown summary of the counter passes of one --counter-pass workload (``RUN_fetch``,
+    ``RUN_write`` and optionally ``RUN_wrreq``, each a rocprofv3 output directory next to the
+    manifest its run wrote): calibrated HBM bytes per call of every item against its
+    algorithmic bytes, and the JSON block ``traffic_from_counters`` reads."""
+    run = args.summarize_counters
+    kinds = [k for k, _ in COUNTER_PASSES if os.path.isdir(f"{run}_{k}")]
+    if "fetch" not in kinds or "write" not in kinds:
+        raise SystemExit(f"need {run}_fetch/ and {run}_write/")
+    mans = {k: json.load(open(f"{run}_{k}.json")) for k in kinds}
+    man = mans["fetch"]
+    for k in kinds:
+        if [(i["label"], i["calls"]) for i in mans[k]["items"]] != \
+                [(i["label"], i["calls"]) for i in man["items"]] or \
+                mans[k]["kernel_source_sha256_16"] != man["kernel_source_sha256_16"]:
+            raise SystemExit(f"the {k} pass ran other launches or another kernel source")
+    passes = {k: _counter_dispatches(f"{run}_{k}") for k in kinds}
+    att = {k: _attribute(man, v) for k, v in passes.items()}
+
+    def per_call(kind, counter, idx_run, calls):
+        disp = passes[kind]
+        vals = [disp[i]["c"][counter] for i in idx_run]
+        lpc = len(vals) // calls
+        return statistics.median(sum(vals[j * lpc:(j + 1) * lpc]) for j in range(calls)), lpc
+
+    nb_kib = man["copy_probe"]["read_bytes"] / 1024
+    f_probe = statistics.median(passes["fetch"][i]["c"]["FETCH_SIZE"] for i in att["fetch"][1])
+    w_probe = statistics.median(passes["write"][i]["c"]["WRITE_SIZE"] for i in att["write"][1])
+    ff, wf = nb_kib / f_probe, (man["copy_probe"]["write_bytes"] / 1024) / w_probe
+
+    seen = {}
+    for k, it in enumerate(man["items"]):
+        seen.setdefault(it["label"], []).append(k)
+    rows, blob = [], {}
+    for label, ks in seen.items():
+        it = man["items"][ks[0]]
+
+        def med(kind, counter):
+            return statistics.median(per_call(kind, counter, att[kind][0][k], it["calls"])[0]
+                                     for k in ks)
+        fk, wk = med("fetch", "FETCH_SIZE"), med("write", "WRITE_SIZE")
+        lpc = per_call("fetch", "FETCH_SIZE", att["fetch"][0][ks[0]], it["calls"])[1]
+        kname = _short_kernel(passes["fetch"][att["fetch"][0][ks[0]][0]]["name"])
+        rd, wr = fk * 1024 * ff, wk * 1024 * wf
+        w64 = None
+        if "wrreq" in passes:
+            tot = med("wrreq", "TCC_EA0_WRREQ_sum")
+            w64 = med("wrreq", "TCC_EA0_WRREQ_64B_sum") / tot if tot else float("nan")
+        rows.append((label, kname, lpc, len(ks) * it["calls"], fk, wk, rd, wr, it["alg_bytes"],
+                     w64))
+        blob[label] = int(round((rd + wr) / lpc))
+
+    has_w = "wrreq" in passes
+    hdr = ("| item | kernel | launches per call | calls | FETCH_SIZE KiB per call | "
+           "WRITE_SIZE KiB per call | HBM read MB | HBM write MB | total MB | algorithmic MB | "
+           "total / algorithmic |" + (" 64-byte share of write requests |" if has_w else ""))
+    lines = [hdr, "|" + "---|" * (hdr.count("|") - 1)]
+    for label, kname, lpc, n, fk, wk, rd, wr, alg, w64 in rows:
+        lines.append(f"| {label} | `{kname}` | {lpc} | {n} | {fk:.0f} | {wk:.0f} | "
+                     f"{rd / 1e6:.2f} | {wr / 1e6:.2f} | {(rd + wr) / 1e6:.2f} | {alg / 1e6:.2f} | "
+                     f"{(rd + wr) / alg:.4f} |" + (f" {w64:.4f} |" if has_w else ""))
+    workload = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
+                + ("fused scales + cast" if man["fused"] else "scales then cast"))
+    block = {"workload": workload, "dtype": man["dtype"], "fused": man["fused"],
+             "kernel_source_sha256_16": man["kernel_source_sha256_16"],
+             "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+             "hbm_bytes_per_launch": blob}
+    argv = list(man["argv"])
+    j = argv.index("--counter-pass")
+    del argv[j:j + 2]
+    name = os.path.basename(run)
+    cmds = [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 600 rocprofv3 --pmc {ctr} "
+            f"--output-format csv -d $R/gpurun_out/cnt/{name}_{k} -o p -- python -u "
+            f"$R/bench.py {' '.join(argv)} --counter-pass $R/gpurun_out/cnt/{name}_{k}.json"
+            for k, ctr in COUNTER_PASSES if k in kinds]
+    table_note = ("" if "--no-kernel-table" in argv else
+                  "  Items other than `step_*` are the per-call table's entries at 16384x6144 "
+                  "(full input, the quarter fragment at offset 17, `partial_own`: the quarter in "
+                  "a rank's own input and fragment-sized output allocations, `full_rowonly`: "
+                  "column-wise outputs absent), each as eager calls rotating over its buffer "
+                  "sets.")
+    md = [f"# HBM traffic per call: rocprofv3 counters, {workload}", "",
+          "One MI355X (gfx950), ROCm 7.2.  `bench.py --counter-pass` runs every launch untimed "
+          "in a fixed order and writes that order to a manifest; each counter set is a "
+          "rocprofv3 run of its own ($R is the repository root):", "", "```", *cmds, "```", "",
+          f"This summary is `python bench.py --summarize-counters gpurun_out/cnt/{name} --out "
+          f"<this file>`, which splits each run's library dispatches into the manifest's items "
+          "(runs of one kernel) and checks the counts." + table_note, "",
+          f"Calibration: the copy probe (torch `copy_` of 256 MiB, `__amd_rocclr_copyBuffer`) "
+          f"reads {f_probe:.0f} KiB of FETCH_SIZE and {w_probe:.0f} KiB of WRITE_SIZE per launch "
+          f"for {nb_kib:.0f} KiB read and written: fetch factor {ff:.4f}, write factor {wf:.4f}.",
+          "",
+          "Per call: the median over the item's calls of the sum over the call's launches.  "
+          "Algorithmic bytes follow `mxfp8_block_scaled_partial_amd/bytes_model.py` (the input "
+          "once, touched amax entries or scale bytes once, one E4M3 byte per element and "
+          "direction).  A ratio near 1.00 means no re-reads and no staging traffic." +
+          (" The last column is the share of HBM write requests (TCC_EA0_WRREQ) that are whole "
+           "64-byte requests." if has_w else ""), "", *lines, "",
+          "`bench.py` reads `roofline.traffic` from this block while the kernel source hash "
+          "matches:", "", "```json", json.dumps(block, indent=1), "```", ""]
+    text = "\n".join(md)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        print(text)
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the writeback runs on a single MI355X "
@@ -287,6 +483,10 @@ def main():
         if cast_ev is not None:
             cast_ev[1].record()
 
+    if args.counter_pass:
+        counter_pass(args, step, stage_names, stage_bytes, m, dev)
+        return
+
     log(f"warmup {args.warmup} steps")
     for i in range(max(2, args.warmup)):
         step(i)
@@ -342,7 +542,7 @@ def main():
     cast_launch_us = cast_ms_mean * 1e3 / n_cast
     cast_bytes_launch = stage_bytes[cast_stage] / n_cast
     achieved = cast_bytes_launch / (cast_launch_us * 1e-6) / 1e9
-    traffic = traffic_from_counters(kname) if args.dtype == "bf16" else None
+    traffic = traffic_from_counters(args.dtype, bool(args.fused), "step_" + cast_stage)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname,
@@ -387,27 +587,7 @@ def main():
             "shared_buffer": single_pass_step(args, sets, spec, frags, s_in, dev, tdt, True)}
 
     if args.copy_probe:
-        # a plain device-to-device copy of known size (256 MiB per launch, rotating over four
-        # buffer pairs so it streams from HBM): the achievable read+write ceiling on this machine,
-        # and the kernel the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are calibrated on
-        nb = 256 << 20
-        pairs = [(torch.empty(nb, dtype=torch.uint8, device=dev),
-                  torch.empty(nb, dtype=torch.uint8, device=dev)) for _ in range(4)]
-        for a, b in pairs:
-            b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = TimingEvent(), TimingEvent()
-        reps = 20
-        e0.record()
-        for i in range(reps):
-            a, b = pairs[i % 4]
-            b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        out["copy_probe"] = {"bytes_per_launch": 2 * nb, "read_bytes": nb, "write_bytes": nb,
-                             "us": round(us, 2), "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
-        del pairs
+        out["copy_probe"] = copy_probe(dev)
 
     if args.kernel_table:
         out["kernels"], out["kernels_other_shapes"] = kernel_table(args, m, dev)
@@ -431,6 +611,66 @@ def main():
         out["cpu_baseline"] = cpu
 
     print(json.dumps(out), flush=True)
+
+
+COPY_PROBE_BYTES = 256 << 20
+COPY_PROBE_LAUNCHES = 24
+
+
+def copy_probe(dev):
+    """A plain device-to-device copy of known size (256 MiB per launch, rotating over four
+    buffer pairs so it streams from HBM): the achievable read + write ceiling on this machine, and
+    the kernel the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are calibrated on.  24 launches:
+    4 untimed, then 20 between HIP events."""
+    import torch
+
+    nb = COPY_PROBE_BYTES
+    pairs = [(torch.empty(nb, dtype=torch.uint8, device=dev),
+              torch.empty(nb, dtype=torch.uint8, device=dev)) for _ in range(4)]
+    for a, b in pairs:
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = TimingEvent(), TimingEvent()
+    reps = COPY_PROBE_LAUNCHES - 4
+    e0.record()
+    for i in range(reps):
+        a, b = pairs[i % 4]
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del pairs
+    return {"bytes_per_launch": 2 * nb, "read_bytes": nb, "write_bytes": nb,
+            "us": round(us, 2), "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
+
+
+def counter_pass(args, step, stage_names, stage_bytes, m, dev):
+    """The launches a rocprofv3 counter pass attributes, untimed and in a fixed order: the
+    step (every stage but the zero-fill, which is torch's), the copy probe, then (unless
+    --no-kernel-table) every entry of the per-call table as ``--counter-calls`` eager calls
+    rotating over its buffer sets.  Writes the order to the manifest: consecutive launches of
+    one library kernel form one item, so ``summarize_counters`` can attribute each dispatch."""
+    import torch
+
+    items = []
+    lib_stages = [s for s in stage_names if s != "zero"]
+    for i in range(max(2, args.warmup) + args.steps):
+        step(i)
+        items += [{"label": f"step_{s}", "calls": 1, "alg_bytes": int(stage_bytes[s])}
+                  for s in lib_stages]
+    torch.cuda.synchronize()
+    copy_probe(dev)
+    if args.kernel_table:
+        kernel_table(args, m, dev, items)
+    torch.cuda.synchronize()
+    man = {"argv": sys.argv[1:], "dtype": args.dtype, "fused": bool(args.fused),
+           "kernel_source_sha256_16": kernel_sha(),
+           "copy_probe": {"launches": COPY_PROBE_LAUNCHES, "read_bytes": COPY_PROBE_BYTES,
+                          "write_bytes": COPY_PROBE_BYTES},
+           "items": items}
+    with open(args.counter_pass, "w") as f:
+        json.dump(man, f, indent=1)
+    log(f"counter pass: {len(items)} items -> {args.counter_pass}")
 
 
 def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
@@ -784,7 +1024,7 @@ def graph_step_us(args, step_fns):
     return round(us, 2)
 
 
-def kernel_table(args, m_default, dev):
+def kernel_table(args, m_default, dev, items=None):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
     scales + cast and (full input only) the single-pass quantize, for every matrix of that
     table (16384x6144, 4096x4096, 1024x1024, 160x96): full input and the quarter fragment
@@ -795,7 +1035,8 @@ def kernel_table(args, m_default, dev):
     matrices; partial runs: quarter-size fragments placed so that input - 17 elements stays
     16-byte aligned): the two large matrices stream from HBM, the small ones stay in the 256 MB
     Infinity Cache like any repeated small call.  Returns the 16384x6144 entries and, by
-    shape, the others."""
+    shape, the others.  With ``items`` (a counter pass) nothing is timed: each entry makes
+    ``--counter-calls`` eager calls and appends its manifest item."""
     import torch
 
     from mxfp8_block_scaled_partial_amd import workloads as wl
@@ -812,7 +1053,7 @@ def kernel_table(args, m_default, dev):
                     m = wl.matrix_large(dtype)
             else:  # N(0,1) times a per-column 2^U[-8, 8], the 4096x4096 recipe
                 m = wl.matrix_square(dtype, rows=rows, cols=cols)
-            entries = time_shape(args, m, dev)
+            entries = time_shape(args, m, dev, items)
             if (rows, cols) == (16384, 6144):
                 table.update(entries)
             else:
@@ -821,7 +1062,7 @@ def kernel_table(args, m_default, dev):
     return table, by_shape
 
 
-def time_shape(args, m, dev):
+def time_shape(args, m, dev, items=None):
     """The table's entries for one matrix in one dtype (see ``kernel_table``)."""
     import numpy as np
     import torch
@@ -892,6 +1133,13 @@ def time_shape(args, m, dev):
         if run == "full":
             kernels.append(("quantize", fused_p, B.mxfp8_quantize))
         for kname, pieces, fn in kernels:
+            if items is not None:
+                for i in range(args.counter_calls):
+                    fn(pieces[i % n_sets])
+                torch.cuda.synchronize()
+                items.append({"label": f"{kname}_{dtype}_{run}", "calls": args.counter_calls,
+                              "alg_bytes": int(pb[kname])})
+                continue
             for i in range(3):
                 fn(pieces[i % n_sets])
             torch.cuda.synchronize()
