@@ -83,8 +83,9 @@ def test_counter_summary_attributes_dispatches_to_the_manifest(tmp_path):
     disp = []
     for _ in range(2):
         disp += step
-    disp += [(copy, 1, 1024, kib / 4, kib / 4)]  # a set-up copy of another shape
     disp += [(copy, 131072, 512, kib / 2, kib)] * 24
+    # the table's set-up copy right behind the probe, of the same launch shape
+    disp += [(copy, 131072, 512, kib / 4, kib / 2)]
     # two calls of two launches each (two buckets)
     disp += [(cast, 50, 256, 1000, 1000), (cast, 50, 256, 1000, 1000)] * 2
     for k, ctr, idx in (("fetch", "FETCH_SIZE", 3), ("write", "WRITE_SIZE", 4)):
