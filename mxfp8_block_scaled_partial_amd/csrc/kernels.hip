@@ -186,6 +186,27 @@ __device__ __forceinline__ int piece_of(const GroupArgs& g, int64_t t) {
 
 // ------------------------------------------------------------------ amax entries
 
+// Global memory at an address computed as an integer (a pointer masked to its dword).  A plain
+// pointer made from an integer is a generic one, and generic (flat) accesses count against the
+// LDS / scalar-load counter as well, so that every wait for one also waits for the others;
+// these are global accesses.
+typedef __attribute__((address_space(1))) const uint32_t global_cu32;
+typedef __attribute__((address_space(1))) uint32_t global_u32;
+
+__device__ __forceinline__ global_u32* global_dword(uintptr_t a) {
+  return reinterpret_cast<global_u32*>(a & ~uintptr_t(3));
+}
+__device__ __forceinline__ global_cu32* global_cdword(uintptr_t a) {
+  return reinterpret_cast<global_cu32*>(a & ~uintptr_t(3));
+}
+
+// Compare-and-swap of a global dword; returns the value it found.
+__device__ __forceinline__ uint32_t global_cas(global_u32* w, uint32_t expected, uint32_t desired) {
+  __hip_atomic_compare_exchange_strong(w, &expected, desired, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return expected;
+}
+
 // Atomic max into N amax entries at once; bit i of `active` selects entry i.  Amax values are
 // non-negative, so unsigned order on the bit patterns is float order.  FP32 entries use the
 // hardware's unsigned atomic max, which returns nothing to wait for.
@@ -203,14 +224,14 @@ __device__ __forceinline__ void atomic_max_entries(uint32_t* const (&p)[N],
 template <int N>
 __device__ __forceinline__ void atomic_max_entries(uint16_t* const (&p)[N],
                                                    const uint32_t (&v)[N], uint32_t active) {
-  uint32_t* w[N];
+  global_u32* w[N];
   int sh[N];
   uint32_t old[N];
   uint32_t pending = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     const uintptr_t a = reinterpret_cast<uintptr_t>(p[i]);
-    w[i] = reinterpret_cast<uint32_t*>(a & ~uintptr_t(3));
+    w[i] = global_dword(a);
     sh[i] = (a & 2) ? 16 : 0;
     old[i] = 0;
     if ((active >> i) & 1u) old[i] = __hip_atomic_load(w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -223,7 +244,7 @@ __device__ __forceinline__ void atomic_max_entries(uint16_t* const (&p)[N],
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if ((pending >> i) & 1u)
-        prev[i] = atomicCAS(w[i], old[i], (old[i] & ~(0xFFFFu << sh[i])) | (v[i] << sh[i]));
+        prev[i] = global_cas(w[i], old[i], (old[i] & ~(0xFFFFu << sh[i])) | (v[i] << sh[i]));
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       if (!((pending >> i) & 1u)) continue;
@@ -261,7 +282,7 @@ __device__ __forceinline__ void update_entry_pair(uint32_t* w, uint32_t v, int m
     const uint32_t nh = m1 == 1 ? vh : (m1 == 2 ? umax(hi, vh) : hi);
     const uint32_t nw = nl | (nh << 16);
     if (known && nw == old) return;
-    const uint32_t prev = atomicCAS(w, old, nw);
+    const uint32_t prev = global_cas(global_dword(reinterpret_cast<uintptr_t>(w)), old, nw);
     if (prev == old) return;
     old = prev;
     known = true;
@@ -442,14 +463,14 @@ __device__ __forceinline__ void load_rows(const T* src, int64_t cols, bool shift
     // lane 63's next dword (p + 14 for a chunk at p = 2 mod 4: dword-aligned).  The mask keeps
     // the compiler from folding the 14 into the instruction offset of a scalar load, whose
     // hardware drops the two low bits of the base address before adding the offset.
-    const uint8_t* t63 = reinterpret_cast<const uint8_t*>((a63 + 14) & ~uint64_t(3));
+    const uint64_t t63 = a63 + 14;
     uint32_t tail[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       if (i < n) {
         raw[i].v = __builtin_nontemporal_load(
             reinterpret_cast<const v4u*>(reinterpret_cast<const uint8_t*>(src + i * cols) - 2));
-        tail[i] = *reinterpret_cast<const uint32_t*>(t63 + i * cols * (int64_t)sizeof(T));
+        tail[i] = *global_cdword(t63 + i * cols * (int64_t)sizeof(T));
       }
     }
     const bool top = (threadIdx.x & (kWaveSize - 1)) == kWaveSize - 1;
@@ -480,63 +501,112 @@ __device__ __forceinline__ void load_rows(const T* src, int64_t cols, bool shift
   }
 }
 
-// Chunk g whose elements a fragment boundary cuts: the fragment's elements, one load each,
-// into el (the others 0); returns the element mask.  Nothing here uses a loaded value.
+// Chunk g's elements in `mask` (a chunk that a fragment boundary cuts; 0: no such chunk), as
+// raw dwords for assemble_chunk: the dwords of the chunk's window (4, or 5 for a BF16 input 2
+// bytes off a dword) that hold an element of the mask are loaded; every other dword re-reads
+// the first of those (dropped by masked_chunk), and without a mask all of them read the dword
+// holding the fragment's first element.  A load never reaches a dword without an element of the
+// fragment, so it stays inside the caller's allocation.  The loads go out unconditionally: a load
+// under a per-lane condition lets the compiler place the first use of its value, and with it a
+// wait for every load in flight, inside the condition.
 template <typename T>
-__device__ __forceinline__ uint32_t issue_masked(const TileArgs& p, int64_t g,
-                                                 uint32_t (&el)[Chunk<T>::E]) {
-  constexpr int E = Chunk<T>::E;
-  uint32_t mask = 0;
+__device__ __forceinline__ void issue_masked(const TileArgs& p, int64_t g, uint32_t mask,
+                                             RawChunk& r) {
+  const bool s2 = sizeof(T) == 2 && p.in_shift2;
+  const uint8_t* a =
+      static_cast<const uint8_t*>(p.input) + (mask ? (g - p.start) * (int64_t)sizeof(T) : 0);
+  global_cu32* w = global_cdword(reinterpret_cast<uintptr_t>(a));
+  uint32_t hold = 0;  // bit j: dword j of the window holds an element of the mask
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int64_t i = g + e;
-    el[e] = 0;
-    if (i >= p.start && i < p.end) {
-      el[e] = load_raw(p.input, i - p.start, (int)sizeof(T));
-      mask |= 1u << e;
-    }
+  for (int j = 0; j < 5; ++j) {
+    uint32_t el;  // the elements dword j holds
+    if constexpr (sizeof(T) == 4)
+      el = j < 4 ? 1u << j : 0u;
+    else
+      el = s2 ? (3u << (2 * j)) >> 1 : (j < 4 ? 3u << (2 * j) : 0u);
+    hold |= (mask & el) ? 1u << j : 0u;
   }
-  return mask;
+  const int jf = hold ? __builtin_ctz(hold) : 0;
+  uint32_t v[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) v[j] = (j < 4 || s2) ? w[((hold >> j) & 1u) ? j : jf] : 0u;
+  r.v = v4u{v[0], v[1], v[2], v[3]};
+  r.t = v[4];
 }
 
+// The assembled chunk d with the elements outside `mask` set to 0.
 template <typename T>
-__device__ __forceinline__ void assemble_masked(const uint32_t (&el)[Chunk<T>::E],
-                                                uint32_t (&d)[4]) {
-  if constexpr (sizeof(T) == 2) {
+__device__ __forceinline__ void masked_chunk(uint32_t mask, uint32_t (&d)[4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[j] = el[2 * j] | (el[2 * j + 1] << 16);
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) d[j] = el[j];
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (sizeof(T) == 2)
+      d[j] &= (((mask >> (2 * j)) & 1u) ? 0xFFFFu : 0u) |
+              (((mask >> (2 * j + 1)) & 1u) ? 0xFFFF0000u : 0u);
+    else
+      d[j] = ((mask >> j) & 1u) ? d[j] : 0u;
   }
 }
 
-// Rows i < nrows_here of an edge tile: chunk i of the wave's rows, masked to the fragment, in
-// d, with per-row element masks in em.  The whole chunks' loads go out first, then the element
-// loads of the chunks a fragment boundary cuts (a lane has at most two: the fragment's start
-// and end), and only then is anything assembled.  Chunks start at flat indices congruent to
+// Which of an edge tile's rows hold a whole chunk of the fragment, which (at most two: the
+// fragment's start and end) a chunk that a fragment boundary cuts, and each row's element
+// mask; from the bounds alone, so a caller can issue other loads before the rows'.
+template <int RW>
+struct RowClass {
+  uint32_t full;      // bit i: row i's chunk lies wholly inside the fragment
+  int cut0, cut1;     // rows whose chunk a fragment boundary cuts (-1: none)
+  uint32_t m0, m1;    // their element masks (0: none)
+  uint32_t em[RW];    // element masks of all rows
+};
+
+// Element mask of chunk g within [start, end).
+template <int E>
+__device__ __forceinline__ uint32_t chunk_mask(const TileArgs& p, int64_t g) {
+  const int lo = (int)max<int64_t>(0, min<int64_t>(E, p.start - g));  // first element inside
+  const int hi = (int)max<int64_t>(0, min<int64_t>(E, p.end - g));    // one past the last
+  return ((1u << hi) - 1) & ~((1u << lo) - 1);
+}
+
+// Rows i < nrows_here of the wave, chunk column c.  Chunks start at flat indices congruent to
 // p.shift modulo E (0 except in the line-owned cast tiles); c may then pass the row's end.
 template <typename T, int RW>
-__device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
-                                                 int nrows_here, int64_t c, bool cvalid,
-                                                 uint32_t (&d)[RW][4], uint32_t (&em)[RW]) {
+__device__ __forceinline__ RowClass<RW> classify_rows(const TileArgs& p, int64_t rfirst,
+                                                      int nrows_here, int64_t c, bool cvalid) {
   constexpr int E = Chunk<T>::E;
-  uint32_t full = 0;      // bit i: row i's chunk lies wholly inside the fragment
-  int cut0 = -1, cut1 = -1;  // rows whose chunk a fragment boundary cuts
+  RowClass<RW> k;
+  k.full = 0;
+  k.cut0 = k.cut1 = -1;
+  k.m0 = k.m1 = 0;
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
+    k.em[i] = 0;
     if (i < nrows_here && cvalid) {
       const int64_t g = (rfirst + i) * p.cols + c;
       if (g >= p.start && g + E <= p.end) {
-        full |= 1u << i;
+        k.full |= 1u << i;
+        k.em[i] = (1u << E) - 1;
       } else if (g + E > p.start && g < p.end) {
-        if (cut0 < 0)
-          cut0 = i;
-        else
-          cut1 = i;
+        k.em[i] = chunk_mask<E>(p, g);
+        if (k.cut0 < 0) {
+          k.cut0 = i;
+          k.m0 = k.em[i];
+        } else {
+          k.cut1 = i;
+          k.m1 = k.em[i];
+        }
       }
     }
   }
+  return k;
+}
+
+// Rows of an edge tile (as classified), masked to the fragment, in d (elements outside it
+// are 0).  The whole chunks' loads go out first, then the element loads of the cut chunks, and
+// only then is anything assembled.
+template <typename T, int RW>
+__device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
+                                                 int64_t c, const RowClass<RW>& k,
+                                                 uint32_t (&d)[RW][4]) {
+  constexpr int E = Chunk<T>::E;
   // Every lane issues every row's chunk load, rows without a whole chunk reading the
   // fragment's first whole chunk instead (discarded): a load under a per-lane condition would
   // make the compiler wait for it where the branches join.  That chunk starts at the first
@@ -550,32 +620,25 @@ __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src
     const T* whole = static_cast<const T*>(p.input) + (g_whole - p.start);
 #pragma unroll
     for (int i = 0; i < RW; ++i)
-      issue_chunk(((full >> i) & 1u) ? src + i * p.cols : whole, p.in_shift2, raw[i]);
+      issue_chunk(((k.full >> i) & 1u) ? src + i * p.cols : whole, p.in_shift2, raw[i]);
   }
-  uint32_t el0[E], el1[E], m0 = 0, m1 = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) el0[e] = el1[e] = 0;
-  if (cut0 >= 0) m0 = issue_masked<T>(p, (rfirst + cut0) * p.cols + c, el0);
-  if (cut1 >= 0) m1 = issue_masked<T>(p, (rfirst + cut1) * p.cols + c, el1);
+  RawChunk cr0, cr1;
+  issue_masked<T>(p, (rfirst + max(k.cut0, 0)) * p.cols + c, k.m0, cr0);
+  issue_masked<T>(p, (rfirst + max(k.cut1, 0)) * p.cols + c, k.m1, cr1);
   uint32_t c0d[4], c1d[4];
-  assemble_masked<T>(el0, c0d);
-  assemble_masked<T>(el1, c1d);
+  assemble_chunk(cr0, p.in_shift2, c0d);
+  assemble_chunk(cr1, p.in_shift2, c1d);
+  masked_chunk<T>(k.m0, c0d);
+  masked_chunk<T>(k.m1, c1d);
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
-    const bool whole = (full >> i) & 1u;
+    const bool whole = (k.full >> i) & 1u;
     assemble_chunk(raw[i], p.in_shift2, d[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d[i][j] = whole ? d[i][j] : 0u;
-    em[i] = whole ? (1u << E) - 1 : 0u;
-    if (i == cut0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[i][j] = c0d[j];
-      em[i] = m0;
-    }
-    if (i == cut1) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) d[i][j] = c1d[j];
-      em[i] = m1;
+    for (int j = 0; j < 4; ++j) {
+      d[i][j] = whole ? d[i][j] : 0u;
+      d[i][j] = i == k.cut0 ? c0d[j] : d[i][j];
+      d[i][j] = i == k.cut1 ? c1d[j] : d[i][j];
     }
   }
 }
@@ -741,8 +804,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   // in LDS and all 256 threads then write the touched entries, at most two of each kind per
   // thread: blocks the piece holds whole are stored, blocks a fragment boundary cuts are
   // merged atomically (all reads, then all swaps).
-  uint32_t em[RW];
-  load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
+  const RowClass<RW> rc = classify_rows<T, RW>(p, r0 + i0, nrows - i0, c, cvalid);
+  const uint32_t(&em)[RW] = rc.em;
+  load_rows_masked<T, RW>(p, src, r0 + i0, c, rc, d);
   uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
 #pragma unroll
   for (int i = 0; i < RW; ++i) {
@@ -1060,42 +1124,49 @@ __device__ __forceinline__ void store_col_scales(const TileArgs& p, int64_t band
   store_scale_bytes<E>(p.scale_col + band * p.ld_sc + c, sb, m);
 }
 
-// Not fused: the column-wise exponent shifts of the lane's E columns, 127 minus the scale
-// bytes, read as one vector when scale_col rows are aligned to E bytes, else one by one.  The
-// values are used at once, so the caller issues this after the tile's other loads: the wait
-// then covers them all.
+// Not fused: the column-wise scale bytes of the lane's E columns, as loaded: one vector when
+// scale_col rows are aligned to E bytes (cw[0 .. E/4) hold the packed bytes), else one load
+// per byte (cw[e]).  col_shifts_of turns them into exponent shifts once they have arrived.
 template <typename T>
-__device__ __forceinline__ void col_shifts(const TileArgs& p, int64_t band, int64_t c,
-                                           int (&cshift)[Chunk<T>::E]) {
+__device__ __forceinline__ void col_scale_raw(const TileArgs& p, int64_t band, int64_t c,
+                                              uint32_t (&cw)[Chunk<T>::E]) {
   constexpr int E = Chunk<T>::E;
   const uint8_t* sc = p.scale_col + band * p.ld_sc + c;
-  uint32_t b[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) cw[e] = 0;
   if (p.sc_vec) {
-    uint32_t w[E / 4];
     if constexpr (E == 8) {
       const uint2 v = *reinterpret_cast<const uint2*>(sc);
-      w[0] = v.x;
-      w[1] = v.y;
+      cw[0] = v.x;
+      cw[1] = v.y;
     } else {
-      w[0] = *reinterpret_cast<const uint32_t*>(sc);
+      cw[0] = *reinterpret_cast<const uint32_t*>(sc);
     }
-#pragma unroll
-    for (int e = 0; e < E; ++e) b[e] = (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
   } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) b[e] = sc[e];
+    for (int e = 0; e < E; ++e) cw[e] = sc[e];
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) cshift[e] = 127 - (int)b[e];
 }
 
-// Tiles a fragment boundary or the short last band cuts, and tiles whose outputs are not
-// dword aligned: masked loads, byte stores or window stores.  The common tile (interior,
-// dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.
-template <typename T, bool kCol, bool kPre, bool kFuse>
+template <typename T>
+__device__ __forceinline__ void col_shifts_of(const TileArgs& p, const uint32_t (&cw)[Chunk<T>::E],
+                                              int (&cshift)[Chunk<T>::E]) {
+  constexpr int E = Chunk<T>::E;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    cshift[e] = 127 - (int)(p.sc_vec ? (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu : cw[e]);
+}
+
+// Tiles a fragment boundary or the short last band cuts (kEdge: masked loads and stores), and
+// interior tiles whose outputs are not dword aligned (window stores).  The common tile
+// (interior, dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.  The
+// two kinds are separate instances, so that no edge tile's code follows a join with loads that
+// an interior tile would have in flight (the compiler would wait for those too).
+template <typename T, bool kCol, bool kPre, bool kFuse, bool kEdge>
 __device__ __forceinline__ void cast_tile_general(
-    const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows, bool interior,
+    const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows,
     int (&cshift)[Chunk<T>::E], bool colw) {
+  constexpr bool interior = !kEdge;
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave;
@@ -1110,7 +1181,14 @@ __device__ __forceinline__ void cast_tile_general(
   const int64_t o0 = (r0 + i0) * p.cols + c - p.start;
   uint32_t d[RW][4], em[RW];
   int rshift[RW];
-  if (interior) {
+  // Every load of the tile goes out before any value is used: the input rows (interior tiles
+  // here; edge tiles, once classified, after the scale loads: the assembly in load_rows_masked
+  // then waits for them all), the row-wise scale bytes or (fused) amax entries, and (not
+  // fused) the column-wise scale bytes.  The scale loads are unconditional, a lane that needs
+  // none reading the tile's first one (dropped): a load under a per-lane condition makes the
+  // compiler wait for it where the branches join.
+  RowClass<RW> rc;
+  if constexpr (interior) {
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       d[i][0] = d[i][1] = d[i][2] = d[i][3] = 0;
@@ -1118,47 +1196,44 @@ __device__ __forceinline__ void cast_tile_general(
     }
     if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, c0 + WC <= p.cols);
   } else {
-    load_rows_masked<T, RW>(p, src, r0 + i0, nrows - i0, c, cvalid, d, em);
-  }
-  // (not fused) the column-wise loads go out after the row-wise ones: their use then waits for
-  // every load of the tile at once
-  if constexpr (kFuse) {
-    // the first lane of each row-wise block writes the scale of a block the fragment
-    // touches; every amax entry is loaded before the first store, so no load waits on one
-    uint32_t ab[RW];
-    bool wr[RW];
+    rc = classify_rows<T, RW>(p, r0 + i0, nrows - i0, c, cvalid);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
+    for (int i = 0; i < RW; ++i) em[i] = rc.em[i];
+    // fused: the rows first, which keeps the column-wise amax entries' registers free sooner
+    if constexpr (kFuse) load_rows_masked<T, RW>(p, src, r0 + i0, c, rc, d);
+  }
+  uint32_t rl[RW];  // row-wise scale bytes or (fused) amax entries, as loaded
+  bool wr[RW];      // (fused) the lane writes row i's scale byte
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if constexpr (kFuse) {
+      // the first lane of each row-wise block writes the scale of a block the fragment touches
       wr[i] = (lane & (kBlockLen / E - 1)) == 0 && cvalid && i < nrows - i0 &&
               (interior || row_block_touched(p, r0 + i0 + i, c));
-      // unconditional (an entry the lane does not need is read at the band's first row and
-      // the tile's first column, then dropped): a load under a per-lane condition makes the
-      // compiler wait for it where the branches join
       const bool need = em[i] || wr[i];
-      const uint32_t v = row_amax<T>(p, need ? r0 + i0 + i : r0, need ? c : c0);
-      ab[i] = need ? v : 0u;
+      rl[i] = row_amax<T>(p, need ? r0 + i0 + i : r0, need ? c : c0);
+    } else {
+      wr[i] = false;
+      rl[i] = em[i] ? srow[i * p.ld_sr] : p.scale_row[r0 * p.ld_sr + (c0 >> 5)];
     }
+  }
+  uint32_t cw[E];  // (not fused) the lane's column-wise scale bytes, as loaded
+  if (!kFuse && colw) col_scale_raw<T>(p, band, cvalid ? c : c0, cw);
+  if constexpr (!kFuse && kEdge) load_rows_masked<T, RW>(p, src, r0 + i0, c, rc, d);
+  if constexpr (kFuse) {
+    // every amax entry was loaded before the first store, so no load waits on one
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      const uint8_t sb = e8m0_of<T>(ab[i]);
+      const uint8_t sb = e8m0_of<T>((em[i] || wr[i]) ? rl[i] : 0u);
       rshift[i] = 127 - (int)sb;
       if (wr[i]) p.scale_row[(r0 + i0 + i) * p.ld_sr + (c >> 5)] = sb;
     }
   } else {
-    uint32_t sb[RW];  // every scale load goes out before the first is used (unconditional,
-                      // as the amax entries above)
+    if (colw && cvalid) col_shifts_of<T>(p, cw, cshift);
 #pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const uint32_t v = em[i] ? srow[i * p.ld_sr] : p.scale_row[r0 * p.ld_sr + (c0 >> 5)];
-      sb[i] = em[i] ? v : 0u;
-    }
-    if (colw) {
-      if (cvalid) col_shifts<T>(p, band, c, cshift);
-    }
-#pragma unroll
-    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)sb[i] : 0;
+    for (int i = 0; i < RW; ++i) rshift[i] = em[i] ? 127 - (int)rl[i] : 0;
   }
-  if (interior) {  // outputs not dword aligned: window stores (every lane takes part)
+  if constexpr (interior) {  // outputs not dword aligned: window stores (every lane takes part)
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       uint32_t q[E / 4];
@@ -1179,25 +1254,25 @@ __device__ __forceinline__ void cast_tile_general(
           store_bytes<E>(p.data_col + o0 + i * p.cols, q, p.nt_col);
       }
     }
-    return;
-  }
-  // edge tile: whole chunks store whole when the outputs are dword aligned, else byte by byte
+  } else {
+    // edge tile: whole chunks store whole when the outputs are dword aligned, else byte by byte
 #pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    if (!em[i]) continue;
-    const int64_t o = o0 + i * p.cols;
-    uint32_t q[E / 4];
-    quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
-    if (em[i] == kFull && p.mo_row == 0)
-      store_bytes<E>(p.data_row + o, q, p.nt_row);
-    else
-      store_masked<E>(p.data_row + o, q, em[i]);
-    if (colw) {
-      quantize_chunk<T, kPre>(d[i], cshift, true, q);
-      if (em[i] == kFull && p.mo_col == 0)
-        store_bytes<E>(p.data_col + o, q, p.nt_col);
+    for (int i = 0; i < RW; ++i) {
+      if (!em[i]) continue;
+      const int64_t o = o0 + i * p.cols;
+      uint32_t q[E / 4];
+      quantize_chunk<T, kPre>(d[i], &rshift[i], false, q);
+      if (em[i] == kFull && p.mo_row == 0)
+        store_bytes<E>(p.data_row + o, q, p.nt_row);
       else
-        store_masked<E>(p.data_col + o, q, em[i]);
+        store_masked<E>(p.data_row + o, q, em[i]);
+      if (colw) {
+        quantize_chunk<T, kPre>(d[i], cshift, true, q);
+        if (em[i] == kFull && p.mo_col == 0)
+          store_bytes<E>(p.data_col + o, q, p.nt_col);
+        else
+          store_masked<E>(p.data_col + o, q, em[i]);
+      }
     }
   }
 }
@@ -1316,7 +1391,10 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     }
     return;
   }
-  cast_tile_general<T, kCol, kPre, kFuse>(p, band, c0, c, i0, nrows, interior, cshift, colw);
+  if (interior)
+    cast_tile_general<T, kCol, kPre, kFuse, false>(p, band, c0, c, i0, nrows, cshift, colw);
+  else
+    cast_tile_general<T, kCol, kPre, kFuse, true>(p, band, c0, c, i0, nrows, cshift, colw);
   if constexpr (kFuse && kCol) {
     if (wave == 0 && cvalid) store_col_scales<T>(p, band, c, nrows, interior, csb);
   }
@@ -1344,7 +1422,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 template <int W>
 __device__ __forceinline__ void load_window(const uint8_t* a, int n, uint32_t (&w)[W]) {
   const uintptr_t ai = reinterpret_cast<uintptr_t>(a);
-  const uint32_t* d = reinterpret_cast<const uint32_t*>(ai & ~uintptr_t(3));
+  global_cu32* d = global_cdword(ai);
   const int last = (int)(((ai + (uintptr_t)n - 1) >> 2) - (ai >> 2));  // last dword to read
   const int sh = (int)(ai & 3);
   uint32_t x[W + 1];
@@ -1435,7 +1513,10 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
     }
     if (cvalid) load_rows<T, RW>(src, p.cols, p.in_shift2, RW, d, u0 + WC <= p.cols);
   } else {
-    load_rows_masked<T, RW>(p, src, v0 + i0, RW, cu, cvalid, d, em);
+    const RowClass<RW> rc = classify_rows<T, RW>(p, v0 + i0, RW, cu, cvalid);
+#pragma unroll
+    for (int i = 0; i < RW; ++i) em[i] = rc.em[i];
+    load_rows_masked<T, RW>(p, src, v0 + i0, cu, rc, d);
   }
   // The two row-wise scale bytes of every row.  In an interior tile every row exists: each is
   // at a fixed lane offset from the row's first scale byte, a scalar address (the host keeps
