@@ -104,6 +104,10 @@ def parse():
                          "markdown: RUN_fetch/ (FETCH_SIZE) and RUN_write/ (WRITE_SIZE), "
                          "optionally RUN_wrreq/ (TCC_EA0_WRREQ_sum, TCC_EA0_WRREQ_64B_sum), "
                          "each with its manifest RUN_<pass>.json; to --out")
+    ap.add_argument("--summarize-trace", metavar="RUN", default=None,
+                    help="(no GPU) summarize the rocprofv3 --kernel-trace run of a "
+                         "--counter-pass workload (RUN_trace/ and RUN_trace.json) as markdown, "
+                         "to --out")
     ap.add_argument("--out", default=None)
     return ap.parse_args()
 
@@ -247,39 +251,116 @@ def _short_kernel(name: str) -> str:
     return f"{m.group(1)}<{t}{', ' + rest if rest else ''}>"
 
 
+MARKER = "FillFunctor<short>"  # LaunchLog's marker kernel
+
+
 def _attribute(man, disp):
-    """Splits the library's dispatches (namespace mxfp8) into the manifest's items (runs of
-    consecutive dispatches of one kernel) and finds the copy probe's launches; checks the
+    """Splits a run's dispatches at LaunchLog's markers into the manifest's items: each item's
+    library dispatches (namespace mxfp8), in order, and the copy probe's copies.  Checks the
     counts."""
-    runs = []
+    spans = []
     for i, d in enumerate(disp):
-        if "mxfp8::" not in d["name"]:
-            continue
-        if runs and runs[-1][-1] == i - 1 and disp[i - 1]["name"] == d["name"]:
-            runs[-1].append(i)
-        else:
-            runs.append([i])
+        if MARKER in d["name"]:
+            spans.append([])
+        elif spans:
+            spans[-1].append(i)
+    spans = spans[1:]  # the first fill is the marker tensor's zero-fill, before any item
     items = man["items"]
-    if len(runs) != len(items):
-        raise SystemExit(f"{len(runs)} runs of library launches, {len(items)} manifest items")
-    for it, r in zip(items, runs):
-        if len(r) % it["calls"]:
-            raise SystemExit(f"{it['label']}: {len(r)} launches for {it['calls']} calls")
-    # the copy probe: the first copy launches after the step's last launch, back to back
-    n_step = sum(1 for it in items if it["label"].startswith("step_"))
-    lo = runs[n_step - 1][-1]
-    hi = runs[n_step][0] if n_step < len(runs) else len(disp)
-    cp = [i for i in range(lo + 1, hi) if "copyBuffer" in disp[i]["name"]]
-    probe = cp[:man["copy_probe"]["launches"]]
-    if len(probe) != man["copy_probe"]["launches"] or probe[-1] - probe[0] != len(probe) - 1 or \
-            len({(disp[i]["grid"], disp[i]["wg"]) for i in probe}) != 1:
-        raise SystemExit("copy probe: expected "
-                         f"{man['copy_probe']['launches']} consecutive copies of one shape")
+    if len(spans) != len(items):
+        raise SystemExit(f"{len(spans)} marked spans, {len(items)} manifest items")
+    runs, probe = [], None
+    for it, sp in zip(items, spans):
+        if it["label"] == "copy_probe":
+            # the probe's copies come first, back to back (later ones set up the next item)
+            n = man["copy_probe"]["launches"]
+            probe = [i for i in sp if "copyBuffer" in disp[i]["name"]][:n]
+            if len(probe) != n or probe[-1] - probe[0] != n - 1 or \
+                    len({(disp[i]["grid"], disp[i].get("wg")) for i in probe}) != 1:
+                raise SystemExit(f"copy probe: expected {n} consecutive copies of one shape")
+            runs.append([])
+            continue
+        lib = [i for i in sp if "mxfp8::" in disp[i]["name"]]
+        if not lib or len(lib) % it["calls"]:
+            raise SystemExit(f"{it['label']}: {len(lib)} launches for {it['calls']} calls")
+        runs.append(lib)
     return runs, probe
 
 
 COUNTER_PASSES = (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE"),
                   ("wrreq", "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum"))
+
+
+ITEM_NOTES = (
+    "Items: `step_*` are the stages of the 4-fragment step; the others are the per-call "
+    "table's entries at 16384x6144, or at the matrix their name starts with (`full`, "
+    "`partial`: the quarter fragment at offset 17, "
+    "`partial_own`: the quarter in a rank's own input and fragment-sized output allocations, "
+    "`full_rowonly`: column-wise outputs absent), each as eager calls rotating over its buffer "
+    "sets, the layer batch's stages (`layer_k_buffers_*`: 8 packed buffers and a K = 8 combine, "
+    "`layer_shared_buffer_*`: one shared buffer) and one rank's fragment of it (`rank_*`: "
+    "fragment 2, in place and into fragment-sized outputs).")
+
+
+def _load_runs(run, kinds):
+    """The manifests of a counter or trace run's passes, checked to hold the same launches."""
+    mans = {k: json.load(open(f"{run}_{k}.json")) for k in kinds}
+    man = mans[kinds[0]]
+    for k in kinds:
+        if [(i["label"], i["calls"]) for i in mans[k]["items"]] != \
+                [(i["label"], i["calls"]) for i in man["items"]] or \
+                mans[k]["kernel_source_sha256_16"] != man["kernel_source_sha256_16"]:
+            raise SystemExit(f"the {k} pass ran other launches or another kernel source")
+    return man
+
+
+def _by_label(man):
+    """Item indices by label, in first-seen order (the copy probe left out)."""
+    seen = {}
+    for k, it in enumerate(man["items"]):
+        if it["label"] != "copy_probe":
+            seen.setdefault(it["label"], []).append(k)
+    return seen
+
+
+def _per_call(vals, calls):
+    """Median over the calls of the sum over each call's launches, and launches per call."""
+    lpc = len(vals) // calls
+    return statistics.median(sum(vals[j * lpc:(j + 1) * lpc]) for j in range(calls)), lpc
+
+
+def _kernels(disp, idx):
+    names = []
+    for i in idx:
+        n = _short_kernel(disp[i]["name"])
+        if n not in names:
+            names.append(n)
+    return ", ".join(f"`{n}`" for n in names)
+
+
+def _commands(man, run, kinds, what):
+    argv = list(man["argv"])
+    j = argv.index("--counter-pass")
+    del argv[j:j + 2]
+    name = os.path.basename(run)
+    out = []
+    for k, ctr in what:
+        if k not in kinds:
+            continue
+        prof = (f"timeout -s KILL 600 rocprofv3 --pmc {ctr}" if ctr else
+                "timeout -k 10 600 rocprofv3 --kernel-trace --stats")
+        out.append(f"cd /tmp && export TMPDIR=/tmp && {prof} --output-format csv -d "
+                   f"$R/gpurun_out/cnt/{name}_{k} -o p -- python -u $R/bench.py {' '.join(argv)} "
+                   f"--counter-pass $R/gpurun_out/cnt/{name}_{k}.json")
+    return out, name
+
+
+def _write(args, md):
+    text = "\n".join(md)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    else:
+        print(text)
 
 
 def summarize_counters(args):
@@ -291,40 +372,26 @@ def summarize_counters(args):
     kinds = [k for k, _ in COUNTER_PASSES if os.path.isdir(f"{run}_{k}")]
     if "fetch" not in kinds or "write" not in kinds:
         raise SystemExit(f"need {run}_fetch/ and {run}_write/")
-    mans = {k: json.load(open(f"{run}_{k}.json")) for k in kinds}
-    man = mans["fetch"]
-    for k in kinds:
-        if [(i["label"], i["calls"]) for i in mans[k]["items"]] != \
-                [(i["label"], i["calls"]) for i in man["items"]] or \
-                mans[k]["kernel_source_sha256_16"] != man["kernel_source_sha256_16"]:
-            raise SystemExit(f"the {k} pass ran other launches or another kernel source")
+    man = _load_runs(run, kinds)
     passes = {k: _counter_dispatches(f"{run}_{k}") for k in kinds}
     att = {k: _attribute(man, v) for k, v in passes.items()}
-
-    def per_call(kind, counter, idx_run, calls):
-        disp = passes[kind]
-        vals = [disp[i]["c"][counter] for i in idx_run]
-        lpc = len(vals) // calls
-        return statistics.median(sum(vals[j * lpc:(j + 1) * lpc]) for j in range(calls)), lpc
 
     nb_kib = man["copy_probe"]["read_bytes"] / 1024
     f_probe = statistics.median(passes["fetch"][i]["c"]["FETCH_SIZE"] for i in att["fetch"][1])
     w_probe = statistics.median(passes["write"][i]["c"]["WRITE_SIZE"] for i in att["write"][1])
     ff, wf = nb_kib / f_probe, (man["copy_probe"]["write_bytes"] / 1024) / w_probe
 
-    seen = {}
-    for k, it in enumerate(man["items"]):
-        seen.setdefault(it["label"], []).append(k)
     rows, blob = [], {}
-    for label, ks in seen.items():
+    for label, ks in _by_label(man).items():
         it = man["items"][ks[0]]
 
         def med(kind, counter):
-            return statistics.median(per_call(kind, counter, att[kind][0][k], it["calls"])[0]
-                                     for k in ks)
+            return statistics.median(
+                _per_call([passes[kind][i]["c"][counter] for i in att[kind][0][k]],
+                          it["calls"])[0] for k in ks)
         fk, wk = med("fetch", "FETCH_SIZE"), med("write", "WRITE_SIZE")
-        lpc = per_call("fetch", "FETCH_SIZE", att["fetch"][0][ks[0]], it["calls"])[1]
-        kname = _short_kernel(passes["fetch"][att["fetch"][0][ks[0]][0]]["name"])
+        lpc = len(att["fetch"][0][ks[0]]) // it["calls"]
+        kname = _kernels(passes["fetch"], att["fetch"][0][ks[0]])
         rd, wr = fk * 1024 * ff, wk * 1024 * wf
         w64 = None
         if "wrreq" in passes:
@@ -335,12 +402,12 @@ def summarize_counters(args):
         blob[label] = int(round((rd + wr) / lpc))
 
     has_w = "wrreq" in passes
-    hdr = ("| item | kernel | launches per call | calls | FETCH_SIZE KiB per call | "
+    hdr = ("| item | kernels | launches per call | calls | FETCH_SIZE KiB per call | "
            "WRITE_SIZE KiB per call | HBM read MB | HBM write MB | total MB | algorithmic MB | "
            "total / algorithmic |" + (" 64-byte share of write requests |" if has_w else ""))
     lines = [hdr, "|" + "---|" * (hdr.count("|") - 1)]
     for label, kname, lpc, n, fk, wk, rd, wr, alg, w64 in rows:
-        lines.append(f"| {label} | `{kname}` | {lpc} | {n} | {fk:.0f} | {wk:.0f} | "
+        lines.append(f"| {label} | {kname} | {lpc} | {n} | {fk:.0f} | {wk:.0f} | "
                      f"{rd / 1e6:.2f} | {wr / 1e6:.2f} | {(rd + wr) / 1e6:.2f} | {alg / 1e6:.2f} | "
                      f"{(rd + wr) / alg:.4f} |" + (f" {w64:.4f} |" if has_w else ""))
     workload = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
@@ -349,27 +416,15 @@ def summarize_counters(args):
              "kernel_source_sha256_16": man["kernel_source_sha256_16"],
              "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
              "hbm_bytes_per_launch": blob}
-    argv = list(man["argv"])
-    j = argv.index("--counter-pass")
-    del argv[j:j + 2]
-    name = os.path.basename(run)
-    cmds = [f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 600 rocprofv3 --pmc {ctr} "
-            f"--output-format csv -d $R/gpurun_out/cnt/{name}_{k} -o p -- python -u "
-            f"$R/bench.py {' '.join(argv)} --counter-pass $R/gpurun_out/cnt/{name}_{k}.json"
-            for k, ctr in COUNTER_PASSES if k in kinds]
-    table_note = ("" if "--no-kernel-table" in argv else
-                  "  Items other than `step_*` are the per-call table's entries at 16384x6144 "
-                  "(full input, the quarter fragment at offset 17, `partial_own`: the quarter in "
-                  "a rank's own input and fragment-sized output allocations, `full_rowonly`: "
-                  "column-wise outputs absent), each as eager calls rotating over its buffer "
-                  "sets.")
+    cmds, name = _commands(man, run, kinds, COUNTER_PASSES)
     md = [f"# HBM traffic per call: rocprofv3 counters, {workload}", "",
           "One MI355X (gfx950), ROCm 7.2.  `bench.py --counter-pass` runs every launch untimed "
-          "in a fixed order and writes that order to a manifest; each counter set is a "
-          "rocprofv3 run of its own ($R is the repository root):", "", "```", *cmds, "```", "",
+          "in a fixed order, a marker kernel before each item, and writes that order to a "
+          "manifest; each counter set is a rocprofv3 run of its own ($R is the repository "
+          "root):", "", "```", *cmds, "```", "",
           f"This summary is `python bench.py --summarize-counters gpurun_out/cnt/{name} --out "
-          f"<this file>`, which splits each run's library dispatches into the manifest's items "
-          "(runs of one kernel) and checks the counts." + table_note, "",
+          f"<this file>`, which splits each run's dispatches at the markers into the manifest's "
+          "items and checks the counts.  " + ITEM_NOTES, "",
           f"Calibration: the copy probe (torch `copy_` of 256 MiB, `__amd_rocclr_copyBuffer`) "
           f"reads {f_probe:.0f} KiB of FETCH_SIZE and {w_probe:.0f} KiB of WRITE_SIZE per launch "
           f"for {nb_kib:.0f} KiB read and written: fetch factor {ff:.4f}, write factor {wf:.4f}.",
@@ -382,18 +437,78 @@ def summarize_counters(args):
            "64-byte requests." if has_w else ""), "", *lines, "",
           "`bench.py` reads `roofline.traffic` from this block while the kernel source hash "
           "matches:", "", "```json", json.dumps(block, indent=1), "```", ""]
-    text = "\n".join(md)
-    if args.out:
-        with open(args.out, "w") as f:
-            f.write(text)
-    else:
-        print(text)
+    _write(args, md)
+
+
+def _trace_dispatches(d):
+    """The dispatches of one rocprofv3 --kernel-trace run (output directory ``d``), in
+    dispatch order: kernel name, grid and duration (µs)."""
+    import csv
+
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_trace.csv under {d}, found {files}")
+    disp = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            disp[int(r["Dispatch_Id"])] = {
+                "name": r["Kernel_Name"], "grid": int(r["Grid_Size_X"]),
+                "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3}
+    return [disp[k] for k in sorted(disp)]
+
+
+def summarize_trace(args):
+    """Markdown summary of the kernel trace of one --counter-pass workload (``RUN_trace``, a
+    rocprofv3 --kernel-trace output directory next to its manifest): kernel-only µs per call
+    of every item, and its algorithmic GB/s and fraction of the 8 TB/s peak."""
+    run = args.summarize_trace
+    man = _load_runs(run, ["trace"])
+    disp = _trace_dispatches(f"{run}_trace")
+    runs, probe = _attribute(man, disp)
+    lines = ["| item | kernels | launches per call | calls | µs per call (median) | min | max | "
+             "algorithmic MB | GB/s | fraction of 8 TB/s |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for label, ks in _by_label(man).items():
+        it = man["items"][ks[0]]
+        per = []
+        for k in ks:
+            v = [disp[i]["us"] for i in runs[k]]
+            lpc = len(v) // it["calls"]
+            per += [sum(v[j * lpc:(j + 1) * lpc]) for j in range(it["calls"])]
+        us = statistics.median(per)
+        gbs = it["alg_bytes"] / (us * 1e-6) / 1e9
+        lines.append(f"| {label} | {_kernels(disp, runs[ks[0]])} | {lpc} | {len(per)} | "
+                     f"{us:.2f} | {min(per):.2f} | {max(per):.2f} | {it['alg_bytes'] / 1e6:.2f} | "
+                     f"{gbs:.1f} | {gbs / HBM_PEAK_GBS:.4f} |")
+    cp = statistics.median(disp[i]["us"] for i in probe)
+    cmds, name = _commands(man, run, ["trace"], (("trace", None),))
+    workload = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
+                + ("fused scales + cast" if man["fused"] else "scales then cast"))
+    md = [f"# Kernel durations per call: rocprofv3 kernel trace, {workload}", "",
+          "One MI355X (gfx950), ROCm 7.2.  `bench.py --counter-pass` runs every launch untimed "
+          "in a fixed order, a marker kernel before each item, and writes that order to a "
+          "manifest ($R is the repository root):", "", "```", *cmds, "```", "",
+          f"This summary is `python bench.py --summarize-trace gpurun_out/cnt/{name} --out "
+          "<this file>`, which splits the traced dispatches at the markers into the manifest's "
+          "items and checks the counts.  " + ITEM_NOTES, "",
+          "Per call: the sum of the call's launch durations (kernel only, from the trace's "
+          "timestamps; no dispatch gap); median, min and max over the item's calls.  The calls "
+          "run eagerly, one item after another with a synchronization between items, so these "
+          "are the kernels' own times, without the per-call overhead that graph replays of the "
+          "per-call table include.  Algorithmic bytes follow "
+          "`mxfp8_block_scaled_partial_amd/bytes_model.py`.", "", *lines, "",
+          f"Copy probe (256 MiB device copy, read + write), median of {len(probe)} launches: "
+          f"{cp:.2f} µs, {2 * COPY_PROBE_BYTES / (cp * 1e-6) / 1e9:.1f} GB/s.", "",
+          f"Kernel source: `kernels.hip` sha256 prefix `{man['kernel_source_sha256_16']}`.", ""]
+    _write(args, md)
 
 
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -484,7 +599,7 @@ def main():
             cast_ev[1].record()
 
     if args.counter_pass:
-        counter_pass(args, step, stage_names, stage_bytes, m, dev)
+        counter_pass(args, stages, n_sets, stage_bytes, m, dev)
         return
 
     log(f"warmup {args.warmup} steps")
@@ -644,33 +759,58 @@ def copy_probe(dev):
             "us": round(us, 2), "GBps": round(2 * nb / (us * 1e-6) / 1e9, 1)}
 
 
-def counter_pass(args, step, stage_names, stage_bytes, m, dev):
-    """The launches a rocprofv3 counter pass attributes, untimed and in a fixed order: the
-    step (every stage but the zero-fill, which is torch's), the copy probe, then (unless
-    --no-kernel-table) every entry of the per-call table as ``--counter-calls`` eager calls
-    rotating over its buffer sets.  Writes the order to the manifest: consecutive launches of
-    one library kernel form one item, so ``summarize_counters`` can attribute each dispatch."""
-    import torch
+class LaunchLog:
+    """The order of the launches of a counter or trace run (--counter-pass): each item is
+    preceded by a marker, a one-element int16 fill (a kernel nothing else here launches), so
+    the summaries can split the profiled dispatches into items whatever kernels an item runs.
+    The marker tensor's own zero-fill, when the log is made, is one more such fill: it opens
+    the span of everything before the first item."""
 
-    items = []
-    lib_stages = [s for s in stage_names if s != "zero"]
+    def __init__(self, dev):
+        import torch
+
+        self.items = []
+        self._t = torch.zeros(1, dtype=torch.int16, device=dev)
+
+    def run(self, label, calls, alg_bytes, fn):
+        """The marker, then fn(i) for i < calls, then a synchronization."""
+        import torch
+
+        self._t.fill_(1)
+        for i in range(calls):
+            fn(i)
+        torch.cuda.synchronize()
+        self.items.append({"label": label, "calls": calls, "alg_bytes": int(alg_bytes)})
+
+
+def counter_pass(args, stages, n_sets, stage_bytes, m, dev):
+    """The launches a rocprofv3 counter or trace pass attributes, untimed and in a fixed order:
+    the steps (each stage but the zero-fill, which is torch's, as an item of one call), the
+    copy probe, then (unless --no-kernel-table) every entry of the per-call table as
+    ``--counter-calls`` eager calls rotating over its buffer sets, and (unless
+    --no-layer-batch) the layer batch's stages and one rank's calls.  Writes the order to the
+    manifest for ``summarize_counters`` and ``summarize_trace``."""
+    L = LaunchLog(dev)
     for i in range(max(2, args.warmup) + args.steps):
-        step(i)
-        items += [{"label": f"step_{s}", "calls": 1, "alg_bytes": int(stage_bytes[s])}
-                  for s in lib_stages]
-    torch.cuda.synchronize()
-    copy_probe(dev)
+        seq = stages[i % n_sets][:-1] + [stages[(i - 1) % n_sets][-1]]
+        for name, fn in seq:
+            if name == "zero":
+                fn()
+            else:
+                L.run(f"step_{name}", 1, stage_bytes[name], lambda i, fn=fn: fn())
+    L.run("copy_probe", 1, 2 * COPY_PROBE_BYTES, lambda i: copy_probe(dev))
     if args.kernel_table:
-        kernel_table(args, m, dev, items)
-    torch.cuda.synchronize()
+        kernel_table(args, m, dev, L)
+    if args.layer_batch:
+        layer_batch(args, dev, L)
     man = {"argv": sys.argv[1:], "dtype": args.dtype, "fused": bool(args.fused),
            "kernel_source_sha256_16": kernel_sha(),
            "copy_probe": {"launches": COPY_PROBE_LAUNCHES, "read_bytes": COPY_PROBE_BYTES,
                           "write_bytes": COPY_PROBE_BYTES},
-           "items": items}
+           "items": L.items}
     with open(args.counter_pass, "w") as f:
         json.dump(man, f, indent=1)
-    log(f"counter pass: {len(items)} items -> {args.counter_pass}")
+    log(f"counter pass: {len(L.items)} items -> {args.counter_pass}")
 
 
 def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
@@ -742,7 +882,7 @@ def single_pass_step(args, sets, spec, frags, s_in, dev, tdt, shared):
                     "with the partial chain for the bands at the cuts"}
 
 
-def layer_batch(args, dev):
+def layer_batch(args, dev, L=None):
     """The transformer-layer batch: QKV 4096x12288 (bidirectional), out-proj 4096x4096
     (row-only), up 4096x14336 (bidirectional), down 14336x4096 (row-only), BF16, end to end in
     one flat buffer of 184 549 376 elements cut into 8 equal fragments (fragments 2 and 5 span
@@ -757,7 +897,10 @@ def layer_batch(args, dev):
 
     ``rank_fragment``: one rank's share, fragment 2 (its pieces of QKV, out-proj and up), per
     call like the kernel table (graph replays of 10 calls over rotating buffer sets): its
-    partial amax, and its cast in place and into fragment-sized outputs."""
+    partial amax, and its cast in place and into fragment-sized outputs.
+
+    With a LaunchLog ``L`` (a counter pass) nothing is timed: the steps' stages and the
+    rank's calls run as items of the log."""
     import numpy as np
     import torch
 
@@ -811,6 +954,17 @@ def layer_batch(args, dev):
                 fn()
             if ev is not None:
                 ev[-1].record()
+
+        if L is not None:
+            for i in range(max(2, args.warmup) + max(4, args.steps // 2)):
+                for nm, fn in plans[i % 2].stages()[:-1] + [plans[(i - 1) % 2].stages()[-1]]:
+                    if nm == "zero":
+                        fn()
+                    else:
+                        L.run(f"layer_{mode}_{nm}", 1, stage_bytes[nm], lambda i, fn=fn: fn())
+            del plans
+            torch.cuda.empty_cache()
+            continue
 
         for i in range(max(2, args.warmup)):
             step(i)
@@ -871,8 +1025,11 @@ def layer_batch(args, dev):
         for kname, call in calls:
             def fn(i, call=call):
                 assert call(plans[i % n_sets], torch.cuda.current_stream().cuda_stream) == 0
-            us = per_call_us(args, fn, 10)
             nb = piece_sum([(fs, fl)], kname)
+            if L is not None:
+                L.run(f"rank_{kname}_{name}", args.counter_calls, nb, fn)
+                continue
+            us = per_call_us(args, fn, 10)
             rank[f"{kname}_{name}"] = {"us": round(us, 2), "alg_bytes": nb,
                                        "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                                        "frac_of_peak": round(nb / (us * 1e-6) / 1e9
@@ -881,7 +1038,7 @@ def layer_batch(args, dev):
         del plans
         torch.cuda.empty_cache()
     res["rank_fragment"] = rank
-    return res
+    return None if L is not None else res
 
 
 def ablation(args, dev, rounds=3):
@@ -1024,7 +1181,7 @@ def graph_step_us(args, step_fns):
     return round(us, 2)
 
 
-def kernel_table(args, m_default, dev, items=None):
+def kernel_table(args, m_default, dev, L=None):
     """Per-call µs and GB/s of partial amax and partial cast, the pages' table, plus the fused
     scales + cast and (full input only) the single-pass quantize, for every matrix of that
     table (16384x6144, 4096x4096, 1024x1024, 160x96): full input and the quarter fragment
@@ -1035,8 +1192,8 @@ def kernel_table(args, m_default, dev, items=None):
     matrices; partial runs: quarter-size fragments placed so that input - 17 elements stays
     16-byte aligned): the two large matrices stream from HBM, the small ones stay in the 256 MB
     Infinity Cache like any repeated small call.  Returns the 16384x6144 entries and, by
-    shape, the others.  With ``items`` (a counter pass) nothing is timed: each entry makes
-    ``--counter-calls`` eager calls and appends its manifest item."""
+    shape, the others.  With a LaunchLog ``L`` (a counter pass) nothing is timed: each entry
+    makes ``--counter-calls`` eager calls as an item of the log."""
     import torch
 
     from mxfp8_block_scaled_partial_amd import workloads as wl
@@ -1053,7 +1210,7 @@ def kernel_table(args, m_default, dev, items=None):
                     m = wl.matrix_large(dtype)
             else:  # N(0,1) times a per-column 2^U[-8, 8], the 4096x4096 recipe
                 m = wl.matrix_square(dtype, rows=rows, cols=cols)
-            entries = time_shape(args, m, dev, items)
+            entries = time_shape(args, m, dev, L)
             if (rows, cols) == (16384, 6144):
                 table.update(entries)
             else:
@@ -1062,7 +1219,7 @@ def kernel_table(args, m_default, dev, items=None):
     return table, by_shape
 
 
-def time_shape(args, m, dev, items=None):
+def time_shape(args, m, dev, L=None):
     """The table's entries for one matrix in one dtype (see ``kernel_table``)."""
     import numpy as np
     import torch
@@ -1133,12 +1290,10 @@ def time_shape(args, m, dev, items=None):
         if run == "full":
             kernels.append(("quantize", fused_p, B.mxfp8_quantize))
         for kname, pieces, fn in kernels:
-            if items is not None:
-                for i in range(args.counter_calls):
-                    fn(pieces[i % n_sets])
-                torch.cuda.synchronize()
-                items.append({"label": f"{kname}_{dtype}_{run}", "calls": args.counter_calls,
-                              "alg_bytes": int(pb[kname])})
+            if L is not None:
+                shape = "" if (rows, cols) == (16384, 6144) else f"{rows}x{cols}_"
+                L.run(f"{shape}{kname}_{dtype}_{run}", args.counter_calls, pb[kname],
+                      lambda i, fn=fn, pieces=pieces: fn(pieces[i % n_sets]))
                 continue
             for i in range(3):
                 fn(pieces[i % n_sets])

@@ -52,42 +52,73 @@ def _write_pass(d, counters, dispatches):
                             c, vals[c], 0, 1])
 
 
+MARK = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<short> >(int)"
+LIB = "void mxfp8::(anonymous namespace)::{}(Args)"
+AMAX = LIB.format("amax_vec_kernel<unsigned short, true, false, 2>")
+AMAX_ROW = LIB.format("amax_vec_kernel<unsigned short, false, false, 2>")
+COMB = LIB.format("combine_kernel<unsigned short>")
+CAST = LIB.format("cast_vec_kernel<unsigned short, true, false, false, 2, false>")
+FILL = "void at::native::vectorized_elementwise_kernel<16, FillFunctor<float> >(int)"
+COPY = "__amd_rocclr_copyBuffer"
+KIB = (256 << 20) / 1024
+
+
+def _manifest(items):
+    return {"argv": ["--steps", "1", "--counter-pass", "x.json"], "dtype": "bf16",
+            "fused": False, "kernel_source_sha256_16": "0123456789abcdef",
+            "copy_probe": {"launches": 24, "read_bytes": 256 << 20, "write_bytes": 256 << 20},
+            "items": items}
+
+
+def _synthetic_run():
+    """A manifest and its dispatches (name, grid, workgroup, FETCH KiB, WRITE KiB, µs): two
+    steps, the copy probe, a table entry of two calls of two launches each and a layer-batch
+    stage whose call runs two kernels."""
+    items = []
+    disp = [(MARK, 1, 256, 0, 0, 1.0)]  # the marker tensor's zero-fill
+    for _ in range(2):
+        disp.append((FILL, 4, 256, 50, 10, 1.0))  # the step's zero-fill: not an item
+        for label, kern, alg, f, w, us in (("step_amax", AMAX, 1000, 900, 100, 30.0),
+                                           ("step_combine", COMB, 100, 80, 20, 5.0),
+                                           ("step_cast", CAST, 2000, 1000, 1000, 70.0)):
+            items.append({"label": label, "calls": 1, "alg_bytes": alg * 1024})
+            disp += [(MARK, 1, 256, 0, 0, 1.0), (kern, 100, 256, f, w, us)]
+    items.append({"label": "copy_probe", "calls": 1, "alg_bytes": 2 * (256 << 20)})
+    disp += [(MARK, 1, 256, 0, 0, 1.0)] + [(COPY, 131072, 512, KIB / 2, KIB, 100.0)] * 24
+    items.append({"label": "cast_bf16_full", "calls": 2, "alg_bytes": 4000 * 1024})
+    # the table's set-up copy and fill land in the previous span: not library launches
+    disp += [(COPY, 131072, 512, KIB / 4, KIB / 2, 50.0), (FILL, 4, 256, 1, 1, 1.0),
+             (MARK, 1, 256, 0, 0, 1.0)]
+    disp += [(CAST, 50, 256, 1000, 1000, 10.0), (CAST, 50, 256, 1000, 1000, 12.0)] * 2
+    items.append({"label": "layer_k_buffers_amax", "calls": 1, "alg_bytes": 3000 * 1024})
+    disp += [(MARK, 1, 256, 0, 0, 1.0), (AMAX, 60, 256, 1500, 50, 20.0),
+             (AMAX_ROW, 40, 256, 1000, 30, 15.0)]
+    return _manifest(items), disp
+
+
+def _write_trace(d, dispatches):
+    os.makedirs(os.path.join(d, "host"), exist_ok=True)
+    cols = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id",
+            "Kernel_Name", "Correlation_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size",
+            "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Workgroup_Size_X",
+            "Workgroup_Size_Y", "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    import csv
+    t = 1000000
+    with open(os.path.join(d, "host", "p_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(cols)
+        for i, (name, grid, wg, us) in enumerate(dispatches):
+            w.writerow(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, i + 1, 1, name, i + 1, t,
+                        t + int(us * 1000), 0, 0, 8, 0, 16, wg, 1, 1, grid, 1, 1])
+            t += int(us * 1000) + 500
+
+
 def test_counter_summary_attributes_dispatches_to_the_manifest(tmp_path):
-    """The counter summary splits the library's dispatches into the manifest's items (runs of
-    one kernel), calibrates on the copy probe and reports bytes against algorithmic bytes."""
+    """The counter summary splits the dispatches at the markers into the manifest's items,
+    calibrates on the copy probe and reports bytes against algorithmic bytes."""
     import json
 
-    sys.path.insert(0, ROOT)
-    import bench
-
-    lib = "void mxfp8::(anonymous namespace)::{}(Args)"
-    amax = lib.format("amax_vec_kernel<unsigned short, true, false, 2>")
-    comb = lib.format("combine_kernel<unsigned short>")
-    cast = lib.format("cast_vec_kernel<unsigned short, true, false, false, 2, false>")
-    fill = "void at::native::vectorized_elementwise_kernel<16, FillFunctor<float> >(int)"
-    copy = "__amd_rocclr_copyBuffer"
-    kib = (256 << 20) / 1024
-    man = {"argv": ["--steps", "1", "--counter-pass", "x.json"], "dtype": "bf16",
-           "fused": False, "kernel_source_sha256_16": "0123456789abcdef",
-           "copy_probe": {"launches": 24, "read_bytes": 256 << 20, "write_bytes": 256 << 20},
-           "items": [{"label": "step_amax", "calls": 1, "alg_bytes": 1000 * 1024},
-                     {"label": "step_combine", "calls": 1, "alg_bytes": 100 * 1024},
-                     {"label": "step_cast", "calls": 1, "alg_bytes": 2000 * 1024},
-                     {"label": "step_amax", "calls": 1, "alg_bytes": 1000 * 1024},
-                     {"label": "step_combine", "calls": 1, "alg_bytes": 100 * 1024},
-                     {"label": "step_cast", "calls": 1, "alg_bytes": 2000 * 1024},
-                     {"label": "cast_bf16_full", "calls": 2, "alg_bytes": 4000 * 1024}]}
-    # FETCH_SIZE reads half the bytes (a factor of 2, like gfx950's 64-byte units)
-    step = [(fill, 4, 256, 50, 10), (amax, 100, 256, 900, 100), (comb, 10, 256, 80, 20),
-            (cast, 100, 256, 1000, 1000)]
-    disp = []
-    for _ in range(2):
-        disp += step
-    disp += [(copy, 131072, 512, kib / 2, kib)] * 24
-    # the table's set-up copy right behind the probe, of the same launch shape
-    disp += [(copy, 131072, 512, kib / 4, kib / 2)]
-    # two calls of two launches each (two buckets)
-    disp += [(cast, 50, 256, 1000, 1000), (cast, 50, 256, 1000, 1000)] * 2
+    man, disp = _synthetic_run()
     for k, ctr, idx in (("fetch", "FETCH_SIZE", 3), ("write", "WRITE_SIZE", 4)):
         _write_pass(str(tmp_path / f"r_{k}"), [ctr],
                     [(d[0], d[1], d[2], {ctr: d[idx]}) for d in disp])
@@ -105,29 +136,52 @@ def test_counter_summary_attributes_dispatches_to_the_manifest(tmp_path):
     assert per["step_cast"] == (2 * 1000 + 1000) * 1024
     # per launch = per call / launches per call
     assert per["cast_bf16_full"] == (2 * 2000 + 2000) * 1024 // 2
+    assert per["layer_k_buffers_amax"] == (2 * 2500 + 80) * 1024 // 2
+    assert "copy_probe" not in per
     assert "| cast_bf16_full | `cast_vec_kernel<bf16, true, false, false, 2, false>` | 2 | 2 |" \
         in text
+    assert ("| layer_k_buffers_amax | `amax_vec_kernel<bf16, true, false, 2>`, "
+            "`amax_vec_kernel<bf16, false, false, 2>` | 2 | 1 |") in text
     assert "--counter-pass $R/gpurun_out/cnt/r_fetch.json" in text
     assert " 1.9000 |" in text  # step_amax: (1800 + 100) KiB / 1000 KiB
+
+
+def test_trace_summary_reports_kernel_time_per_call(tmp_path):
+    import json
+
+    man, disp = _synthetic_run()
+    _write_trace(str(tmp_path / "r_trace"), [(d[0], d[1], d[2], d[5]) for d in disp])
+    json.dump(man, open(tmp_path / "r_trace.json", "w"))
+    out = tmp_path / "t.md"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-trace",
+                        str(tmp_path / "r"), "--out", str(out)], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    row = [l for l in text.splitlines() if l.startswith("| cast_bf16_full |")][0].split("|")
+    assert row[3].strip() == "2" and row[4].strip() == "2"
+    assert float(row[5]) == 22.0  # each call: 10 + 12 µs
+    amax = [l for l in text.splitlines() if l.startswith("| step_amax |")][0].split("|")
+    assert float(amax[5]) == 30.0 and amax[4].strip() == "2"
+    assert float(amax[9]) == round(1000 * 1024 / 30e-6 / 1e9, 1)
+    layer = [l for l in text.splitlines() if l.startswith("| layer_k_buffers_amax |")][0]
+    assert "| 35.00 |" in layer
+    assert "median of 24 launches: 100.00 µs" in text
+    assert "--kernel-trace --stats" in text
 
 
 def test_counter_summary_refuses_a_manifest_that_does_not_match(tmp_path):
     import json
 
-    lib = "void mxfp8::(anonymous namespace)::amax_vec_kernel<float, true>(Args)"
-    man = {"argv": ["--counter-pass", "x"], "dtype": "fp32", "fused": False,
-           "kernel_source_sha256_16": "0", "copy_probe": {"launches": 1, "read_bytes": 1024,
-                                                          "write_bytes": 1024},
-           "items": [{"label": "step_amax", "calls": 1, "alg_bytes": 1},
-                     {"label": "step_cast", "calls": 1, "alg_bytes": 1}]}
-    for k, ctr in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
-        _write_pass(str(tmp_path / f"r_{k}"), [ctr], [(lib, 1, 256, {ctr: 1.0}),
-                                                       ("__amd_rocclr_copyBuffer", 1, 1,
-                                                        {ctr: 1.0})])
+    man, disp = _synthetic_run()
+    man["items"] = man["items"][:-1]  # one item fewer than the marked spans
+    for k, ctr, idx in (("fetch", "FETCH_SIZE", 3), ("write", "WRITE_SIZE", 4)):
+        _write_pass(str(tmp_path / f"r_{k}"), [ctr],
+                    [(d[0], d[1], d[2], {ctr: d[idx]}) for d in disp])
         json.dump(man, open(tmp_path / f"r_{k}.json", "w"))
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-counters",
                         str(tmp_path / "r")], capture_output=True, text=True, timeout=120)
-    assert r.returncode != 0 and "1 runs of library launches, 2 manifest items" in r.stderr
+    assert r.returncode != 0 and "9 marked spans, 8 manifest items" in r.stderr
 
 
 def test_roofline_traffic_is_read_per_step_configuration(tmp_path, monkeypatch):
