@@ -53,8 +53,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000,
+                    help="untimed steps first: an idle GPU takes a few tens of ms of work to "
+                         "reach its steady clocks")
     ap.add_argument("--dtype", choices=["bf16", "fp32"], default="bf16")
     ap.add_argument("--min-footprint-gb", type=float, default=1.2,
                     help="distinct input/output sets rotate until this many GB are in use")
@@ -607,20 +609,6 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the oracle leg runs before the timed region: it times the oracle on the host and checks
-    # the warm-up steps' outputs for weight 0 (the same input and fragments) bit for bit
-    cpu = None
-    if args.cpu:
-        wb0 = sets[0][1]
-        ar0, ac0 = wb0.combined.views(0)
-        st0 = wb0.storage[0]
-        gpu0 = {"amax_row": ar0, "amax_col": ac0, "scale_row": st0.scale_row,
-                "scale_col": st0.scale_col, "data_row": st0.data_row, "data_col": st0.data_col}
-        cpu = cpu_baseline(m, args.cpu_rows, s_in, gpu0 if args.cpu_rows == rows else None)
-        for i in range(args.warmup):  # the GPU idled meanwhile: warm it up again
-            step(i)
-        torch.cuda.synchronize()
-
     # the timed steps: wall clock over all of them; HIP events around the cast launch of
     # every CAST_SAMPLE-th step (each event marker costs the stream a few µs, so sampling
     # keeps the measurement from lengthening the steps it measures)
@@ -723,7 +711,16 @@ def main():
         out["ablation"] = ablation(args, dev)
 
     if args.cpu:
-        out["cpu_baseline"] = cpu
+        # the oracle leg runs after every GPU measurement (the GPU idles meanwhile): it times
+        # the oracle on the host and checks the outputs the steps left for weight 0 (the same
+        # input and fragments; every step writes the same bytes) bit for bit
+        wb0 = sets[0][1]
+        ar0, ac0 = wb0.combined.views(0)
+        st0 = wb0.storage[0]
+        gpu0 = {"amax_row": ar0, "amax_col": ac0, "scale_row": st0.scale_row,
+                "scale_col": st0.scale_col, "data_row": st0.data_row, "data_col": st0.data_col}
+        out["cpu_baseline"] = cpu_baseline(m, args.cpu_rows, s_in,
+                                           gpu0 if args.cpu_rows == rows else None)
 
     print(json.dumps(out), flush=True)
 
@@ -1009,6 +1006,8 @@ def layer_batch(args, dev, L=None):
     fs, fl = frags[f]
     rank = {"fragment": [fs, fl], "pieces": [[i, st, n] for (i, st, n, _) in
                                               W.split_fragment(specs, fs, fl)]}
+    # one launch per kernel specialization: the bidirectional pieces and the row-only ones
+    n_launch = len({specs[i].colwise for (i, _, _, _) in W.split_fragment(specs, fs, fl)})
     per_set = fl * 2 * 2 + 2 * packed * 3
     n_sets = max(2, min(10, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
     for name, fo in (("in_place", False), ("fragment_outputs", True)):
@@ -1034,7 +1033,7 @@ def layer_batch(args, dev, L=None):
                                        "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                                        "frac_of_peak": round(nb / (us * 1e-6) / 1e9
                                                              / HBM_PEAK_GBS, 4),
-                                       "launches": 1, "buffer_sets": n_sets}
+                                       "launches": n_launch, "buffer_sets": n_sets}
         del plans
         torch.cuda.empty_cache()
     res["rank_fragment"] = rank
