@@ -272,6 +272,9 @@ def _attribute(man, disp):
         raise SystemExit(f"{len(spans)} marked spans, {len(items)} manifest items")
     runs, probe = [], None
     for it, sp in zip(items, spans):
+        if it.get("aux"):
+            runs.append([])
+            continue
         if it["label"] == "copy_probe":
             # the probe's copies come first, back to back (later ones set up the next item)
             n = man["copy_probe"]["launches"]
@@ -300,7 +303,9 @@ ITEM_NOTES = (
     "`full_rowonly`: column-wise outputs absent), each as eager calls rotating over its buffer "
     "sets, the layer batch's stages (`layer_k_buffers_*`: 8 packed buffers and a K = 8 combine, "
     "`layer_shared_buffer_*`: one shared buffer) and one rank's fragment of it (`rank_*`: "
-    "fragment 2, in place and into fragment-sized outputs).")
+    "fragment 2, in place and into fragment-sized outputs), and with --ablation the runtime-guard "
+    "ablation's calls (`abl_compile_time_*`: the product library, `abl_runtime_guard_*`: the "
+    "ablation library built by `build.py --ablation`).")
 
 
 def _load_runs(run, kinds):
@@ -319,7 +324,7 @@ def _by_label(man):
     """Item indices by label, in first-seen order (the copy probe left out)."""
     seen = {}
     for k, it in enumerate(man["items"]):
-        if it["label"] != "copy_probe":
+        if it["label"] != "copy_probe" and not it.get("aux"):
             seen.setdefault(it["label"], []).append(k)
     return seen
 
@@ -769,8 +774,9 @@ class LaunchLog:
         self.items = []
         self._t = torch.zeros(1, dtype=torch.int16, device=dev)
 
-    def run(self, label, calls, alg_bytes, fn):
-        """The marker, then fn(i) for i < calls, then a synchronization."""
+    def run(self, label, calls, alg_bytes, fn, aux=False):
+        """The marker, then fn(i) for i < calls, then a synchronization.  An ``aux`` item (work
+        between measured items, such as a check) only delimits: the summaries skip it."""
         import torch
 
         self._t.fill_(1)
@@ -778,6 +784,8 @@ class LaunchLog:
             fn(i)
         torch.cuda.synchronize()
         self.items.append({"label": label, "calls": calls, "alg_bytes": int(alg_bytes)})
+        if aux:
+            self.items[-1]["aux"] = True
 
 
 def counter_pass(args, stages, n_sets, stage_bytes, m, dev):
@@ -800,6 +808,8 @@ def counter_pass(args, stages, n_sets, stage_bytes, m, dev):
         kernel_table(args, m, dev, L)
     if args.layer_batch:
         layer_batch(args, dev, L)
+    if args.ablation:
+        ablation(args, dev, L=L)
     man = {"argv": sys.argv[1:], "dtype": args.dtype, "fused": bool(args.fused),
            "kernel_source_sha256_16": kernel_sha(),
            "copy_probe": {"launches": COPY_PROBE_LAUNCHES, "read_bytes": COPY_PROBE_BYTES,
@@ -1040,7 +1050,7 @@ def layer_batch(args, dev, L=None):
     return None if L is not None else res
 
 
-def ablation(args, dev, rounds=3):
+def ablation(args, dev, rounds=3, L=None):
     """The PR page's one design measurement ("Bidirectional kernel performance": an earlier
     version whose amax selected the column-wise work with runtime pointer guards was 21-35%
     slower) redone on MI355X with the current kernels: the product's compile-time
@@ -1049,12 +1059,14 @@ def ablation(args, dev, rounds=3):
     16384x6144 BF16 and FP32, full input and the quarter fragment at offset 17, row-only and
     bidirectional, amax and cast; per call from graph replays of 10 calls over rotating buffer
     sets, the two builds interleaved over ``rounds`` rounds (median).  Each case also checks
-    that the two builds write the same bytes."""
+    that the two builds write the same bytes.  With a LaunchLog ``L`` (a counter pass) nothing
+    is timed: each case's calls run as one item per build (``abl_<build>_<case>``)."""
     import numpy as np
     import torch
 
     from mxfp8_block_scaled_partial_amd import binding as B
     from mxfp8_block_scaled_partial_amd import build as hip_build
+    from mxfp8_block_scaled_partial_amd import bytes_model as BM
     from mxfp8_block_scaled_partial_amd import workloads as wl
 
     libs = {"compile_time": B.lib(), "runtime_guard": B.load_library(hip_build.GUARDS_LIB)}
@@ -1098,19 +1110,36 @@ def ablation(args, dev, rounds=3):
                 for kname in ("amax", "cast"):
                     # same bytes from both builds (set 0, outputs cleared before each)
                     outs = []
-                    for name, L in libs.items():
-                        b = sets[0]
-                        for t in (b["ar"], b["ac"], b["drb"], b["dcb"]):
-                            t.zero_()
-                        f = getattr(L, f"mxfp8_partial_{kname}")
-                        assert f(arrs[kname][0], 1, torch.cuda.current_stream().cuda_stream) == 0
-                        torch.cuda.synchronize()
-                        outs.append([t.clone() for t in (b["ar"], b["ac"], b["drb"], b["dcb"])])
+
+                    def check(_):
+                        for name, lb in libs.items():
+                            b = sets[0]
+                            for t in (b["ar"], b["ac"], b["drb"], b["dcb"]):
+                                t.zero_()
+                            f = getattr(lb, f"mxfp8_partial_{kname}")
+                            assert f(arrs[kname][0], 1,
+                                     torch.cuda.current_stream().cuda_stream) == 0
+                            torch.cuda.synchronize()
+                            outs.append([t.clone() for t in (b["ar"], b["ac"], b["drb"], b["dcb"])])
+                    if L is not None:
+                        L.run(f"abl_check_{kname}_{dtype}_{run}_{colwise}", 1, 0, check, aux=True)
+                    else:
+                        check(0)
                     same = all(torch.equal(a, c) for a, c in zip(*outs))
+                    key = f"{kname}_{dtype}_{run}_{'bidirectional' if colwise else 'rowonly'}"
+                    if L is not None:
+                        assert same, key
+                        nb_alg = BM.piece_bytes(rows, cols, s, l, s_in, colwise)[kname]
+                        for name, lib in libs.items():
+                            f = getattr(lib, f"mxfp8_partial_{kname}")
+                            L.run(f"abl_{name}_{key}", args.counter_calls, nb_alg,
+                                  lambda i, f=f, a=arrs[kname]: f(
+                                      a[i % n_sets], 1, torch.cuda.current_stream().cuda_stream))
+                        continue
                     times = {name: [] for name in libs}
                     for _ in range(rounds):
-                        for name, L in libs.items():
-                            f = getattr(L, f"mxfp8_partial_{kname}")
+                        for name, lb in libs.items():
+                            f = getattr(lb, f"mxfp8_partial_{kname}")
 
                             def fn(i, f=f, a=arrs[kname]):
                                 assert f(a[i % n_sets], 1,
@@ -1118,7 +1147,6 @@ def ablation(args, dev, rounds=3):
                             times[name].append(per_call_us(args, fn, 10))
                     ct = statistics.median(times["compile_time"])
                     rg = statistics.median(times["runtime_guard"])
-                    key = f"{kname}_{dtype}_{run}_{'bidirectional' if colwise else 'rowonly'}"
                     out[key] = {"compile_time_us": round(ct, 2), "runtime_guard_us": round(rg, 2),
                                 "ratio": round(rg / ct, 3), "same_bytes": same,
                                 "buffer_sets": n_sets}

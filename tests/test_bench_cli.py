@@ -90,6 +90,9 @@ def _synthetic_run():
     disp += [(COPY, 131072, 512, KIB / 4, KIB / 2, 50.0), (FILL, 4, 256, 1, 1, 1.0),
              (MARK, 1, 256, 0, 0, 1.0)]
     disp += [(CAST, 50, 256, 1000, 1000, 10.0), (CAST, 50, 256, 1000, 1000, 12.0)] * 2
+    # an aux item (a check between measured items): it only delimits
+    items.append({"label": "abl_check_x", "calls": 1, "alg_bytes": 0, "aux": True})
+    disp += [(MARK, 1, 256, 0, 0, 1.0), (CAST, 50, 256, 7, 7, 3.0), (AMAX, 60, 256, 7, 7, 3.0)]
     items.append({"label": "layer_k_buffers_amax", "calls": 1, "alg_bytes": 3000 * 1024})
     disp += [(MARK, 1, 256, 0, 0, 1.0), (AMAX, 60, 256, 1500, 50, 20.0),
              (AMAX_ROW, 40, 256, 1000, 30, 15.0)]
@@ -137,7 +140,7 @@ def test_counter_summary_attributes_dispatches_to_the_manifest(tmp_path):
     # per launch = per call / launches per call
     assert per["cast_bf16_full"] == (2 * 2000 + 2000) * 1024 // 2
     assert per["layer_k_buffers_amax"] == (2 * 2500 + 80) * 1024 // 2
-    assert "copy_probe" not in per
+    assert "copy_probe" not in per and "abl_check_x" not in per
     assert "| cast_bf16_full | `cast_vec_kernel<bf16, true, false, false, 2, false>` | 2 | 2 |" \
         in text
     assert ("| layer_k_buffers_amax | `amax_vec_kernel<bf16, true, false, 2>`, "
@@ -167,6 +170,7 @@ def test_trace_summary_reports_kernel_time_per_call(tmp_path):
     layer = [l for l in text.splitlines() if l.startswith("| layer_k_buffers_amax |")][0]
     assert "| 35.00 |" in layer
     assert "median of 24 launches: 100.00 µs" in text
+    assert "abl_check_x" not in text
     assert "--kernel-trace --stats" in text
 
 
@@ -181,7 +185,7 @@ def test_counter_summary_refuses_a_manifest_that_does_not_match(tmp_path):
         json.dump(man, open(tmp_path / f"r_{k}.json", "w"))
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-counters",
                         str(tmp_path / "r")], capture_output=True, text=True, timeout=120)
-    assert r.returncode != 0 and "9 marked spans, 8 manifest items" in r.stderr
+    assert r.returncode != 0 and "10 marked spans, 9 manifest items" in r.stderr
 
 
 def test_roofline_traffic_is_read_per_step_configuration(tmp_path, monkeypatch):
