@@ -361,6 +361,18 @@ def _commands(man, run, kinds, what):
     return out, name
 
 
+def _workload(man):
+    """What a --counter-pass run covered, from its manifest."""
+    argv = man["argv"]
+    w = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
+         + ("fused scales + cast" if man["fused"] else "scales then cast"))
+    extra = [what for flag, on, what in (
+        ("--no-kernel-table", False, "the per-call table"),
+        ("--no-layer-batch", False, "the layer batch"),
+        ("--ablation", True, "the runtime-guard ablation")) if (flag in argv) == on]
+    return w + ("; " + ", ".join(extra) if extra else "")
+
+
 def _write(args, md):
     text = "\n".join(md)
     if args.out:
@@ -417,8 +429,7 @@ def summarize_counters(args):
         lines.append(f"| {label} | {kname} | {lpc} | {n} | {fk:.0f} | {wk:.0f} | "
                      f"{rd / 1e6:.2f} | {wr / 1e6:.2f} | {(rd + wr) / 1e6:.2f} | {alg / 1e6:.2f} | "
                      f"{(rd + wr) / alg:.4f} |" + (f" {w64:.4f} |" if has_w else ""))
-    workload = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
-                + ("fused scales + cast" if man["fused"] else "scales then cast"))
+    workload = _workload(man)
     block = {"workload": workload, "dtype": man["dtype"], "fused": man["fused"],
              "kernel_source_sha256_16": man["kernel_source_sha256_16"],
              "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
@@ -488,8 +499,7 @@ def summarize_trace(args):
                      f"{gbs:.1f} | {gbs / HBM_PEAK_GBS:.4f} |")
     cp = statistics.median(disp[i]["us"] for i in probe)
     cmds, name = _commands(man, run, ["trace"], (("trace", None),))
-    workload = (f"16384x6144 {man['dtype']} step, 4 fragments, bidirectional, "
-                + ("fused scales + cast" if man["fused"] else "scales then cast"))
+    workload = _workload(man)
     md = [f"# Kernel durations per call: rocprofv3 kernel trace, {workload}", "",
           "One MI355X (gfx950), ROCm 7.2.  `bench.py --counter-pass` runs every launch untimed "
           "in a fixed order, a marker kernel before each item, and writes that order to a "
