@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 CAST_SAMPLE = 4  # timed steps per cast-duration sample
+CPU_LEG_SECONDS = 10.0  # CPU work of the oracle leg, one thread
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for partial amax + cast"
 KERNEL_SRC = os.path.join(ROOT, "mxfp8_block_scaled_partial_amd", "csrc", "kernels.hip")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -1396,9 +1397,14 @@ def cpu_baseline(m, cpu_rows, s_in, gpu=None):
     frags = [(cuts[i], cuts[i + 1] - cuts[i]) for i in range(4)]
     x = m.data[:n]
     oracle.lib()
+    # the one-thread leg repeats the whole sample until about 10 s of CPU work have run
     t0 = time.perf_counter()
     want = oracle.writeback(x, rows, cols, frags, colwise=True)
-    dt = time.perf_counter() - t0
+    reps = 1
+    while time.perf_counter() - t0 < CPU_LEG_SECONDS:
+        oracle.writeback(x, rows, cols, frags, colwise=True)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
     check = "not run (sample is not the whole weight)"
     if gpu is not None:
         import numpy as np
@@ -1432,16 +1438,21 @@ def cpu_baseline(m, cpu_rows, s_in, gpu=None):
         oracle.writeback(x[lo:hi], r1 - r0, cols, pieces, colwise=True)
 
     t0 = time.perf_counter()
+    reps_all = 0
     with ThreadPoolExecutor(cores) as ex:
-        list(ex.map(group, range(cores)))
-    dt_all = time.perf_counter() - t0
+        while reps_all == 0 or time.perf_counter() - t0 < CPU_LEG_SECONDS / 4:
+            list(ex.map(group, range(cores)))
+            reps_all += 1
+    dt_all = (time.perf_counter() - t0) / reps_all
     sample = (f"first {rows} of 16384 rows ({rows}x{cols}, {n} elements), 4 fragments, whole "
               "path (amax, combine, scales, cast), C oracle")
     return {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": round(dt, 2), "sample": sample + ", one thread",
+            "seconds": round(dt * reps, 2), "runs": reps,
+            "sample": sample + f", one thread, {reps} runs of the sample",
             "gpu_step_vs_oracle": check,
             "all_cores": {"value": round(total / dt_all / 1e9, 3), "unit": "GB/s",
-                          "cores": cores, "seconds": round(dt_all, 2),
+                          "cores": cores, "seconds": round(dt_all * reps_all, 2),
+                          "runs": reps_all,
                           "sample": sample + f", {cores} threads over groups of 32-row bands"},
             "host_cpus": len(os.sched_getaffinity(0)), "host_cpu_model": cpu_model()}
 
