@@ -186,10 +186,10 @@ int mxfp8_check_call(const mxfp8_piece* pieces, int n, int kernel);
  * as fragment-sized outputs) while cols is a multiple of 128 and both outputs share their
  * offset within a line, 0 = the element-wise path (other cols), negative = the piece fails
  * validation (the status code, negated).
- * Host-only; launches nothing.  For a BF16 input 2 bytes past a 4-byte boundary the
- * vectorized path reads, never writes, the 2 bytes that share a 4-byte word with the first
- * and with the last input element, and ignores them; no kernel reads anything else outside
- * the fragment. */
+ * Host-only; launches nothing.  For a BF16 input the vectorized path may read, never writes,
+ * the other 2 bytes of the 4-byte word that holds the fragment's first element and of the one
+ * that holds its last element, and ignores them; no kernel reads anything else outside the
+ * fragment. */
 int mxfp8_query_path(const mxfp8_piece* piece, int kernel);
 
 #ifdef __cplusplus
