@@ -14,8 +14,9 @@ left in the 256 MB Infinity Cache.
 
 Prints one JSON line: ``value`` is the step's algorithmic HBM bytes / wall time (GB/s);
 ``roofline`` is for the dominant kernel (the cast, or with ``--fused`` the fused one), from
-timing-only HIP events (no system-scope fence) recorded on the launch stream around the cast
-call of every fourth timed step;
+timing-only HIP events (no system-scope fence) that the runtime stamps at the cast kernel's
+start and end on every fourth timed step (and, for comparison, events recorded on the launch
+stream around the call on the steps halfway between);
 ``kernels`` is the per-call table (partial amax, partial cast and the fused scales + cast;
 full input and the quarter fragment at offset 17, BF16 and FP32; at 16384x6144 also the quarter
 fragment in one rank's own buffers, ``*_partial_own``: input and fragment-sized outputs in
@@ -600,9 +601,10 @@ def main():
     stage_names = [name for name, _ in sets[0][2].stages()]
     stages = [s[2].stages() for s in sets]
 
-    def step(i, ev=None, cast_ev=None):
-        """One step; ``ev`` times every stage (the breakdown pass), ``cast_ev`` only the cast
-        (the timed steps: each event marker costs the stream a few µs)."""
+    def step(i, ev=None, cast_ev=None, kernel_ev=None):
+        """One step; ``ev`` times every stage (the breakdown pass), ``cast_ev`` brackets the
+        cast call with markers on the stream, ``kernel_ev`` has the library stamp the cast's
+        own kernel start and end (the timed steps: each marker costs the stream a few µs)."""
         seq = stages[i % n_sets][:-1] + [stages[(i - 1) % n_sets][-1]]
         last = len(seq) - 1
         for j, (_, fn) in enumerate(seq):
@@ -610,6 +612,8 @@ def main():
                 ev[j].record()
             if cast_ev is not None and j == last:
                 cast_ev[0].record()
+            if kernel_ev is not None and j == last:
+                B.mxfp8_time_next_call(kernel_ev[0].ev.value, kernel_ev[1].ev.value)
             fn()
         if ev is not None:
             ev[-1].record()
@@ -625,20 +629,25 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # the timed steps: wall clock over all of them; HIP events around the cast launch of
-    # every CAST_SAMPLE-th step (each event marker costs the stream a few µs, so sampling
-    # keeps the measurement from lengthening the steps it measures)
+    # the timed steps: wall clock over all of them.  The cast call of every CAST_SAMPLE-th
+    # step is timed by HIP events that the runtime stamps at its kernel's start and end
+    # (mxfp8_time_next_call: hipExtLaunchKernel events), and that of the steps halfway between
+    # by events recorded on the stream around the call, which also hold its dispatch (each
+    # marker costs the stream a few µs, so sampling keeps the measurement from lengthening the
+    # steps it measures)
+    kev = {i: (TimingEvent(), TimingEvent()) for i in range(0, args.steps, CAST_SAMPLE)}
     cev = {i: (TimingEvent(), TimingEvent())
-           for i in range(0, args.steps, CAST_SAMPLE)}
+           for i in range(CAST_SAMPLE // 2, args.steps, CAST_SAMPLE)}
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, cast_ev=cev.get(i))
+        step(args.warmup + i, cast_ev=cev.get(i), kernel_ev=kev.get(i))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    cast_ms_mean = sum(a.elapsed_time(b) for a, b in cev.values()) / len(cev)
+    cast_ms_mean = sum(a.elapsed_time(b) for a, b in kev.values()) / len(kev)
+    cast_ms_bracket = sum(a.elapsed_time(b) for a, b in cev.values()) / len(cev)
 
     # the stage breakdown, from a separate pass with an event before every stage
     # (informational: the markers themselves lengthen that pass's steps)
@@ -666,6 +675,11 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname,
                 "launch_us": round(cast_launch_us, 2),
+                "launch_us_with_dispatch": round(cast_ms_bracket * 1e3 / n_cast, 2),
+                "timing": f"mean over {len(kev)} timed steps of HIP events stamped at the "
+                          "cast kernel's start and end (hipExtLaunchKernel); "
+                          "launch_us_with_dispatch: events recorded around the call on the "
+                          f"stream, {len(cev)} other timed steps",
                 "alg_bytes_per_launch": int(cast_bytes_launch)}
 
     # the same steps replayed from captured graphs (no host launch gaps)

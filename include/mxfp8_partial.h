@@ -169,6 +169,18 @@ int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream);
 /* Message for the calling thread's last non-OK status (static storage, thread-local). */
 const char* mxfp8_last_error(void);
 
+/* Times the kernels of the calling thread's next call of a launching entry point
+ * (mxfp8_partial_amax, mxfp8_combine_amax, mxfp8_compute_scales, mxfp8_partial_cast,
+ * mxfp8_scales_and_cast, mxfp8_quantize): start_event and stop_event are hipEvent_t handles
+ * the caller created (host pointers, caller-owned).  That call launches through
+ * hipExtLaunchKernel, and the runtime stamps start_event when the call's first kernel starts
+ * and stop_event when its last kernel ends, so hipEventElapsedTime gives the kernels' time
+ * without the dispatch around them.  The next such call consumes the events whether it
+ * launches, launches nothing (an empty call: the events stay unrecorded) or fails; both
+ * NULL cancels.  Not for a stream being captured into a graph.  Returns MXFP8_OK, or
+ * MXFP8_ERR_ARG if exactly one event is NULL.  Host-only; launches nothing. */
+int mxfp8_time_next_call(void* start_event, void* stop_event);
+
 /* Validates a whole call of entry point kernel = 0 (mxfp8_partial_amax), 1
  * (mxfp8_partial_cast), 2 (mxfp8_scales_and_cast), 3 (mxfp8_quantize) or 4
  * (mxfp8_compute_scales) exactly as that entry point does, every piece and the pieces

@@ -21,6 +21,12 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local mxfp8::CallEvents g_events;
+
+// Clears the timing events when an entry point returns: they time one call, launched or not.
+struct EventsOnce {
+  ~EventsOnce() { g_events = mxfp8::CallEvents{}; }
+};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -324,6 +330,7 @@ int validate_call(const mxfp8_piece* pieces, int n, Kind kind, std::vector<mxfp8
 
 template <typename Launch>
 int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch launch) {
+  const EventsOnce once;
   const char* fn = kKindName[kind];
   std::vector<mxfp8::Piece> todo;
   const int st = validate_call(pieces, n, kind, todo);
@@ -335,6 +342,10 @@ int run_pieces(const mxfp8_piece* pieces, int n, void* stream, Kind kind, Launch
 }
 
 }  // namespace
+
+namespace mxfp8 {
+CallEvents& call_events() { return g_events; }
+}  // namespace mxfp8
 
 extern "C" {
 
@@ -360,6 +371,7 @@ int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream) {
 
 int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
                        int32_t amax_dtype, void* hip_stream) {
+  const EventsOnce once;
   const char* fn = "mxfp8_combine_amax";
   if (amax_dtype != MXFP8_FP32 && amax_dtype != MXFP8_BF16)
     return fail(MXFP8_ERR_DTYPE, "%s: unknown amax_dtype %d", fn, amax_dtype);
@@ -387,6 +399,14 @@ int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
 }
 
 const char* mxfp8_last_error(void) { return g_err; }
+
+int mxfp8_time_next_call(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(MXFP8_ERR_ARG, "mxfp8_time_next_call: give both events or neither");
+  g_events.start = static_cast<hipEvent_t>(start_event);
+  g_events.stop = static_cast<hipEvent_t>(stop_event);
+  return MXFP8_OK;
+}
 
 int mxfp8_check_call(const mxfp8_piece* pieces, int n, int kernel) {
   if (kernel < 0 || kernel > 4)

@@ -36,6 +36,7 @@
 //    for BF16, cols % 4 != 0 for FP32) run an element-wise kernel: one lane per column, same
 //    band tiling, same results.  Any alignment of input and outputs stays on the vector path
 //    (dword loads with a 2-byte realign, window stores).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -2180,6 +2181,21 @@ size_t cap_lds(K kernel, int cap) {
 // for the vector kernels (a workgroup per tile) and kWavesPerGroup for the element-wise ones
 // (a wave per tile).  Launches under kSmallLaunchTiles tiles run `small_kernel`; the others
 // run `kernel`, held at `cap` resident workgroups per CU (0: no cap).
+// One kernel launch.  With a call being timed (mxfp8_time_next_call) the launch goes through
+// hipExtLaunchKernel, whose events the runtime stamps when the kernel itself starts and ends:
+// the call's first kernel records the start event, every kernel the stop event.
+template <typename F, typename... A>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_t s, A... args) {
+  CallEvents& ev = call_events();
+  if (ev.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shm, s, ev.start, ev.stop, 0, args...);
+    ev.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  }
+  return hipGetLastError();
+}
+
 template <typename K>
 hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>& ps,
                           int tiles_per_wg, int cap, hipStream_t s) {
@@ -2202,8 +2218,7 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
       g.base = g0 * tiles_per_wg;
       const int64_t ng = std::min<int64_t>(kMaxLaunchGroups, groups - g0);
-      hipLaunchKernelGGL(k, dim3((unsigned)ng), dim3(kThreads), shm, s, g);
-      const hipError_t e = hipGetLastError();
+      const hipError_t e = launch_kernel(k, dim3((unsigned)ng), dim3(kThreads), shm, s, g);
       if (e != hipSuccess) return e;
     }
   }
@@ -2486,11 +2501,9 @@ hipError_t launch_compute_scales(const Piece* ps, int n, hipStream_t s) {
       }
       g.first[g.n] = (uint32_t)wg;
       if (wg == 0) continue;
-      if (bf16)
-        hipLaunchKernelGGL(scales_kernel<uint16_t>, dim3(wg), dim3(256), 0, s, g);
-      else
-        hipLaunchKernelGGL(scales_kernel<uint32_t>, dim3(wg), dim3(256), 0, s, g);
-      const hipError_t e = hipGetLastError();
+      const hipError_t e =
+          bf16 ? launch_kernel(scales_kernel<uint16_t>, dim3(wg), dim3(256), 0, s, g)
+               : launch_kernel(scales_kernel<uint32_t>, dim3(wg), dim3(256), 0, s, g);
       if (e != hipSuccess) return e;
     }
   }
@@ -2515,11 +2528,10 @@ hipError_t launch_combine(void* dst, const void* const* srcs, int k, int64_t cou
     a.vec = vec;
     const int64_t work = vec ? cdiv(count * esz, 16) : count;
     const int64_t groups = std::max<int64_t>(1, std::min<int64_t>(cdiv(work, 256), 256 * 16));
-    if (dtype == kBF16)
-      hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3((unsigned)groups), dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL(combine_kernel<uint32_t>, dim3((unsigned)groups), dim3(256), 0, s, a);
-    const hipError_t e = hipGetLastError();
+    const hipError_t e =
+        dtype == kBF16
+            ? launch_kernel(combine_kernel<uint16_t>, dim3((unsigned)groups), dim3(256), 0, s, a)
+            : launch_kernel(combine_kernel<uint32_t>, dim3((unsigned)groups), dim3(256), 0, s, a);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

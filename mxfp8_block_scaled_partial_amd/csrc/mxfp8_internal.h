@@ -42,6 +42,14 @@ bool cast_fast_ok(const Piece& p);
 // Whether the plain cast takes the line-owned tiles.
 bool cast_lines_ok(const Piece& p);
 
+// Kernel timing of one call (mxfp8_time_next_call), this thread's: while `stop` is set, every
+// launch records it when its kernel ends, and the first one records `start` when its kernel
+// starts (then `start` is cleared).  The entry point that consumes them clears both.
+struct CallEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+CallEvents& call_events();
+
 // Pieces sharing a kernel specialization go out in as few launches as possible.
 hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s);
 hipError_t launch_partial_cast(const Piece* ps, int n, hipStream_t s);

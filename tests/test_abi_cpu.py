@@ -462,3 +462,19 @@ def test_query_path_reports_line_owned_cast_tiles():
     # rows that are not whole lines
     assert q(raw_piece(rows=64, cols=192, start=17, length=1000, data_row=BASE + 0x50000000,
                        data_col=BASE + 0x60000000), 1) == 1
+
+
+def test_call_timing_needs_both_events_or_neither():
+    """mxfp8_time_next_call arms the next launching call with a start and a stop event; one
+    without the other is an argument error, and both NULL cancels.  An empty call consumes
+    the events without launching anything."""
+    L = B.lib()
+    fake = ctypes.c_void_p(BASE)
+    assert L.mxfp8_time_next_call(fake, None) == B.ERR_ARG
+    assert "both events" in B.mxfp8_last_error()
+    assert L.mxfp8_time_next_call(None, fake) == B.ERR_ARG
+    assert L.mxfp8_time_next_call(None, None) == B.OK
+    # armed, then consumed by an empty call (nothing launched, no event touched)
+    assert L.mxfp8_time_next_call(fake, fake) == B.OK
+    assert L.mxfp8_partial_amax(None, 0, None) == B.OK
+    assert L.mxfp8_time_next_call(None, None) == B.OK
