@@ -601,7 +601,7 @@ __device__ __forceinline__ RowClass<RW> classify_rows(const TileArgs& p, int64_t
 }
 
 // Rows of an edge tile (as classified), masked to the fragment, in d (elements outside it
-// are 0).  The whole chunks' loads go out first, then the element loads of the cut chunks, and
+// are 0).  The whole chunks' loads go out first, then the word loads of the cut chunks, and
 // only then is anything assembled.
 template <typename T, int RW>
 __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,

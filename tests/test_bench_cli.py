@@ -211,3 +211,17 @@ def test_roofline_traffic_is_read_per_step_configuration(tmp_path, monkeypatch):
     assert bench.traffic_from_counters("fp32", False, "step_cast") == 22
     assert bench.traffic_from_counters("bf16", True, "step_scales_cast") == 33
     assert bench.traffic_from_counters("fp32", True, "step_scales_cast") is None
+
+
+def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+
+    src = open(bench.KERNEL_SRC).read()
+    base = bench.kernel_sha()
+    f = tmp_path / "k.hip"
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(f))
+    f.write_text(src.replace("// ", "//  note: ", 3) + "\n/* a new\n   comment */\n")
+    assert bench.kernel_sha() == base
+    f.write_text(src.replace("kBlockLen", "kBlockLen + 0", 1))
+    assert bench.kernel_sha() != base

@@ -78,6 +78,26 @@ def test_tiny_fragments(start, length, dtype):
         assert_same(got, want, rows, cols, f"{inputs}: ")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("inputs", ["views", "own"])
+@pytest.mark.parametrize("base", ["mid_row", "row_end"])
+def test_cut_at_every_position_of_a_chunk(dtype, inputs, base):
+    """Two fragments cut at every element position of two 16-byte chunks (both 4-byte word
+    parities for BF16): the edge tiles load each cut chunk as the words that hold its
+    fragment elements, and the two fragments merge the cut blocks."""
+    rows, cols = 64, 256
+    n = rows * cols
+    E = 8 if dtype == "bf16" else 4
+    b0 = 37 * cols + 64 if base == "mid_row" else 38 * cols - 2 * E
+    x = wl.random_matrix(rows, cols, dtype, seed=11 + cols, kind="mixed")
+    for j in range(2 * E):
+        cut = b0 + j
+        frags = [(0, cut), (cut, n - cut)]
+        want = oracle.writeback(x, rows, cols, frags, True)
+        got = run_matrix(x, rows, cols, frags, True, inputs=inputs, shared=False)
+        assert_same(got, want, rows, cols, f"cut {cut}: ")
+
+
 def test_vector_and_element_paths_are_both_exercised():
     x = torch.zeros(64 * 64, dtype=torch.bfloat16, device=DEV)
     ar = torch.zeros(64, 2, dtype=torch.bfloat16, device=DEV)
