@@ -112,6 +112,9 @@ def parse():
                     help="(no GPU) summarize the rocprofv3 --kernel-trace run of a "
                          "--counter-pass workload (RUN_trace/ and RUN_trace.json) as markdown, "
                          "to --out")
+    ap.add_argument("--summarize-stats", metavar="DIR", default=None,
+                    help="(no GPU) summarize a rocprofv3 --kernel-trace --stats run of the "
+                         "benchmark (DIR, with its JSON line in DIR.log) as markdown, to --out")
     ap.add_argument("--out", default=None)
     return ap.parse_args()
 
@@ -526,6 +529,83 @@ def summarize_trace(args):
     _write(args, md)
 
 
+STATS_NAMES = {"FillFunctor<c10::BFloat16>": "torch fill, bf16 (zero-fill of the packed amax buffers)",
+               "FillFunctor<float>": "torch fill, fp32 (zero-fill of the packed amax buffers)",
+               "FillFunctor<unsigned char>": "torch fill, u8 (buffer set-up)",
+               "FillFunctor<long>": "torch fill, i64 (set-up)",
+               "__amd_rocclr_copyBuffer": "__amd_rocclr_copyBuffer (device copy: the 256 MiB copy "
+                                          "probe and the input-set clones)"}
+
+
+def summarize_stats(args):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of the benchmark: the kernel
+    durations of ``DIR/*_kernel_stats.csv``, the same run's JSON line (``DIR.log``) and the
+    dominant kernel's kernel-only fraction of peak."""
+    import csv
+
+    d = args.summarize_stats.rstrip("/")
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_stats.csv under {d}, found {files}")
+    rows = list(csv.DictReader(open(files[0])))
+    b = json.loads([ln for ln in open(d + ".log") if ln.startswith("{")][-1])
+    fused = "fused" in b["roofline"]["kernel"]
+    t = "unsigned short" if b["dtype"] == "bf16" else "unsigned int"
+    pattern = f"cast_vec_kernel<{t}, true, false, {'true' if fused else 'false'}"
+    dom = [r for r in rows if pattern in r["Name"]]
+    if len(dom) != 1:
+        raise SystemExit(f"no single {pattern} row in {files[0]}")
+    avg = float(dom[0]["AverageNs"]) / 1e3
+    alg = b["roofline"]["alg_bytes_per_launch"]
+    argv = ([] if b["dtype"] == "bf16" else ["--dtype", b["dtype"]]) + (["--fused"] if fused else [])
+    if b["steps"] != 200:
+        argv += ["--steps", str(b["steps"])]
+    if b["warmup"] != 1000:
+        argv += ["--warmup", str(b["warmup"])]
+    for key, flag in (("kernels", "--no-kernel-table"), ("cpu_baseline", "--no-cpu-baseline"),
+                      ("single_pass_step", "--no-single-pass"), ("layer_batch", "--no-layer-batch")):
+        if key not in b:
+            argv.append(flag)
+    if "ablation" in b:
+        argv.append("--ablation")
+    name = os.path.basename(d)
+    cmd = (f"cd /tmp && export TMPDIR=/tmp && timeout -k 10 600 rocprofv3 --kernel-trace --stats "
+           f"--output-format csv -d $R/gpurun_out/stats/{name} -o step -- python -u $R/bench.py "
+           f"{' '.join(argv)}")
+
+    def label(n):
+        for k, v in STATS_NAMES.items():
+            if k in n:
+                return v
+        return "`" + _short_kernel(n) + "`"
+    md = [f"# Kernel durations: rocprofv3 --kernel-trace --stats, {b['config']['rows']}x"
+          f"{b['config']['cols']} {b['dtype'].upper()} writeback step", "",
+          f"Workload: {b['config']['workload']}; {b['warmup']} warm-up and {b['steps']} timed steps, "
+          "then the stage-breakdown pass and the steps replayed from graphs, plus the copy probe.  "
+          "One MI355X (gfx950), ROCm 7.2 ($R is the repository root on the GPU box):", "", "```",
+          cmd + f" > $R/gpurun_out/stats/{name}.log 2>&1", "```", "",
+          f"This summary is `python bench.py --summarize-stats gpurun_out/stats/{name} --out <this "
+          "file>`.  From `step_kernel_stats.csv` (µs):", "",
+          "| kernel | calls | average | min | max |", "|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {label(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                  f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    rl = b["roofline"]
+    md += ["", "The same run's `bench.py` line (under the profiler, whose serialization slows every "
+           "launch a little and the event-marked ones more): stage breakdown pass (µs, an event "
+           "before every stage) " + ", ".join(f"{k} {v}" for k, v in
+                                              b["stage_us_breakdown_pass"].items())
+           + f"; one step replayed from a graph {b['graph_us_per_step']} µs; the cast from the "
+           f"events stamped at its kernel's start and end {rl['launch_us']} µs, from markers "
+           f"around the call {rl.get('launch_us_with_dispatch')} µs.", "",
+           f"Kernel only, the step's cast moves {alg / 1e6:.1f} MB (algorithmic) in {avg:.2f} µs on "
+           f"average = {alg / (avg * 1e-6) / 1e12:.2f} TB/s ({alg / (avg * 1e-6) / 8e12 * 100:.1f}% of "
+           "8 TB/s).  `roofline.achieved` divides the same bytes by the mean of the kernel-stamped "
+           "events over the timed steps.", "",
+           f"Kernel source: `kernels.hip` sha256 prefix `{kernel_sha()}`.", ""]
+    _write(args, md)
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -533,6 +613,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_stats:
+        summarize_stats(args)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -225,3 +225,35 @@ def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
     assert bench.kernel_sha() == base
     f.write_text(src.replace("kBlockLen", "kBlockLen + 0", 1))
     assert bench.kernel_sha() != base
+
+
+def test_stats_summary_reads_the_kernel_stats_and_the_bench_line(tmp_path):
+    import csv
+    import json
+
+    d = tmp_path / "step_bf16"
+    os.makedirs(d / "host")
+    with open(d / "host" / "step_kernel_stats.csv", "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+                    "StdDev"])
+        w.writerow([CAST, 10, 730000, 73000.0, 50.0, 70000, 76000, 1.0])
+        w.writerow([AMAX, 10, 360000, 36000.0, 25.0, 35000, 37000, 1.0])
+        w.writerow([FILL, 11, 88000, 8000.0, 5.0, 7000, 9000, 1.0])
+    line = {"dtype": "bf16", "steps": 200, "warmup": 1000,
+            "config": {"rows": 16384, "cols": 6144, "workload": "a step"},
+            "roofline": {"kernel": "cast_vec_kernel<bf16, colwise>", "launch_us": 73.1,
+                         "launch_us_with_dispatch": 75.0, "alg_bytes_per_launch": 408944694},
+            "stage_us_breakdown_pass": {"cast": 74.0}, "graph_us_per_step": 141.0}
+    (tmp_path / "step_bf16.log").write_text("noise\n" + json.dumps(line) + "\n")
+    out = tmp_path / "s.md"
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--summarize-stats",
+                        str(d), "--out", str(out)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    text = out.read_text()
+    assert "| `cast_vec_kernel<bf16, true, false, false, 2, false>` | 10 | 73.00 | 70.00 | 76.00 |" \
+        in text
+    assert "in 73.00 µs on average = 5.60 TB/s (70.0% of 8 TB/s)" in text
+    # the benchmark's command, rebuilt from the sections its JSON line lacks
+    assert ("python -u $R/bench.py --no-kernel-table --no-cpu-baseline --no-single-pass "
+            "--no-layer-batch > $R/gpurun_out/stats/step_bf16.log 2>&1") in text
