@@ -112,19 +112,25 @@ struct TileArgs {
   int32_t shift;   // line-owned cast tiles: flat offset of every tile column (0 elsewhere)
   int32_t row_pair, col_pair;  // BF16 amax rows start on 4-byte boundaries: entries 2k, 2k + 1
                                // share an aligned 32-bit word
+  int64_t tile0;   // tiles of the piece that earlier launches of its group covered
 };
 
 // One launch covers up to kMaxGroup pieces that share a kernel specialization: tiles are
-// numbered piece after piece, first[k] being the first tile of piece k.  A group with more
-// than kMaxLaunchGroups workgroups goes out as several launches, base being the tile of the
-// launch's first workgroup, so no grid comes near the 2^32 work-items a dispatch can hold.
+// numbered piece after piece.  A group with more than kMaxLaunchGroups workgroups goes out as
+// several launches, so no grid comes near the 2^32 work-items a dispatch can hold.  first[k]
+// is the first tile of piece k counted from the launch's first workgroup: 0 for a piece that
+// an earlier launch of the group began (its tile0 then counts the tiles already covered), and
+// kNoPiece for one that starts after the launch and for the unused entries (k >= n).  A launch
+// holds fewer than 2^31 tiles, so every entry is below 2^31.  The header comes first and is
+// 68 bytes, so one scalar load fetches it.
 constexpr int kMaxGroup = 16;
 constexpr int64_t kMaxLaunchGroups = int64_t(1) << 20;
+constexpr uint32_t kNoPiece = 0x7FFFFFFFu;  // beyond every tile of a launch
+static_assert(kMaxLaunchGroups * kWavesPerGroup < kNoPiece, "tiles of a launch below kNoPiece");
 struct GroupArgs {
-  TileArgs piece[kMaxGroup];
-  int64_t first[kMaxGroup + 1];
-  int64_t base;
+  uint32_t first[kMaxGroup];
   int32_t n;
+  TileArgs piece[kMaxGroup];
 };
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -170,19 +176,60 @@ __device__ __forceinline__ uint32_t round_bf16_bits(uint32_t u) {
 }
 
 // Dispatch round-robins consecutive workgroup ids over the XCDs; renumber them so that each
-// XCD works through one contiguous range of tiles.
-__device__ __forceinline__ int64_t xcd_remap(int64_t wg, int64_t nwg) {
-  const int64_t per = nwg / kNumXcd, rem = nwg % kNumXcd;
-  const int64_t xcd = wg % kNumXcd, idx = wg / kNumXcd;
-  const int64_t base = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
-  return base + idx;
+// XCD works through one contiguous range of tiles: XCD x takes per + 1 ids if x < rem, else
+// per, starting at x * per + min(x, rem).  32-bit and branch-free (a launch holds at most
+// kMaxLaunchGroups workgroups).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t wg, uint32_t nwg) {
+  const uint32_t per = nwg / kNumXcd, rem = nwg % kNumXcd;
+  const uint32_t xcd = wg % kNumXcd, idx = wg / kNumXcd;
+  return xcd * per + min(xcd, rem) + idx;
 }
 
-// Piece of a grouped launch that global tile t belongs to (uniform: a scalar loop).
-__device__ __forceinline__ int piece_of(const GroupArgs& g, int64_t t) {
-  int k = 0;
-  while (k + 1 < g.n && t >= g.first[k + 1]) ++k;
-  return k;
+// The fields of a piece that a tile's first loads depend on, held in scalar registers at one
+// point: the compiler then issues their scalar loads together and waits once.  Left to itself
+// it puts each load next to its first use, often behind a branch of its own, and every such
+// load is one more round trip before the tile's first global load; in a launch of one round
+// all workgroups start cold and wait for each of them.
+__device__ __forceinline__ void pin_tile_fields(const GroupArgs& g, int k) {
+  const TileArgs& p = g.piece[k];
+  asm volatile("" ::"s"(g.first[k]), "s"(p.tile0), "s"(p.rows), "s"(p.cols), "s"(p.start),
+               "s"(p.end), "s"(p.input), "s"(p.band0), "s"(p.ntc), "s"(p.ntiles),
+               "s"(p.in_shift2), "s"(p.shift));
+}
+
+// The same for the cast, plus what its common tile's path test and scale loads read.
+__device__ __forceinline__ void pin_cast_fields(const GroupArgs& g, int k) {
+  const TileArgs& p = g.piece[k];
+  asm volatile("" ::"s"(g.first[k]), "s"(p.tile0), "s"(p.rows), "s"(p.cols), "s"(p.start),
+               "s"(p.end), "s"(p.input), "s"(p.band0), "s"(p.ntc), "s"(p.ntiles),
+               "s"(p.in_shift2), "s"(p.shift), "s"(p.nt_row), "s"(p.nt_col), "s"(p.sc_vec),
+               "s"(p.scale_row), "s"(p.ld_sr), "s"(p.scale_col), "s"(p.ld_sc));
+}
+
+// The launch's header and grid size, held in scalar registers at one point (one batch of
+// scalar loads, one round trip) ahead of the workgroup's tile and piece.
+__device__ __forceinline__ void pin_header(const GroupArgs& g) {
+  asm volatile("" ::"s"(gridDim.x), "s"(g.first[1]), "s"(g.first[2]), "s"(g.first[3]),
+               "s"(g.first[4]), "s"(g.first[5]), "s"(g.first[6]), "s"(g.first[7]),
+               "s"(g.first[8]), "s"(g.first[9]), "s"(g.first[10]), "s"(g.first[11]),
+               "s"(g.first[12]), "s"(g.first[13]), "s"(g.first[14]), "s"(g.first[15]));
+  static_assert(kMaxGroup == 16, "pin_header names every entry of first[] after the first");
+}
+
+// Piece of a grouped launch that tile t of the launch belongs to: the number of later pieces
+// whose first tile is at or before t (first[] never decreases, unused entries never match).
+// Uniform, and branch-free over all kMaxGroup entries, so the header arrives in one scalar
+// load: a loop over the pieces waited for one load per piece before the tile's first global
+// load.  Every entry and t are below 2^31, so first[j] - t - 1 is negative exactly when
+// first[j] <= t, and its sign bit counts the piece: three scalar instructions per entry (a
+// comparison turned into a count went through vector registers, and the extra prologue time
+// of every workgroup cost the full-size cast 1%).
+__device__ __forceinline__ int piece_of(const GroupArgs& g, uint32_t t) {
+  const uint32_t nt = ~t;  // first[j] - t - 1 == first[j] + ~t
+  uint32_t k = 0;
+#pragma unroll
+  for (int j = 1; j < kMaxGroup; ++j) k += (g.first[j] + nt) >> 31;
+  return (int)k;
 }
 
 // ------------------------------------------------------------------ amax entries
@@ -716,13 +763,16 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;  // uniform over the workgroup
-  const int64_t band = p.band0 + tile / p.ntc;
-  const int64_t c0 = (tile % p.ntc) * WC;
+  const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
+  const int64_t band = p.band0 + bq;
+  const int64_t c0 = (int64_t)(t32 - bq * n32) * WC;
   const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen;
   const bool cvalid = c < p.cols;
@@ -731,9 +781,11 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   // A tile holding a row's short last block (cols % 32 != 0) takes the edge path, whose entry
-  // writes go through LDS: the interior path's per-lane writes assume whole blocks.
-  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end &&
-                        (p.cols % kBlockLen == 0 || c0 + WC <= p.cols);
+  // writes go through LDS: the interior path's per-lane writes assume whole blocks.  The tests
+  // are joined with & rather than &&: every field they read is then loaded in one batch, where
+  // a branch per test cost a scalar round trip each before the tile's first global load.
+  const bool interior = (nrows == kBlockLen) & (tile_first >= p.start) & (tile_end <= p.end) &
+                        ((p.cols % kBlockLen == 0) | (c0 + WC <= p.cols));
   const bool colw = kCol && (!kGuard || p.amax_col != nullptr);  // column-wise entries
 
   uint32_t col[4] = {0, 0, 0, 0};
@@ -1290,10 +1342,12 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_cast_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;  // uniform over the workgroup
   const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
   const int64_t band = p.band0 + bq;
@@ -1305,6 +1359,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const int i0 = wave * RW;
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
+  // (with && rather than &: the fields are pinned already, and & slowed the edge tiles by
+  // 0.3 µs in a call of one round)
   const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
   static_assert(!(kGuard && kFuse), "the runtime-guard ablation covers the plain cast");
   const bool colw = kCol && (!kGuard || p.data_col != nullptr);  // column-wise output
@@ -1472,10 +1528,12 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
   const int lane = threadIdx.x & (kWaveSize - 1);
   // uniform over the wave: row addresses stay in scalar registers, a lane adds its offset
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;  // uniform over the workgroup
   const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
   const int64_t vband = p.band0 + bq;  // virtual band; -1 holds row 0's first delta columns
@@ -1487,7 +1545,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
   const int64_t cu = u + p.shift;
   const int64_t tile_first = v0 * p.cols + p.shift + u0;
   const int64_t tile_last = (v0 + kBlockLen - 1) * p.cols + p.shift + min<int64_t>(u0 + WC, p.cols) - 1;
-  const bool interior = tile_first >= p.start && tile_last < p.end;
+  const bool interior = (tile_first >= p.start) & (tile_last < p.end);
   const bool last_tc = u0 + WC >= p.cols;  // the column tile whose chunks reach the next row
 
   // Where the lane's chunk lies, the same for every row: wholly in the next row (wrap), across
@@ -1605,10 +1663,12 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x);
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;  // uniform over the workgroup
   const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
   const int64_t band = p.band0 + bq;
@@ -1727,10 +1787,12 @@ __global__ __launch_bounds__(kThreads) void amax_elem_kernel(GroupArgs ga) {
   // the wave index is uniform over the wave: readfirstlane lets the compiler keep the tile's
   // indices and addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * kElemTileCols;
@@ -1787,10 +1849,12 @@ __global__ __launch_bounds__(kThreads) void cast_elem_kernel(GroupArgs ga) {
   // the wave index is uniform over the wave: readfirstlane lets the compiler keep the tile's
   // indices and addresses in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c0 = (tile % p.ntc) * kElemTileCols;
@@ -1850,10 +1914,12 @@ template <typename T, bool kCol, bool kPre>
 __global__ __launch_bounds__(kThreads) void quantize_elem_kernel(GroupArgs ga) {
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t gtile = ga.base + xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
-  const int k = piece_of(ga, gtile);
+  pin_header(ga);
+  const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerGroup + wave;
+  const int k = piece_of(ga, lt);
   const TileArgs& p = ga.piece[k];
-  const int64_t tile = gtile - ga.first[k];
+  pin_tile_fields(ga, k);
+  const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;
   const int64_t band = p.band0 + tile / p.ntc;
   const int64_t c = (tile % p.ntc) * kElemTileCols + lane;
@@ -2202,21 +2268,27 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
   for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
     GroupArgs g{};
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
-    int64_t total = 0;
+    int64_t first[kMaxGroup], total = 0;
     for (int k = 0; k < g.n; ++k) {
       if (ps[i0 + k].ntiles > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;  // 32-bit tile ids
       g.piece[k] = ps[i0 + k];
-      g.first[k] = total;
+      first[k] = total;
       // element-wise tiles start on a workgroup boundary so each workgroup has one piece
       total += cdiv(g.piece[k].ntiles, tiles_per_wg) * tiles_per_wg;
     }
-    g.first[g.n] = total;
     const int64_t groups = cdiv(total, tiles_per_wg);
     const bool small = total < kSmallLaunchTiles;
     const K k = small ? small_kernel : kernel;
     const size_t shm = small ? 0 : cap_lds(k, cap);
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
-      g.base = g0 * tiles_per_wg;
+      // the pieces' first tiles counted from this launch's first workgroup (see GroupArgs)
+      const int64_t base = g0 * tiles_per_wg;
+      for (int j = g.n; j < kMaxGroup; ++j) g.first[j] = kNoPiece;
+      for (int j = 0; j < g.n; ++j) {
+        const int64_t f = first[j] - base;
+        g.first[j] = f <= 0 ? 0u : (f >= (int64_t)kNoPiece ? kNoPiece : (uint32_t)f);
+        g.piece[j].tile0 = f < 0 ? -f : 0;
+      }
       const int64_t ng = std::min<int64_t>(kMaxLaunchGroups, groups - g0);
       const hipError_t e = launch_kernel(k, dim3((unsigned)ng), dim3(kThreads), shm, s, g);
       if (e != hipSuccess) return e;
