@@ -28,7 +28,6 @@ from __future__ import annotations
 import argparse
 import ctypes
 import glob
-import hashlib
 import json
 import os
 import re
@@ -205,12 +204,21 @@ class TimingEvent:
 
 
 def kernel_sha() -> str:
-    """Hash of the kernel source without its comments and blank space (no string literal in
-    it holds a comment marker), so that a counter summary stays valid across comment edits."""
-    text = open(KERNEL_SRC).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+    """Hash of the kernel source without its comments and blank space, so that a counter
+    summary stays valid across comment edits; the build embeds the same hash in the library
+    (mxfp8_build_id)."""
+    from mxfp8_block_scaled_partial_amd import build as hip_build
+
+    return hip_build.kernel_source_hash(KERNEL_SRC)
+
+
+def library_matches_source() -> tuple:
+    """(build id of the loaded library, whether it was built from the current kernel
+    source): a library left over from another source would measure other kernels."""
+    from mxfp8_block_scaled_partial_amd import binding as B
+
+    bid = B.mxfp8_build_id()
+    return bid, bid == kernel_sha()
 
 
 def counter_blocks():
@@ -223,11 +231,14 @@ def counter_blocks():
     return out
 
 
-def traffic_from_counters(dtype: str, fused: bool, label: str):
+def traffic_from_counters(dtype: str, fused: bool, label: str, library_id: str | None = None):
     """Calibrated HBM bytes per launch of the step stage ``label`` (e.g. ``step_cast``) from the
     committed counter summary of the same step (dtype, fused), if it was taken on the current
-    kernel source; None otherwise."""
+    kernel source and (``library_id``: the running library's build id) the running library was
+    built from it; None otherwise."""
     sha = kernel_sha()
+    if library_id is not None and library_id != sha:
+        return None
     for d in counter_blocks():
         if (d.get("dtype"), d.get("fused")) == (dtype, fused) and \
                 d.get("kernel_source_sha256_16") == sha and label in d.get("hbm_bytes_per_launch", {}):
@@ -602,7 +613,9 @@ def summarize_stats(args):
            f"average = {alg / (avg * 1e-6) / 1e12:.2f} TB/s ({alg / (avg * 1e-6) / 8e12 * 100:.1f}% of "
            "8 TB/s).  `roofline.achieved` divides the same bytes by the mean of the kernel-stamped "
            "events over the timed steps.", "",
-           f"Kernel source: `kernels.hip` sha256 prefix `{kernel_sha()}`.", ""]
+           f"Kernel source: `kernels.hip` sha256 prefix "
+           f"`{b.get('library', {}).get('build_id', kernel_sha())}` (the build id the library "
+           "reported).", ""]
     _write(args, md)
 
 
@@ -708,6 +721,14 @@ def main():
         if cast_ev is not None:
             cast_ev[1].record()
 
+    lib_id, lib_ok = library_matches_source()
+    if not lib_ok:
+        if args.counter_pass:
+            raise SystemExit(f"the library was built from kernel source {lib_id}, not from the "
+                             f"current {kernel_sha()}: rebuild it before a counter pass")
+        log(f"WARNING: the library was built from kernel source {lib_id}, not from the current "
+            f"{kernel_sha()}; roofline.traffic stays null")
+
     if args.counter_pass:
         counter_pass(args, stages, n_sets, stage_bytes, m, dev)
         return
@@ -758,7 +779,7 @@ def main():
     cast_launch_us = cast_ms_mean * 1e3 / n_cast
     cast_bytes_launch = stage_bytes[cast_stage] / n_cast
     achieved = cast_bytes_launch / (cast_launch_us * 1e-6) / 1e9
-    traffic = traffic_from_counters(args.dtype, bool(args.fused), "step_" + cast_stage)
+    traffic = traffic_from_counters(args.dtype, bool(args.fused), "step_" + cast_stage, lib_id)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "kernel": kname,
@@ -794,6 +815,7 @@ def main():
                                   else "scales, partial cast"),
                    "rows": rows, "cols": cols, "fragments": frags, "buffer_sets": n_sets,
                    "step_alg_bytes": step_bytes},
+        "library": {"build_id": lib_id, "kernel_source": kernel_sha(), "matches_source": lib_ok},
         "graph_us_per_step": graph_us,
         "graph_GBps": round(step_bytes / (graph_us * 1e-6) / 1e9, 1),
         "stage_us_breakdown_pass": {k: round(v * 1e3, 2) for k, v in stage_ms.items()},
@@ -924,7 +946,7 @@ def counter_pass(args, stages, n_sets, stage_bytes, m, dev):
     if args.ablation:
         ablation(args, dev, L=L)
     man = {"argv": sys.argv[1:], "dtype": args.dtype, "fused": bool(args.fused),
-           "kernel_source_sha256_16": kernel_sha(),
+           "kernel_source_sha256_16": library_matches_source()[0],
            "copy_probe": {"launches": COPY_PROBE_LAUNCHES, "read_bytes": COPY_PROBE_BYTES,
                           "write_bytes": COPY_PROBE_BYTES},
            "items": L.items}

@@ -169,6 +169,12 @@ int mxfp8_quantize(const mxfp8_piece* pieces, int n, void* hip_stream);
 /* Message for the calling thread's last non-OK status (static storage, thread-local). */
 const char* mxfp8_last_error(void);
 
+/* The kernel source this library was built from: 16 hex digits of SHA-256 over the kernel
+ * source with its comments and blank space removed, as the build computed it, or "unknown"
+ * for a build that did not set it.  Static storage; host-only.  For tying a measurement to
+ * the source it ran. */
+const char* mxfp8_build_id(void);
+
 /* Times the kernels of the calling thread's next call of a launching entry point
  * (mxfp8_partial_amax, mxfp8_combine_amax, mxfp8_compute_scales, mxfp8_partial_cast,
  * mxfp8_scales_and_cast, mxfp8_quantize): start_event and stop_event are hipEvent_t handles

@@ -28,7 +28,7 @@ STATUS_NAMES = {OK: "OK", ERR_ARG: "ERR_ARG", ERR_RANGE: "ERR_RANGE", ERR_DTYPE:
 # every entry point declared in include/mxfp8_partial.h
 EXPORTS = ("mxfp8_partial_amax", "mxfp8_combine_amax", "mxfp8_compute_scales",
            "mxfp8_partial_cast", "mxfp8_scales_and_cast", "mxfp8_quantize", "mxfp8_last_error",
-           "mxfp8_check_call", "mxfp8_query_path", "mxfp8_time_next_call")
+           "mxfp8_check_call", "mxfp8_query_path", "mxfp8_time_next_call", "mxfp8_build_id")
 
 # kernel numbers of mxfp8_check_call / mxfp8_query_path
 K_AMAX, K_CAST, K_SCALES_CAST, K_QUANTIZE, K_SCALES = range(5)
@@ -95,6 +95,8 @@ def load_library(path: str):
     L.mxfp8_query_path.restype = ctypes.c_int
     L.mxfp8_time_next_call.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     L.mxfp8_time_next_call.restype = ctypes.c_int
+    L.mxfp8_build_id.argtypes = []
+    L.mxfp8_build_id.restype = ctypes.c_char_p
     return L
 
 
@@ -273,6 +275,11 @@ def mxfp8_time_next_call(start_event: int, stop_event: int) -> None:
     """Times the kernels of this thread's next launching call with two hipEvent_t handles
     (raw handles, e.g. from hipEventCreateWithFlags; 0, 0 cancels)."""
     _check(lib().mxfp8_time_next_call(start_event or None, stop_event or None))
+
+
+def mxfp8_build_id(library=None) -> str:
+    """The kernel source hash the library (default: the loaded one) was built from."""
+    return (library or lib()).mxfp8_build_id().decode()
 
 
 def mxfp8_last_error() -> str:

@@ -10,7 +10,9 @@ only; the product is libmxfp8partial.so.
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,11 +35,23 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmxfp8partial.so)")
 
 
+def kernel_source_hash(path: str = os.path.join(CSRC, "kernels.hip")) -> str:
+    """16 hex digits of SHA-256 over the kernel source with its comments and blank space
+    removed (no string literal in it holds a comment marker): the identity of the kernels a
+    build holds, unchanged by comment edits.  The library reports the hash it was built from
+    (mxfp8_build_id), so measurements can be tied to the source they ran."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
+
+
 def flags(runtime_guards: bool = False) -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
             # packed FP32 instructions are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             f"-DMXFP8_RUNTIME_GUARDS={int(runtime_guards)}",
+            f'-DMXFP8_KERNEL_SOURCE_HASH="{kernel_source_hash()}"',
             "-Wall", "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 

@@ -400,6 +400,13 @@ int mxfp8_combine_amax(void* dst, const void* const* srcs, int k, int64_t count,
 
 const char* mxfp8_last_error(void) { return g_err; }
 
+// Set by the build (build.py) to the hash of the kernel source it compiled.
+#ifndef MXFP8_KERNEL_SOURCE_HASH
+#define MXFP8_KERNEL_SOURCE_HASH "unknown"
+#endif
+
+const char* mxfp8_build_id(void) { return MXFP8_KERNEL_SOURCE_HASH; }
+
 int mxfp8_time_next_call(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))
     return fail(MXFP8_ERR_ARG, "mxfp8_time_next_call: give both events or neither");

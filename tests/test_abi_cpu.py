@@ -478,3 +478,14 @@ def test_call_timing_needs_both_events_or_neither():
     assert L.mxfp8_time_next_call(fake, fake) == B.OK
     assert L.mxfp8_partial_amax(None, 0, None) == B.OK
     assert L.mxfp8_time_next_call(None, None) == B.OK
+
+
+def test_library_reports_the_kernel_source_it_was_built_from():
+    """mxfp8_build_id is the build's hash of the kernel source (comments and blank space
+    removed); the in-tree library must be built from the current source."""
+    from mxfp8_block_scaled_partial_amd import build as hip_build
+
+    bid = B.mxfp8_build_id(B.load_library(B.LIB_PATH))
+    assert re.fullmatch(r"[0-9a-f]{16}", bid), bid
+    assert bid == hip_build.kernel_source_hash(), (
+        "libmxfp8partial.so was built from another kernel source; rebuild it")

@@ -211,6 +211,9 @@ def test_roofline_traffic_is_read_per_step_configuration(tmp_path, monkeypatch):
     assert bench.traffic_from_counters("fp32", False, "step_cast") == 22
     assert bench.traffic_from_counters("bf16", True, "step_scales_cast") == 33
     assert bench.traffic_from_counters("fp32", True, "step_scales_cast") is None
+    # a running library built from another kernel source gets no counter traffic
+    assert bench.traffic_from_counters("bf16", False, "step_cast", sha) == 11
+    assert bench.traffic_from_counters("bf16", False, "step_cast", "0123456789abcdef") is None
 
 
 def test_kernel_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):

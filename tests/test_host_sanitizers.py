@@ -32,8 +32,11 @@ def sanitized(tmp_path_factory):
     d = tmp_path_factory.mktemp("sanitized")
     abi = str(d / "libmxfp8partial_san.so")
     orc = str(d / "libmxfp8_oracle_san.so")
+    from mxfp8_block_scaled_partial_amd import build as hip_build
+
     subprocess.check_call(
         ["g++", "-std=c++17", "-fPIC", "-shared", *SAN, "-D__HIP_PLATFORM_AMD__",
+         f'-DMXFP8_KERNEL_SOURCE_HASH="{hip_build.kernel_source_hash()}"',
          "-I/opt/rocm/include", f"-I{ROOT}/include", f"-I{CSRC}",
          os.path.join(CSRC, "abi.cpp"), os.path.join(CSRC, "paths.cpp"),
          os.path.join(ROOT, "tests", "sanitize", "launch_stubs.cpp"), "-o", abi])
