@@ -84,7 +84,9 @@ constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-lau
 // --ablation) runs the amax and the plain cast of rows of whole chunks through one kernel per
 // dtype for row-only and bidirectional calls, the column-wise work selected at run time by a
 // test of the column-wise pointer: the kernels the pages measured before the compile-time
-// specialization.  The product library (MXFP8_RUNTIME_GUARDS=0) never instantiates them.
+// specialization.  The product library (MXFP8_RUNTIME_GUARDS=0) takes those kernels only for
+// small calls that hold both directions (one_launch_for_both); everything else runs the
+// compile-time specialized kernels.
 constexpr bool kRuntimeGuards = MXFP8_RUNTIME_GUARDS != 0;
 
 struct TileArgs {
@@ -746,8 +748,9 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // Tiles wholly inside the fragment write their entries without reading them (each block has
 // a single owner); edge tiles write the entries of blocks the piece holds whole and merge
 // those of cut blocks atomically, since a neighbouring piece may share them.
-// kGuard (the runtime-guard ablation library only, with kCol = true): one kernel for both
-// kinds of call, its column-wise work selected at run time by the column-wise pointer.
+// kGuard (with kCol = true; the ablation library, and small calls holding both directions):
+// one kernel for both kinds of piece, its column-wise work selected at run time by the
+// column-wise pointer.
 template <typename T, bool kCol, bool kPre, int kOcc, bool kGuard = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
@@ -2325,6 +2328,23 @@ inline std::vector<TileArgs> both_directions(const Buckets& bk, int bf16, int pr
   return v;
 }
 
+// Whether a call's vector pieces of one element type hold both directions in fewer than
+// kSmallLaunchTiles tiles.  Such a call (one rank's share of a batch of row-only and
+// bidirectional weights) goes out as one launch of the kernel that selects the column-wise
+// work per piece at run time: one launch's fixed cost is most of a small call's time, and the
+// run-time selection costs little next to it (one rank's layer-batch fragment: amax 16.6 ->
+// 14.2 us, cast 21.8 -> 19.9 us).  Larger calls keep one compile-time specialized launch per
+// direction, which there measured faster (layer-batch cast 119.5 against 126.5 us).
+inline bool one_launch_for_both(const Buckets& bk, int bf16, int pre) {
+  const std::vector<TileArgs>& c = bk.b[bf16][1][pre][1];
+  const std::vector<TileArgs>& r = bk.b[bf16][0][pre][1];
+  if (c.empty() || r.empty()) return false;
+  int64_t tiles = 0;
+  for (const TileArgs& t : c) tiles += t.ntiles;
+  for (const TileArgs& t : r) tiles += t.ntiles;
+  return tiles < kSmallLaunchTiles;
+}
+
 template <typename T, bool kCol, bool kPre>
 hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
                               hipStream_t s) {
@@ -2380,6 +2400,22 @@ hipError_t launch_cast_guarded(const Buckets& bk, hipStream_t s) {
   return e;
 }
 
+// The casts of one element type and pre-round setting: with run-time guards (the ablation
+// library, or a small call holding both directions) one kernel for the vector pieces of both
+// directions, else one compile-time specialized launch per direction.
+template <typename T, bool kPre, bool kFuse>
+hipError_t launch_cast_dtype(const Buckets& bk, hipStream_t s) {
+  const int bf16 = sizeof(T) == 2, pre = kPre;
+  if constexpr (!kFuse) {
+    if (kRuntimeGuards || one_launch_for_both(bk, bf16, pre))
+      return launch_cast_guarded<T, kPre>(bk, s);
+  }
+  hipError_t e = launch_cast_bucket<T, true, kPre, kFuse>(bk.b[bf16][1][pre][1], bk.b[bf16][1][pre][0], s);
+  if (e == hipSuccess)
+    e = launch_cast_bucket<T, false, kPre, kFuse>(bk.b[bf16][0][pre][1], bk.b[bf16][0][pre][0], s);
+  return e;
+}
+
 template <bool kFuse>
 hipError_t launch_cast_pieces(const Piece* ps, int n, hipStream_t s) {
   Buckets bk, lines;  // lines: pieces of the plain cast that take the line-owned tiles
@@ -2395,18 +2431,9 @@ hipError_t launch_cast_pieces(const Piece* ps, int n, hipStream_t s) {
       bk.b[p.dtype == kBF16][p.data_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
   }
   hipError_t e = hipSuccess;  // each launch only if everything before it went out
-  if constexpr (kRuntimeGuards && !kFuse) {
-    if (e == hipSuccess) e = launch_cast_guarded<uint16_t, false>(bk, s);
-    if (e == hipSuccess) e = launch_cast_guarded<uint32_t, false>(bk, s);
-    if (e == hipSuccess) e = launch_cast_guarded<uint32_t, true>(bk, s);
-  } else {
-    if (e == hipSuccess) e = launch_cast_bucket<uint16_t, true, false, kFuse>(bk.b[1][1][0][1], bk.b[1][1][0][0], s);
-    if (e == hipSuccess) e = launch_cast_bucket<uint16_t, false, false, kFuse>(bk.b[1][0][0][1], bk.b[1][0][0][0], s);
-    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, true, false, kFuse>(bk.b[0][1][0][1], bk.b[0][1][0][0], s);
-    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, false, false, kFuse>(bk.b[0][0][0][1], bk.b[0][0][0][0], s);
-    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, true, true, kFuse>(bk.b[0][1][1][1], bk.b[0][1][1][0], s);
-    if (e == hipSuccess) e = launch_cast_bucket<uint32_t, false, true, kFuse>(bk.b[0][0][1][1], bk.b[0][0][1][0], s);
-  }
+  if (e == hipSuccess) e = launch_cast_dtype<uint16_t, false, kFuse>(bk, s);
+  if (e == hipSuccess) e = launch_cast_dtype<uint32_t, false, kFuse>(bk, s);
+  if (e == hipSuccess) e = launch_cast_dtype<uint32_t, true, kFuse>(bk, s);
   if constexpr (!kFuse) {
     if (e == hipSuccess) e = launch_lines_bucket<uint16_t, true, false>(lines.b[1][1][0][1], s);
     if (e == hipSuccess) e = launch_lines_bucket<uint16_t, false, false>(lines.b[1][0][0][1], s);
@@ -2436,23 +2463,23 @@ hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
   return e;
 }
 
-template <bool kGuards>
+// The amax of one element type and pre-round setting, dispatched as the cast's
+// (launch_cast_dtype).
+template <typename T, bool kPre>
+hipError_t launch_amax_dtype(const Buckets& bk, hipStream_t s) {
+  const int bf16 = sizeof(T) == 2, pre = kPre;
+  if (kRuntimeGuards || one_launch_for_both(bk, bf16, pre)) return launch_amax_guarded<T, kPre>(bk, s);
+  hipError_t e = launch_amax_bucket<T, true, kPre>(bk.b[bf16][1][pre][1], bk.b[bf16][1][pre][0], s);
+  if (e == hipSuccess) e = launch_amax_bucket<T, false, kPre>(bk.b[bf16][0][pre][1], bk.b[bf16][0][pre][0], s);
+  return e;
+}
+
 hipError_t launch_amax_buckets(const Buckets& bk, hipStream_t s) {
   hipError_t e = hipSuccess;  // each launch only if everything before it went out
-  if constexpr (kGuards) {
-    if (e == hipSuccess) e = launch_amax_guarded<uint16_t, false>(bk, s);
-    if (e == hipSuccess) e = launch_amax_guarded<uint32_t, false>(bk, s);
-    if (e == hipSuccess) e = launch_amax_guarded<uint32_t, true>(bk, s);
-    return e;
-  } else {
-    if (e == hipSuccess) e = launch_amax_bucket<uint16_t, true, false>(bk.b[1][1][0][1], bk.b[1][1][0][0], s);
-    if (e == hipSuccess) e = launch_amax_bucket<uint16_t, false, false>(bk.b[1][0][0][1], bk.b[1][0][0][0], s);
-    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, true, false>(bk.b[0][1][0][1], bk.b[0][1][0][0], s);
-    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, false, false>(bk.b[0][0][0][1], bk.b[0][0][0][0], s);
-    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, true, true>(bk.b[0][1][1][1], bk.b[0][1][1][0], s);
-    if (e == hipSuccess) e = launch_amax_bucket<uint32_t, false, true>(bk.b[0][0][1][1], bk.b[0][0][1][0], s);
-    return e;
-  }
+  if (e == hipSuccess) e = launch_amax_dtype<uint16_t, false>(bk, s);
+  if (e == hipSuccess) e = launch_amax_dtype<uint32_t, false>(bk, s);
+  if (e == hipSuccess) e = launch_amax_dtype<uint32_t, true>(bk, s);
+  return e;
 }
 
 hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
@@ -2463,7 +2490,7 @@ hipError_t launch_partial_amax(const Piece* ps, int n, hipStream_t s) {
     const int64_t width = vec ? kWaveSize * (16 / elem_size(p.dtype)) : kElemTileCols;
     bk.b[p.dtype == kBF16][p.amax_col != nullptr][p.preround][vec].push_back(tile_args(p, width));
   }
-  return launch_amax_buckets<kRuntimeGuards>(bk, s);
+  return launch_amax_buckets(bk, s);
 }
 
 template <typename T, bool kCol, bool kPre>
