@@ -79,6 +79,12 @@ struct Occupancy {
   }
 };
 constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-launch settings
+// Below these many tiles the cast splits its tiles (cast_vec_kernel's kSplit): 4 ways under
+// 1024 tiles, 8 ways under 64.  Measured (graph replays): 1024x1024 BF16 quarter 6.74 -> 3.12
+// us, 4096x4096 BF16 quarter 9.63 -> 6.38 us; an 8-way split of the 128 tiles of the 1024x1024
+// FP32 cast and a 4-way split of 1024 tiles or more ran slower.
+constexpr int64_t kSplit4Tiles = 1024;
+constexpr int64_t kSplit8Tiles = 64;
 
 // The runtime-guard ablation library (built with MXFP8_RUNTIME_GUARDS=1 by build.py
 // --ablation) runs the amax and the plain cast of rows of whole chunks through one kernel per
@@ -1218,17 +1224,16 @@ __device__ __forceinline__ void col_shifts_of(const TileArgs& p, const uint32_t 
 // (interior, dword-aligned outputs) takes its own straight-line block in cast_vec_kernel.  The
 // two kinds are separate instances, so that no edge tile's code follows a join with loads that
 // an interior tile would have in flight (the compiler would wait for those too).
-template <typename T, bool kCol, bool kPre, bool kFuse, bool kEdge>
+template <typename T, bool kCol, bool kPre, bool kFuse, bool kEdge, int kSplit = 1>
 __device__ __forceinline__ void cast_tile_general(
-    const TileArgs& p, int64_t band, int64_t c0, int64_t c, int i0, int nrows,
+    const TileArgs& p, int64_t band, int64_t r0, int64_t c0, int64_t c, int i0, int nrows,
     int (&cshift)[Chunk<T>::E], bool colw) {
   constexpr bool interior = !kEdge;
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
-  constexpr int RW = kRowsPerWave;
+  constexpr int RW = kRowsPerWave / kSplit;
   constexpr uint32_t kFull = (1u << E) - 1;
   const int lane = threadIdx.x & (kWaveSize - 1);
-  const int64_t r0 = band * kBlockLen;
   const bool cvalid = c < p.cols;
   const int64_t cend = min<int64_t>(c0 + WC, p.cols);
   const bool first = lane == 0, last = c + E == cend;
@@ -1336,14 +1341,19 @@ __device__ __forceinline__ void cast_tile_general(
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.  kGuard as for the amax (not fused): the column-wise work
 // follows a run-time test of data_col.  kScaleFirst (not fused): the common tile loads its
-// scale bytes before its input rows (see there).
+// scale bytes before its input rows (see there).  kSplit (not fused; launches too small to
+// fill the GPU): a workgroup takes 32 / kSplit rows of a band, wave w rows
+// (8 / kSplit) w ... , so each wave's serial work, an edge tile's above all, is kSplit times
+// shorter; tile t of a piece is then (sub-band t / ntc, column tile t % ntc).
 template <typename T, bool kCol, bool kPre, bool kFuse, int kOcc, bool kGuard = false,
-          bool kScaleFirst = false>
+          bool kScaleFirst = false, int kSplit = 1>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int WC = kWaveSize * E;
-  constexpr int RW = kRowsPerWave;
+  constexpr int RW = kRowsPerWave / kSplit;
+  constexpr int kTileRows = kBlockLen / kSplit;
+  static_assert(kSplit == 1 || (!kFuse && !kScaleFirst), "split tiles: the plain cast's small launches");
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
@@ -1355,18 +1365,19 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
   if (tile >= p.ntiles) return;  // uniform over the workgroup
   const uint32_t t32 = (uint32_t)tile, n32 = (uint32_t)p.ntc, bq = t32 / n32;
-  const int64_t band = p.band0 + bq;
+  const int64_t band = p.band0 + bq / kSplit;
   const int64_t c0 = (int64_t)(t32 - bq * n32) * WC;
   const int64_t c = c0 + lane * E;
-  const int64_t r0 = band * kBlockLen;
+  const int64_t r0 = band * kBlockLen + (int64_t)(bq % kSplit) * kTileRows;  // the tile's first row
+  if (kSplit > 1 && r0 >= p.rows) return;  // a short last band's missing rows (uniform)
   const bool cvalid = c < p.cols;
-  const int nrows = (int)min<int64_t>(kBlockLen, p.rows - r0);
+  const int nrows = (int)min<int64_t>(kTileRows, p.rows - r0);
   const int i0 = wave * RW;
   const int64_t tile_first = r0 * p.cols + c0;
   const int64_t tile_end = (r0 + nrows - 1) * p.cols + min<int64_t>(c0 + WC, p.cols);
   // (with && rather than &: the fields are pinned already, and & slowed the edge tiles by
   // 0.3 µs in a call of one round)
-  const bool interior = nrows == kBlockLen && tile_first >= p.start && tile_end <= p.end;
+  const bool interior = nrows == kTileRows && tile_first >= p.start && tile_end <= p.end;
   static_assert(!(kGuard && kFuse), "the runtime-guard ablation covers the plain cast");
   const bool colw = kCol && (!kGuard || p.data_col != nullptr);  // column-wise output
 
@@ -1466,9 +1477,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
     return;
   }
   if (interior)
-    cast_tile_general<T, kCol, kPre, kFuse, false>(p, band, c0, c, i0, nrows, cshift, colw);
+    cast_tile_general<T, kCol, kPre, kFuse, false, kSplit>(p, band, r0, c0, c, i0, nrows, cshift, colw);
   else
-    cast_tile_general<T, kCol, kPre, kFuse, true>(p, band, c0, c, i0, nrows, cshift, colw);
+    cast_tile_general<T, kCol, kPre, kFuse, true, kSplit>(p, band, r0, c0, c, i0, nrows, cshift, colw);
   if constexpr (kFuse && kCol) {
     if (wave == 0 && cvalid) store_col_scales<T>(p, band, c, nrows, interior, csb);
   }
@@ -2281,21 +2292,31 @@ hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_
 
 template <typename K>
 hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>& ps,
-                          int tiles_per_wg, int cap, hipStream_t s) {
+                          int tiles_per_wg, int cap, hipStream_t s, K split4_kernel = nullptr,
+                          K split8_kernel = nullptr) {
   for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
     GroupArgs g{};
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
     int64_t first[kMaxGroup], total = 0;
+    for (int k = 0; k < g.n; ++k) total += ps[i0 + k].ntiles;
+    // A launch of few tiles leaves most of the GPU idle: split4_kernel / split8_kernel take
+    // each tile as 4 / 8 smaller ones (cast_vec_kernel's kSplit), the pieces' tile counts
+    // scaled to match.
+    const int split = split8_kernel != nullptr && total < kSplit8Tiles   ? 8
+                      : split4_kernel != nullptr && total < kSplit4Tiles ? 4
+                                                                         : 1;
+    total = 0;
     for (int k = 0; k < g.n; ++k) {
-      if (ps[i0 + k].ntiles > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;  // 32-bit tile ids
       g.piece[k] = ps[i0 + k];
+      g.piece[k].ntiles *= split;
+      if (g.piece[k].ntiles > 0xFFFFFFFFll) return hipErrorInvalidConfiguration;  // 32-bit tile ids
       first[k] = total;
       // element-wise tiles start on a workgroup boundary so each workgroup has one piece
       total += cdiv(g.piece[k].ntiles, tiles_per_wg) * tiles_per_wg;
     }
     const int64_t groups = cdiv(total, tiles_per_wg);
     const bool small = total < kSmallLaunchTiles;
-    const K k = small ? small_kernel : kernel;
+    const K k = split == 8 ? split8_kernel : split == 4 ? split4_kernel : small ? small_kernel : kernel;
     const size_t shm = small ? 0 : cap_lds(k, cap);
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
       // the pieces' first tiles counted from this launch's first workgroup (see GroupArgs)
@@ -2366,10 +2387,14 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
   // large bidirectional BF16 launches load the scale bytes first (cast_vec_kernel's
   // kScaleFirst; the row-only cast measured 0.8% slower with it)
   constexpr bool kSF = sizeof(T) == 2 && kCol && !kFuse;
+  // launches too small to fill the GPU (not fused) cast split tiles (cast_vec_kernel's kSplit)
+  constexpr int kS4 = kFuse ? 1 : 4, kS8 = kFuse ? 1 : 8;
   if (!vec.empty())
     e = launch_grouped(cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, kSF>,
                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1,
-                       Occupancy<T>::cast_cap(kCol, kFuse), s);
+                       Occupancy<T>::cast_cap(kCol, kFuse), s,
+                       kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS4>,
+                       kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS8>);
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
                        elem, kWavesPerGroup, 0, s);
@@ -2393,7 +2418,9 @@ hipError_t launch_cast_guarded(const Buckets& bk, hipStream_t s) {
     e = launch_grouped(  // one kernel for both directions: it takes the bidirectional order
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, sizeof(T) == 2>,
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true>, v, 1,
-        Occupancy<T>::cast_cap(true, false), s);
+        Occupancy<T>::cast_cap(true, false), s,
+        cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4>,
+        cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8>);
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_cast_bucket<T, true, kPre, false>(none, bk.b[bf16][1][pre][0], s);
   if (e == hipSuccess) e = launch_cast_bucket<T, false, kPre, false>(none, bk.b[bf16][0][pre][0], s);

@@ -66,8 +66,11 @@ def test_timed_call_writes_the_same_bytes_and_sits_inside_the_markers():
 
 
 def test_a_call_of_two_kernels_is_timed_from_first_start_to_last_end():
-    """Row-only and bidirectional pieces go out as two launches; the interval covers both."""
-    m = wl.matrix_square("fp32", rows=4096, cols=4096)
+    """Row-only and bidirectional pieces of a large call (4096 tiles, well above the size
+    under which a call holding both directions goes out as one launch) go out as two launches;
+    the interval covers both.  Each launch timed alone also holds its own ramp-up and drain,
+    so the pair takes somewhat less than the sum."""
+    m = wl.matrix_square("fp32", rows=8192, cols=4096)
     n = m.rows * m.cols
     frags = [(0, n // 2), (n // 2, n // 2)]
     want, x, outs, pieces = _cast_pieces(m, frags, [True, False])
@@ -84,7 +87,7 @@ def test_a_call_of_two_kernels_is_timed_from_first_start_to_last_end():
     B.mxfp8_partial_cast(pieces)
     torch.cuda.synchronize()
     both = k0.elapsed_time(k1)
-    assert both >= 0.9 * sum(singles), (both, singles)
+    assert both > max(singles) and both >= 0.8 * sum(singles), (both, singles)
     for (s, l, dr, dc) in outs:
         assert np.array_equal(to_np(dr), want["data_row"][s:s + l])
         if dc is not None:
