@@ -85,6 +85,11 @@ constexpr int64_t kSmallLaunchTiles = 2048;  // below this many tiles: small-lau
 // FP32 cast and a 4-way split of 1024 tiles or more ran slower.
 constexpr int64_t kSplit4Tiles = 1024;
 constexpr int64_t kSplit8Tiles = 64;
+// Below this many tiles the amax, whose band must stay in one workgroup (its column-wise
+// blocks are 32 rows), takes wider workgroups instead: 8 waves of 4 rows.  Measured (graph
+// replays): 1024x1024 BF16 full 3.58 -> 3.38 us, quarter at offset 17 6.52 -> 5.89 us,
+// 4096x4096 FP32 quarter 7.06 -> 6.42 us; 16 waves of 2 rows ran 3-12% slower than 8.
+constexpr int64_t kAmax8Tiles = 1024;
 
 // The runtime-guard ablation library (built with MXFP8_RUNTIME_GUARDS=1 by build.py
 // --ablation) runs the amax and the plain cast of rows of whole chunks through one kernel per
@@ -756,18 +761,21 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // those of cut blocks atomically, since a neighbouring piece may share them.
 // kGuard (with kCol = true; the ablation library, and small calls holding both directions):
 // one kernel for both kinds of piece, its column-wise work selected at run time by the
-// column-wise pointer.
-template <typename T, bool kCol, bool kPre, int kOcc, bool kGuard = false>
-__global__ __launch_bounds__(kThreads)
+// column-wise pointer.  kWaves: the workgroup's waves, each taking 32 / kWaves rows of the
+// band (8 waves of 4 rows for launches too small to fill the GPU).
+template <typename T, bool kCol, bool kPre, int kOcc, bool kGuard = false,
+          int kWaves = kWavesPerGroup>
+__global__ __launch_bounds__(kWaveSize * kWaves)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int LB = kBlockLen / E;     // lanes sharing one row-wise block (4 BF16, 8 FP32)
   constexpr int WC = kWaveSize * E;     // tile width in columns
-  constexpr int RW = kRowsPerWave;
-  constexpr int NK = RW / LB;           // row maxima each lane keeps (2 BF16, 1 FP32)
+  constexpr int RW = kBlockLen / kWaves;  // rows of the band per wave (8; 4 with 8 waves)
+  constexpr int NK = RW >= LB ? RW / LB : 1;  // row maxima each lane keeps (2 BF16, 1 FP32)
   constexpr int NBLK = WC / kBlockLen;  // row-wise blocks across the tile (16 BF16, 8 FP32)
-  __shared__ uint4 s_col[kWavesPerGroup][kWaveSize];
-  __shared__ uint32_t s_touch[kWavesPerGroup][kWaveSize];
+  constexpr int kT = kWaveSize * kWaves;  // threads of the workgroup
+  __shared__ uint4 s_col[kWaves][kWaveSize];
+  __shared__ uint32_t s_touch[kWaves][kWaveSize];
   __shared__ uint32_t s_rmax[kBlockLen][NBLK];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
@@ -828,7 +836,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
         keep[i / LB] = m;
       }
     }
-    if (!rvec && cvalid) {
+    // (with fewer rows per wave than lanes per block, lane l keeps row l % LB if it has one)
+    if (!rvec && cvalid && (RW >= LB || lane % LB < RW)) {
 #pragma unroll
       for (int k = 0; k < NK; ++k) ar[(int64_t)k * LB * p.ld_ar] = (T)keep[k];
     }
@@ -849,7 +858,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     if (colw) {
       if (wave == 0 && cvalid) {
 #pragma unroll
-        for (int w = 1; w < kWavesPerGroup; ++w) fold_col<T>(col, s_col[w][lane]);
+        for (int w = 1; w < kWaves; ++w) fold_col<T>(col, s_col[w][lane]);
         if (p.col_vec) {
           *reinterpret_cast<uint4*>(ac) = make_uint4(col[0], col[1], col[2], col[3]);
         } else {
@@ -882,7 +891,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   // BF16 entries whose rows start on 4-byte boundaries: one thread per aligned word of two
   // entries (row-wise: blocks 2k, 2k + 1 of a row; column-wise: columns 2t, 2t + 1)
   constexpr bool kPairs = sizeof(T) == 2;
-  if (kPairs && p.row_pair) {
+  if (kPairs && p.row_pair && threadIdx.x < kBlockLen * (NBLK / 2)) {
     constexpr int PR = NBLK / 2;  // word pairs per row of the tile (8)
     const int row = threadIdx.x / PR, k2 = 2 * (threadIdx.x % PR);
     const int64_t r = r0 + row;
@@ -900,12 +909,15 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
                                                     (c0 >> 5) + k2),
                         s_rmax[row][k2] | (s_rmax[row][k2 + 1] << 16), mode[0], mode[1]);
   } else {
-    constexpr int kPer = kBlockLen * NBLK / kThreads;  // row entries per thread (2 or 1)
+    // row entries per thread (2 or 1 with 256 threads; threads past the tile's entries idle)
+    constexpr int kPer = kBlockLen * NBLK >= kT ? kBlockLen * NBLK / kT : 1;
     T* ptr[kPer];
     uint32_t v[kPer], act = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int e = threadIdx.x + j * kThreads;
+      const int e0 = threadIdx.x + j * kT;
+      const bool ok = e0 < kBlockLen * NBLK;
+      const int e = ok ? e0 : 0;
       const int row = e / NBLK, blk = e % NBLK;
       const int64_t r = r0 + row;
       const int64_t bc = c0 + blk * kBlockLen;  // the block's first column
@@ -913,7 +925,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
       ptr[j] = static_cast<T*>(p.amax_row) + r * p.ld_ar + (c0 >> 5) + blk;
       v[j] = s_rmax[row][blk];
-      if (row < nrows && bc < p.cols && gb < p.end && ge > p.start) {
+      if (ok && row < nrows && bc < p.cols && gb < p.end && ge > p.start) {
         if (gb >= p.start && ge <= p.end)
           *ptr[j] = (T)v[j];  // whole block: this tile is its only writer
         else
@@ -923,11 +935,13 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     atomic_max_entries<kPer>(ptr, v, act);
   }
   if (colw && kPairs && p.col_pair) {
-    const int cc = 2 * threadIdx.x;        // columns cc, cc + 1 within the tile (WC = 512)
+    const int cc0 = 2 * threadIdx.x;        // columns cc, cc + 1 within the tile (WC = 512)
+    const bool ok = cc0 < WC;               // threads past the tile's columns idle
+    const int cc = ok ? cc0 : 0;
     const int ln = cc / E, q = (cc % E) / 2;  // lane and dword of s_col holding both
     uint32_t m = 0, t = 0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w) {
+    for (int w = 0; w < kWaves; ++w) {
       const uint4 o = s_col[w][ln];
       const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
       m = pk_max_u16(m, ov[q]);
@@ -939,23 +953,25 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       const int64_t cg = c0 + cc + h;
       // the block's first and last elements decide whether the piece holds it whole
       const int64_t gf = r0 * p.cols + cg, gl = (r0 + nrows - 1) * p.cols + cg;
-      if (cg < p.cols && ((t >> (2 * q + h)) & 1u)) mode[h] = (gf >= p.start && gl < p.end) ? 1 : 2;
+      if (ok && cg < p.cols && ((t >> (2 * q + h)) & 1u)) mode[h] = (gf >= p.start && gl < p.end) ? 1 : 2;
     }
     if (mode[0] | mode[1])
       update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_col) + band * p.ld_ac +
                                                     c0 + cc),
                         m, mode[0], mode[1]);
   } else if (colw) {
-    constexpr int kPer = WC / kThreads;  // columns per thread (2 or 1)
+    constexpr int kPer = WC >= kT ? WC / kT : 1;  // columns per thread (2 or 1 with 256 threads)
     T* ptr[kPer];
     uint32_t v[kPer], act = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const int cc = threadIdx.x + j * kThreads;  // column within the tile
+      const int cc0 = threadIdx.x + j * kT;  // column within the tile
+      const bool ok = cc0 < WC;              // threads past the tile's columns idle
+      const int cc = ok ? cc0 : 0;
       const int ln = cc / E, e = cc % E;
       uint32_t m = 0, t = 0;
 #pragma unroll
-      for (int w = 0; w < kWavesPerGroup; ++w) {
+      for (int w = 0; w < kWaves; ++w) {
         const uint4 o = s_col[w][ln];
         const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
         m = umax(m, col_entry<T>(ov, e));
@@ -965,7 +981,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
       v[j] = m;
       // the block's first and last elements decide whether the piece holds it whole
       const int64_t gf = r0 * p.cols + c0 + cc, gl = (r0 + nrows - 1) * p.cols + c0 + cc;
-      if (c0 + cc < p.cols && ((t >> e) & 1u)) {
+      if (ok && c0 + cc < p.cols && ((t >> e) & 1u)) {
         if (gf >= p.start && gl < p.end)
           *ptr[j] = (T)m;
         else
@@ -2290,21 +2306,31 @@ hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_
   return hipGetLastError();
 }
 
+// A kernel for launches of fewer than `below` tiles: it takes each tile as `split` workgroups
+// of `threads` threads (the cast's split tiles, the amax's wide workgroups).
+template <typename K>
+struct Tier {
+  K kernel = nullptr;
+  int64_t below = 0;
+  int split = 1;
+  int threads = kThreads;
+};
+
 template <typename K>
 hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>& ps,
-                          int tiles_per_wg, int cap, hipStream_t s, K split4_kernel = nullptr,
-                          K split8_kernel = nullptr) {
+                          int tiles_per_wg, int cap, hipStream_t s, Tier<K> t1 = {},
+                          Tier<K> t2 = {}) {
   for (size_t i0 = 0; i0 < ps.size(); i0 += kMaxGroup) {
     GroupArgs g{};
     g.n = (int32_t)std::min<size_t>(kMaxGroup, ps.size() - i0);
     int64_t first[kMaxGroup], total = 0;
     for (int k = 0; k < g.n; ++k) total += ps[i0 + k].ntiles;
-    // A launch of few tiles leaves most of the GPU idle: split4_kernel / split8_kernel take
-    // each tile as 4 / 8 smaller ones (cast_vec_kernel's kSplit), the pieces' tile counts
-    // scaled to match.
-    const int split = split8_kernel != nullptr && total < kSplit8Tiles   ? 8
-                      : split4_kernel != nullptr && total < kSplit4Tiles ? 4
-                                                                         : 1;
+    // A launch of few tiles leaves most of the GPU idle: the first tier (t1, then t2) whose
+    // bound it stays under runs it, with the pieces' tile counts scaled by its split.
+    const Tier<K> tier = t1.kernel != nullptr && total < t1.below   ? t1
+                         : t2.kernel != nullptr && total < t2.below ? t2
+                                                                    : Tier<K>{};
+    const int split = tier.split;
     total = 0;
     for (int k = 0; k < g.n; ++k) {
       g.piece[k] = ps[i0 + k];
@@ -2316,7 +2342,7 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     }
     const int64_t groups = cdiv(total, tiles_per_wg);
     const bool small = total < kSmallLaunchTiles;
-    const K k = split == 8 ? split8_kernel : split == 4 ? split4_kernel : small ? small_kernel : kernel;
+    const K k = tier.kernel != nullptr ? tier.kernel : small ? small_kernel : kernel;
     const size_t shm = small ? 0 : cap_lds(k, cap);
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
       // the pieces' first tiles counted from this launch's first workgroup (see GroupArgs)
@@ -2328,7 +2354,7 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
         g.piece[j].tile0 = f < 0 ? -f : 0;
       }
       const int64_t ng = std::min<int64_t>(kMaxLaunchGroups, groups - g0);
-      const hipError_t e = launch_kernel(k, dim3((unsigned)ng), dim3(kThreads), shm, s, g);
+      const hipError_t e = launch_kernel(k, dim3((unsigned)ng), dim3(tier.threads), shm, s, g);
       if (e != hipSuccess) return e;
     }
   }
@@ -2373,7 +2399,9 @@ hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vecto
   if (!vec.empty())
     e = launch_grouped(amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmax>,
                        amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, vec, 1,
-                       Occupancy<T>::kAmaxCap, s);
+                       Occupancy<T>::kAmaxCap, s,
+                       {amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8>,
+                        kAmax8Tiles, 1, kWaveSize * 8});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, amax_elem_kernel<T, kCol, kPre>, elem,
                        kWavesPerGroup, 0, s);
@@ -2393,8 +2421,10 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
     e = launch_grouped(cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, kSF>,
                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1,
                        Occupancy<T>::cast_cap(kCol, kFuse), s,
-                       kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS4>,
-                       kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS8>);
+                       {kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS8>,
+                        kSplit8Tiles, kS8},
+                       {kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS4>,
+                        kSplit4Tiles, kS4});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
                        elem, kWavesPerGroup, 0, s);
@@ -2419,8 +2449,8 @@ hipError_t launch_cast_guarded(const Buckets& bk, hipStream_t s) {
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, sizeof(T) == 2>,
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true>, v, 1,
         Occupancy<T>::cast_cap(true, false), s,
-        cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4>,
-        cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8>);
+        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8>, kSplit8Tiles, 8},
+        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4>, kSplit4Tiles, 4});
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_cast_bucket<T, true, kPre, false>(none, bk.b[bf16][1][pre][0], s);
   if (e == hipSuccess) e = launch_cast_bucket<T, false, kPre, false>(none, bk.b[bf16][0][pre][0], s);
@@ -2482,7 +2512,9 @@ hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
   if (!v.empty())
     e = launch_grouped(amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmax, true>,
                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true>, v, 1,
-                       Occupancy<T>::kAmaxCap, s);
+                       Occupancy<T>::kAmaxCap, s,
+                       {amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8>,
+                        kAmax8Tiles, 1, kWaveSize * 8});
   // the element-wise kernels keep their compile-time specializations
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_amax_bucket<T, true, kPre>(none, bk.b[bf16][1][pre][0], s);
