@@ -1369,7 +1369,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int WC = kWaveSize * E;
   constexpr int RW = kRowsPerWave / kSplit;
   constexpr int kTileRows = kBlockLen / kSplit;
-  static_assert(kSplit == 1 || (!kFuse && !kScaleFirst), "split tiles: the plain cast's small launches");
+  static_assert(kSplit == 1 || !kScaleFirst, "split tiles: small launches");
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
@@ -1386,6 +1386,10 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   const int64_t c = c0 + lane * E;
   const int64_t r0 = band * kBlockLen + (int64_t)(bq % kSplit) * kTileRows;  // the tile's first row
   if (kSplit > 1 && r0 >= p.rows) return;  // a short last band's missing rows (uniform)
+  // (fused) the band's column-wise scale bytes are written once, by its first sub-tile, which
+  // tests every column block against the fragment over all the band's rows
+  const bool col_writer = kSplit == 1 || bq % kSplit == 0;
+  const int band_rows = (int)min<int64_t>(kBlockLen, p.rows - band * kBlockLen);
   const bool cvalid = c < p.cols;
   const int nrows = (int)min<int64_t>(kTileRows, p.rows - r0);
   const int i0 = wave * RW;
@@ -1488,7 +1492,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
       }
     }
     if constexpr (kFuse && kCol) {
-      if (wave == 0) store_col_scales<T>(p, band, c, nrows, true, csb);
+      if (wave == 0 && col_writer) store_col_scales<T>(p, band, c, band_rows, kSplit == 1, csb);
     }
     return;
   }
@@ -1497,7 +1501,8 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   else
     cast_tile_general<T, kCol, kPre, kFuse, true, kSplit>(p, band, r0, c0, c, i0, nrows, cshift, colw);
   if constexpr (kFuse && kCol) {
-    if (wave == 0 && cvalid) store_col_scales<T>(p, band, c, nrows, interior, csb);
+    if (wave == 0 && cvalid && col_writer)
+      store_col_scales<T>(p, band, c, band_rows, kSplit == 1 && interior, csb);
   }
 }
 
@@ -2415,16 +2420,15 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
   // large bidirectional BF16 launches load the scale bytes first (cast_vec_kernel's
   // kScaleFirst; the row-only cast measured 0.8% slower with it)
   constexpr bool kSF = sizeof(T) == 2 && kCol && !kFuse;
-  // launches too small to fill the GPU (not fused) cast split tiles (cast_vec_kernel's kSplit)
-  constexpr int kS4 = kFuse ? 1 : 4, kS8 = kFuse ? 1 : 8;
+  // launches too small to fill the GPU cast split tiles (cast_vec_kernel's kSplit)
   if (!vec.empty())
     e = launch_grouped(cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, kSF>,
                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1,
                        Occupancy<T>::cast_cap(kCol, kFuse), s,
-                       {kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS8>,
-                        kSplit8Tiles, kS8},
-                       {kFuse ? nullptr : cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, kS4>,
-                        kSplit4Tiles, kS4});
+                       {cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 8>,
+                        kSplit8Tiles, 8},
+                       {cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 4>,
+                        kSplit4Tiles, 4});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
                        elem, kWavesPerGroup, 0, s);
