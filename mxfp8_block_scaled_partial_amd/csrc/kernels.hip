@@ -1701,14 +1701,14 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
 // reduces the row-wise blocks with DPP and the column-wise blocks over the four waves in LDS,
 // and writes the amax (when requested), the E8M0 scales and the E4M3 data.  All loads are
 // issued before the first store.
-template <typename T, bool kCol, bool kPre, int kOcc>
-__global__ __launch_bounds__(kThreads)
+template <typename T, bool kCol, bool kPre, int kOcc, int kWaves = kWavesPerGroup>
+__global__ __launch_bounds__(kWaveSize * kWaves)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
   constexpr int LB = kBlockLen / E;
   constexpr int WC = kWaveSize * E;
-  constexpr int RW = kRowsPerWave;
-  __shared__ uint4 s_col[kWavesPerGroup][kWaveSize];
+  constexpr int RW = kBlockLen / kWaves;  // rows of the band per wave (8; 4 with 8 waves)
+  __shared__ uint4 s_col[kWaves][kWaveSize];
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
@@ -1749,7 +1749,7 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
     s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kWavesPerGroup; ++w)
+    for (int w = 0; w < kWaves; ++w)
       if (w != wave) fold_col<T>(col, s_col[w][lane]);
   }
 
@@ -2563,7 +2563,10 @@ hipError_t launch_quantize_bucket(const std::vector<TileArgs>& vec,
   if (!vec.empty())
     e = launch_grouped(quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>,
                        quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kCast>, vec, 1,
-                       Occupancy<T>::kQuantCap, s);
+                       Occupancy<T>::kQuantCap, s,
+                       // launches too small to fill the GPU: 8-wave workgroups, as the amax's
+                       {quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, 8>,
+                        kAmax8Tiles, 1, kWaveSize * 8});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(quantize_elem_kernel<T, kCol, kPre>, quantize_elem_kernel<T, kCol, kPre>,
                        elem, kWavesPerGroup, 0, s);
