@@ -125,6 +125,8 @@ struct TileArgs {
   int32_t shift;   // line-owned cast tiles: flat offset of every tile column (0 elsewhere)
   int32_t row_pair, col_pair;  // BF16 amax rows start on 4-byte boundaries: entries 2k, 2k + 1
                                // share an aligned 32-bit word
+  int32_t amax_own;  // no other piece of the launch has this piece's amax arrays: the BF16
+                     // merges of cut blocks are a load and a store, not compare-and-swap
   int64_t tile0;   // tiles of the piece that earlier launches of its group covered
 };
 
@@ -347,6 +349,109 @@ __device__ __forceinline__ void update_entry_pair(uint32_t* w, uint32_t v, int m
     if (prev == old) return;
     old = prev;
     known = true;
+  }
+}
+
+// Entry words: BF16 entry updates planned ahead of the data (the amax's narrow edge tiles).  An
+// entry is updated through the aligned 32-bit word that holds two of them.  An EntryWord names
+// that word and, per half h (bits 16h .. 16h + 15 of v), whether to store it (bit h of `set`:
+// the piece holds the block whole, so this thread is its only writer) or MAX-merge it (bit h
+// of `merge`: a fragment boundary cuts the block, so a neighbouring piece may share it).
+// Halves in neither mask are left alone.
+struct EntryWord {
+  uint32_t* w;
+  uint32_t v;
+  uint32_t set, merge;
+};
+
+// Half h of the word's value (0: none) for a lone entry p, with mode 1 (store) or 2 (merge).
+__device__ __forceinline__ EntryWord entry_half(uint16_t* p, uint32_t v, int mode) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const int h = (int)(a >> 1) & 1;
+  return EntryWord{reinterpret_cast<uint32_t*>(a & ~uintptr_t(3)), v << (16 * h),
+                   (uint32_t)(mode == 1) << h, (uint32_t)(mode == 2) << h};
+}
+
+// Both halves of the aligned word w (v: the low entry's value in bits 0-15, the high one's in
+// 16-31), with modes m0, m1 as for entry_half.
+__device__ __forceinline__ EntryWord entry_pair(uint16_t* w, uint32_t v, int m0, int m1) {
+  return EntryWord{reinterpret_cast<uint32_t*>(w), v,
+                   (uint32_t)(m0 == 1) | ((uint32_t)(m1 == 1) << 1),
+                   (uint32_t)(m0 == 2) | ((uint32_t)(m1 == 2) << 1)};
+}
+
+// The word that results from `old` under u.
+__device__ __forceinline__ uint32_t entry_word_update(uint32_t old, const EntryWord& u) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t o = (old >> (16 * h)) & 0xFFFFu, v = (u.v >> (16 * h)) & 0xFFFFu;
+    const uint32_t n = ((u.set >> h) & 1u) ? v : (((u.merge >> h) & 1u) ? umax(o, v) : o);
+    out |= n << (16 * h);
+  }
+  return out;
+}
+
+// Applies N entry words atomically, old[i] being a value of word i read earlier in the
+// launch.  Words without a merge are plain stores (32 or 16 bits).  The others go through
+// compare-and-swap expecting old[i], all issued before any result is awaited, so they cost one
+// round trip together; a word that already holds the result is left alone, and a swap that
+// finds another value (a neighbouring piece's merge, an entry of the word stored by another
+// thread) retries with it.
+template <int N>
+__device__ __forceinline__ void apply_entry_words(const EntryWord (&u)[N],
+                                                  const uint32_t (&old0)[N]) {
+  uint32_t old[N], pending = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    old[i] = old0[i];
+    if (u[i].merge) {
+      pending |= 1u << i;
+    } else if (u[i].set == 3u) {
+      *u[i].w = u[i].v;
+    } else if (u[i].set == 1u) {
+      *reinterpret_cast<uint16_t*>(u[i].w) = (uint16_t)u[i].v;
+    } else if (u[i].set == 2u) {
+      *(reinterpret_cast<uint16_t*>(u[i].w) + 1) = (uint16_t)(u[i].v >> 16);
+    }
+  }
+  while (pending) {
+    uint32_t prev[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      prev[i] = old[i];
+      if (!((pending >> i) & 1u)) continue;
+      const uint32_t nw = entry_word_update(old[i], u[i]);
+      if (nw == old[i])
+        pending &= ~(1u << i);  // the word already holds the result
+      else
+        prev[i] = global_cas(global_dword(reinterpret_cast<uintptr_t>(u[i].w)), old[i], nw);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (((pending >> i) & 1u) && prev[i] == old[i]) pending &= ~(1u << i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) old[i] = prev[i];
+  }
+}
+
+// Applies N entry words with plain stores, merges taken against old[i], the word's value at
+// the start of the launch: for a piece that no other piece of its launch shares amax arrays
+// with, every entry has one writer in the launch, and a launch runs after the work enqueued
+// before it.  Only the halves a word updates are stored.
+template <int N>
+__device__ __forceinline__ void store_entry_words(const EntryWord (&u)[N],
+                                                  const uint32_t (&old)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t act = u[i].set | u[i].merge;
+    const uint32_t nw = entry_word_update(old[i], u[i]);
+    if (act == 3u)
+      *u[i].w = nw;
+    else if (act == 1u)
+      *reinterpret_cast<uint16_t*>(u[i].w) = (uint16_t)nw;
+    else if (act == 2u)
+      *(reinterpret_cast<uint16_t*>(u[i].w) + 1) = (uint16_t)(nw >> 16);
   }
 }
 
@@ -704,6 +809,116 @@ __device__ __forceinline__ void load_rows_masked(const TileArgs& p, const T* src
   }
 }
 
+// The row classification of the amax's narrow edge tiles (8 waves of 4 rows), where the tile's
+// latency is the call's: as RowClass without the per-row masks (cut_mask derives them), and
+// computed without branches, so the rows' loads go out soon after the tile starts; the loads
+// are issued (issue_rows_masked) and assembled (assemble_rows_masked) apart, so the caller can
+// do what needs no data in between.
+template <int RW>
+struct RowCuts {
+  uint32_t full;      // bit i: row i's chunk lies wholly inside the fragment
+  int cut0, cut1;     // rows whose chunk a fragment boundary cuts (-1: none)
+  uint32_t m0, m1;    // their element masks (0: none)
+};
+
+// Row i's element mask (bit e: element e of its chunk lies in the fragment).
+template <typename T, int RW>
+__device__ __forceinline__ uint32_t cut_mask(const RowCuts<RW>& k, int i) {
+  constexpr uint32_t kAll = (1u << Chunk<T>::E) - 1;
+  return ((k.full >> i) & 1u) ? kAll : (i == k.cut0 ? k.m0 : (i == k.cut1 ? k.m1 : 0u));
+}
+
+// Rows i < nrows_here of the wave, chunk column c (as classify_rows).
+template <typename T, int RW>
+__device__ __forceinline__ RowCuts<RW> classify_cuts(const TileArgs& p, int64_t rfirst,
+                                                     int nrows_here, int64_t c, bool cvalid) {
+  constexpr int E = Chunk<T>::E;
+  RowCuts<RW> k;
+  k.full = 0;
+  k.cut0 = k.cut1 = -1;
+  const int64_t g0 = rfirst * p.cols + c;  // the first row's chunk
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int64_t g = g0 + i * p.cols;
+    const bool in = (i < nrows_here) & cvalid;
+    const bool whole = in & (g >= p.start) & (g + E <= p.end);
+    const bool cut = in & !whole & (g + E > p.start) & (g < p.end);
+    k.full |= (uint32_t)whole << i;
+    // a chunk column meets the fragment's two boundaries at most once each
+    const bool first = cut & (k.cut0 < 0);
+    const bool second = cut & !first;
+    k.cut1 = second ? i : k.cut1;
+    k.cut0 = first ? i : k.cut0;
+  }
+  // the cut chunks' masks: elements [lo, hi) of the chunk lie in the fragment (both in [0, E]
+  // for a cut chunk; for none the mask is 0)
+  auto mask = [&](int i) -> uint32_t {
+    const int64_t g = g0 + max(i, 0) * p.cols;
+    const int lo = g < p.start ? (int)(p.start - g) : 0;
+    const int hi = g + E > p.end ? (int)(p.end - g) : E;
+    const uint32_t m = ((1u << (hi & 31)) - 1) & ~((1u << (lo & 31)) - 1);
+    return i >= 0 ? m : 0u;
+  };
+  k.m0 = mask(k.cut0);
+  k.m1 = mask(k.cut1);
+  return k;
+}
+
+// The loads of an edge tile's rows in flight.
+template <int RW>
+struct MaskedRows {
+  RawChunk raw[RW];
+  RawChunk cr0, cr1;
+};
+
+// Issues the rows' loads as load_rows_masked does: the whole chunks' first (one uniform branch
+// on the 2-byte shift for all rows), then the word loads of the cut chunks.
+template <typename T, int RW>
+__device__ __forceinline__ void issue_rows_masked(const TileArgs& p, const T* src, int64_t rfirst,
+                                                  int64_t c, const RowCuts<RW>& k,
+                                                  MaskedRows<RW>& ml) {
+  constexpr int E = Chunk<T>::E;
+  const int64_t g_whole = p.start + ((((int64_t)p.shift - p.start) % E) + E) % E;
+  if (g_whole + E <= p.end) {
+    const T* whole = static_cast<const T*>(p.input) + (g_whole - p.start);
+    if (sizeof(T) == 2 && p.in_shift2) {
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        issue_chunk(((k.full >> i) & 1u) ? src + i * p.cols : whole, true, ml.raw[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RW; ++i)
+        issue_chunk(((k.full >> i) & 1u) ? src + i * p.cols : whole, false, ml.raw[i]);
+    }
+  }
+  issue_masked<T>(p, (rfirst + max(k.cut0, 0)) * p.cols + c, k.m0, ml.cr0);
+  issue_masked<T>(p, (rfirst + max(k.cut1, 0)) * p.cols + c, k.m1, ml.cr1);
+}
+
+// The rows in d, masked to the fragment (elements outside it are 0).
+template <typename T, int RW>
+__device__ __forceinline__ void assemble_rows_masked(const TileArgs& p, const RowCuts<RW>& k,
+                                                     const MaskedRows<RW>& ml,
+                                                     uint32_t (&d)[RW][4]) {
+  const bool s2 = sizeof(T) == 2 && p.in_shift2;
+  uint32_t c0d[4], c1d[4];
+  assemble_chunk(ml.cr0, s2, c0d);
+  assemble_chunk(ml.cr1, s2, c1d);
+  masked_chunk<T>(k.m0, c0d);
+  masked_chunk<T>(k.m1, c1d);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const bool whole = (k.full >> i) & 1u;
+    assemble_chunk(ml.raw[i], s2, d[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      d[i][j] = whole ? d[i][j] : 0u;
+      d[i][j] = i == k.cut0 ? c0d[j] : d[i][j];
+      d[i][j] = i == k.cut1 ? c1d[j] : d[i][j];
+    }
+  }
+}
+
 // Scale byte from the amax bit pattern: floor(log2 amax) = exponent field - 127 for normal
 // values, so the biased MX exponent is field - 8, clamped at 0 (subnormal and zero amax
 // included); the field is at most 254 for finite amax, so the upper clamp never applies.
@@ -870,125 +1085,227 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
     return;
   }
 
-  // Edge tile: a fragment boundary, the short last band or a row's short last block cuts it.
-  // Every wave loads its rows masked to the fragment; the row-wise and column-wise maxima meet
-  // in LDS and all 256 threads then write the touched entries, at most two of each kind per
-  // thread: blocks the piece holds whole are stored, blocks a fragment boundary cuts are
-  // merged atomically (all reads, then all swaps).
-  const RowClass<RW> rc = classify_rows<T, RW>(p, r0 + i0, nrows - i0, c, cvalid);
-  const uint32_t(&em)[RW] = rc.em;
-  load_rows_masked<T, RW>(p, src, r0 + i0, c, rc, d);
-  uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
-#pragma unroll
-  for (int i = 0; i < RW; ++i) {
-    const uint32_t m = group_max<LB>(chunk_absmax<T, kCol, kPre>(d[i], col));
-    if ((lane % LB) == 0) s_rmax[i0 + i][lane / LB] = m;
-    touched |= em[i];
-  }
-  s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
-  s_touch[wave][lane] = touched;
-  __syncthreads();
-  // BF16 entries whose rows start on 4-byte boundaries: one thread per aligned word of two
-  // entries (row-wise: blocks 2k, 2k + 1 of a row; column-wise: columns 2t, 2t + 1)
-  constexpr bool kPairs = sizeof(T) == 2;
-  if (kPairs && p.row_pair && threadIdx.x < kBlockLen * (NBLK / 2)) {
-    constexpr int PR = NBLK / 2;  // word pairs per row of the tile (8)
-    const int row = threadIdx.x / PR, k2 = 2 * (threadIdx.x % PR);
-    const int64_t r = r0 + row;
-    int mode[2] = {0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t bc = c0 + (k2 + h) * kBlockLen;  // the block's first column
-      const int64_t gb = r * p.cols + bc;
-      const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
-      if (row < nrows && bc < p.cols && gb < p.end && ge > p.start)
-        mode[h] = (gb >= p.start && ge <= p.end) ? 1 : 2;
-    }
-    if (mode[0] | mode[1])
-      update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_row) + r * p.ld_ar +
-                                                    (c0 >> 5) + k2),
-                        s_rmax[row][k2] | (s_rmax[row][k2 + 1] << 16), mode[0], mode[1]);
-  } else {
-    // row entries per thread (2 or 1 with 256 threads; threads past the tile's entries idle)
-    constexpr int kPer = kBlockLen * NBLK >= kT ? kBlockLen * NBLK / kT : 1;
-    T* ptr[kPer];
-    uint32_t v[kPer], act = 0;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e0 = threadIdx.x + j * kT;
-      const bool ok = e0 < kBlockLen * NBLK;
-      const int e = ok ? e0 : 0;
-      const int row = e / NBLK, blk = e % NBLK;
+  if constexpr (kWaves >= 8 && sizeof(T) == 2) {
+    // BF16 edge tile of a launch too small to fill the GPU, whose latency is the call's.  As
+    // below, but each thread (of 512) takes one row-wise and one column-wise entry word, planned
+    // from the geometry alone while the rows' loads are in flight: a word that takes a merge is
+    // loaded with the data (a word without one loads the tile's first row-wise entry word
+    // instead, so every load stays in bounds).  A piece that owns its amax arrays in the launch
+    // then stores its merges against those values, and no compare-and-swap round trip follows
+    // the data; otherwise the merges go through compare-and-swap, starting from them.
+    static_assert(kBlockLen * NBLK <= kT && WC <= kT, "one entry of each kind per thread");
+    const RowCuts<RW> rc = classify_cuts<T, RW>(p, r0 + i0, nrows - i0, c, cvalid);
+    MaskedRows<RW> ml;
+    issue_rows_masked<T, RW>(p, src, r0 + i0, c, rc, ml);
+    // Which update a block's entry takes: 0 none (no element of the fragment), 1 a store (the
+    // piece holds the block whole), 2 a merge (a fragment boundary cuts it).  A column-wise
+    // block's mode holds if the column has an element of the fragment in the band.
+    auto row_mode = [&](int row, int blk) -> int {
       const int64_t r = r0 + row;
       const int64_t bc = c0 + blk * kBlockLen;  // the block's first column
       const int64_t gb = r * p.cols + bc;
-      const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
-      ptr[j] = static_cast<T*>(p.amax_row) + r * p.ld_ar + (c0 >> 5) + blk;
-      v[j] = s_rmax[row][blk];
-      if (ok && row < nrows && bc < p.cols && gb < p.end && ge > p.start) {
-        if (gb >= p.start && ge <= p.end)
-          *ptr[j] = (T)v[j];  // whole block: this tile is its only writer
-        else
-          act |= 1u << j;
-      }
+      const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past it
+      if (!(row < nrows && bc < p.cols && gb < p.end && ge > p.start)) return 0;
+      return (gb >= p.start && ge <= p.end) ? 1 : 2;
+    };
+    auto col_mode = [&](int cc) -> int {
+      const int64_t cg = c0 + cc;
+      // the block's first and last elements decide whether the piece holds it whole
+      const int64_t gf = r0 * p.cols + cg, gl = (r0 + nrows - 1) * p.cols + cg;
+      if (cg >= p.cols) return 0;
+      return (gf >= p.start && gl < p.end) ? 1 : 2;
+    };
+    constexpr int PR = NBLK / 2;  // BF16 entry words per row of the tile (8)
+    const int t = threadIdx.x;
+    T* const arow = static_cast<T*>(p.amax_row) + r0 * p.ld_ar + (c0 >> 5);
+    T* const acol = static_cast<T*>(p.amax_col) + band * p.ld_ac + c0;
+    // the thread's row-wise entry (or aligned pair: blocks 2k, 2k + 1) and column-wise column
+    // (or aligned pair of columns 2t, 2t + 1); pairs where rows of the amax array start on
+    // 4-byte boundaries, so no two threads of the tile share a word
+    const bool rpair = p.row_pair, cpair = p.col_pair;
+    const bool rok = t < kBlockLen * (rpair ? PR : NBLK);
+    const int re = rok ? t : 0;
+    const int row = rpair ? re / PR : re / NBLK;
+    const int blk = rpair ? 2 * (re % PR) : re % NBLK;
+    const int cc0 = cpair ? 2 * t : t;
+    const bool cok = cc0 < WC;
+    const int cc = cok ? cc0 : 0;
+    EntryWord u[2];
+    u[0] = rpair ? entry_pair(arow + row * p.ld_ar + blk, 0, rok ? row_mode(row, blk) : 0,
+                              rok ? row_mode(row, blk + 1) : 0)
+                 : entry_half(arow + row * p.ld_ar + blk, 0, rok ? row_mode(row, blk) : 0);
+    u[1] = EntryWord{nullptr, 0, 0, 0};
+    if (colw)
+      u[1] = cpair ? entry_pair(acol + cc, 0, cok ? col_mode(cc) : 0, cok ? col_mode(cc + 1) : 0)
+                   : entry_half(acol + cc, 0, cok ? col_mode(cc) : 0);
+    const uintptr_t any = reinterpret_cast<uintptr_t>(arow);
+    uint32_t old[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      old[j] = *global_cdword(u[j].merge ? reinterpret_cast<uintptr_t>(u[j].w) : any);
+
+    assemble_rows_masked<T, RW>(p, rc, ml, d);
+    uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t m = group_max<LB>(chunk_absmax<T, kCol, kPre>(d[i], col));
+      if ((lane % LB) == 0) s_rmax[i0 + i][lane / LB] = m;
+      touched |= cut_mask<T, RW>(rc, i);
     }
-    atomic_max_entries<kPer>(ptr, v, act);
-  }
-  if (colw && kPairs && p.col_pair) {
-    const int cc0 = 2 * threadIdx.x;        // columns cc, cc + 1 within the tile (WC = 512)
-    const bool ok = cc0 < WC;               // threads past the tile's columns idle
-    const int cc = ok ? cc0 : 0;
-    const int ln = cc / E, q = (cc % E) / 2;  // lane and dword of s_col holding both
-    uint32_t m = 0, t = 0;
+    s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    s_touch[wave][lane] = touched;
+    __syncthreads();
+
+    // the column's (or pair's) maximum over the waves, and whether it has an element of the
+    // fragment in the band
+    const int ln = cc / E, e = cc % E;  // lane of s_col holding it, and its element there
+    uint32_t cm = 0, ct = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       const uint4 o = s_col[w][ln];
       const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-      m = pk_max_u16(m, ov[q]);
-      t |= s_touch[w][ln];
+      cm = cpair ? pk_max_u16(cm, ov[e / 2]) : umax(cm, col_entry<T>(ov, e));
+      ct |= s_touch[w][ln];
     }
-    int mode[2] = {0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t cg = c0 + cc + h;
-      // the block's first and last elements decide whether the piece holds it whole
-      const int64_t gf = r0 * p.cols + cg, gl = (r0 + nrows - 1) * p.cols + cg;
-      if (ok && cg < p.cols && ((t >> (2 * q + h)) & 1u)) mode[h] = (gf >= p.start && gl < p.end) ? 1 : 2;
+    u[0].v = rpair ? s_rmax[row][blk] | (s_rmax[row][blk + 1] << 16)
+                   : s_rmax[row][blk] << (((u[0].set | u[0].merge) & 2u) ? 16 : 0);
+    if (cpair) {
+      const uint32_t tm = (ct >> e) & 3u;  // e even: the pair's two columns
+      u[1].v = cm;
+      u[1].set &= tm;
+      u[1].merge &= tm;
+    } else {
+      const int h = ((u[1].set | u[1].merge) & 2u) ? 1 : 0;  // the half holding the entry
+      const uint32_t tm = ((ct >> e) & 1u) << h;
+      u[1].v = cm << (16 * h);
+      u[1].set &= tm;
+      u[1].merge &= tm;
     }
-    if (mode[0] | mode[1])
-      update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_col) + band * p.ld_ac +
-                                                    c0 + cc),
-                        m, mode[0], mode[1]);
-  } else if (colw) {
-    constexpr int kPer = WC >= kT ? WC / kT : 1;  // columns per thread (2 or 1 with 256 threads)
-    T* ptr[kPer];
-    uint32_t v[kPer], act = 0;
+    if (p.amax_own)
+      store_entry_words(u, old);
+    else
+      apply_entry_words(u, old);
+  } else {
+    // Edge tile: a fragment boundary, the short last band or a row's short last block cuts it.
+    // Every wave loads its rows masked to the fragment; the row-wise and column-wise maxima meet
+    // in LDS and all threads then write the touched entries, at most two of each kind per
+    // thread: blocks the piece holds whole are stored, blocks a fragment boundary cuts are
+    // merged atomically (all reads, then all swaps).
+    const RowClass<RW> rc = classify_rows<T, RW>(p, r0 + i0, nrows - i0, c, cvalid);
+    const uint32_t(&em)[RW] = rc.em;
+    load_rows_masked<T, RW>(p, src, r0 + i0, c, rc, d);
+    uint32_t touched = 0;  // bit e: column c + e has an element of the fragment in these rows
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int cc0 = threadIdx.x + j * kT;  // column within the tile
-      const bool ok = cc0 < WC;              // threads past the tile's columns idle
+    for (int i = 0; i < RW; ++i) {
+      const uint32_t m = group_max<LB>(chunk_absmax<T, kCol, kPre>(d[i], col));
+      if ((lane % LB) == 0) s_rmax[i0 + i][lane / LB] = m;
+      touched |= em[i];
+    }
+    s_col[wave][lane] = make_uint4(col[0], col[1], col[2], col[3]);
+    s_touch[wave][lane] = touched;
+    __syncthreads();
+    // BF16 entries whose rows start on 4-byte boundaries: one thread per aligned word of two
+    // entries (row-wise: blocks 2k, 2k + 1 of a row; column-wise: columns 2t, 2t + 1)
+    constexpr bool kPairs = sizeof(T) == 2;
+    if (kPairs && p.row_pair && threadIdx.x < kBlockLen * (NBLK / 2)) {
+      constexpr int PR = NBLK / 2;  // word pairs per row of the tile (8)
+      const int row = threadIdx.x / PR, k2 = 2 * (threadIdx.x % PR);
+      const int64_t r = r0 + row;
+      int mode[2] = {0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t bc = c0 + (k2 + h) * kBlockLen;  // the block's first column
+        const int64_t gb = r * p.cols + bc;
+        const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
+        if (row < nrows && bc < p.cols && gb < p.end && ge > p.start)
+          mode[h] = (gb >= p.start && ge <= p.end) ? 1 : 2;
+      }
+      if (mode[0] | mode[1])
+        update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_row) + r * p.ld_ar +
+                                                      (c0 >> 5) + k2),
+                          s_rmax[row][k2] | (s_rmax[row][k2 + 1] << 16), mode[0], mode[1]);
+    } else {
+      // row entries per thread (2 or 1 with 256 threads; threads past the tile's entries idle)
+      constexpr int kPer = kBlockLen * NBLK >= kT ? kBlockLen * NBLK / kT : 1;
+      T* ptr[kPer];
+      uint32_t v[kPer], act = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int e0 = threadIdx.x + j * kT;
+        const bool ok = e0 < kBlockLen * NBLK;
+        const int e = ok ? e0 : 0;
+        const int row = e / NBLK, blk = e % NBLK;
+        const int64_t r = r0 + row;
+        const int64_t bc = c0 + blk * kBlockLen;  // the block's first column
+        const int64_t gb = r * p.cols + bc;
+        const int64_t ge = r * p.cols + min<int64_t>(bc + kBlockLen, p.cols);  // one past its last
+        ptr[j] = static_cast<T*>(p.amax_row) + r * p.ld_ar + (c0 >> 5) + blk;
+        v[j] = s_rmax[row][blk];
+        if (ok && row < nrows && bc < p.cols && gb < p.end && ge > p.start) {
+          if (gb >= p.start && ge <= p.end)
+            *ptr[j] = (T)v[j];  // whole block: this tile is its only writer
+          else
+            act |= 1u << j;
+        }
+      }
+      atomic_max_entries<kPer>(ptr, v, act);
+    }
+    if (colw && kPairs && p.col_pair) {
+      const int cc0 = 2 * threadIdx.x;        // columns cc, cc + 1 within the tile (WC = 512)
+      const bool ok = cc0 < WC;               // threads past the tile's columns idle
       const int cc = ok ? cc0 : 0;
-      const int ln = cc / E, e = cc % E;
+      const int ln = cc / E, q = (cc % E) / 2;  // lane and dword of s_col holding both
       uint32_t m = 0, t = 0;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const uint4 o = s_col[w][ln];
         const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
-        m = umax(m, col_entry<T>(ov, e));
+        m = pk_max_u16(m, ov[q]);
         t |= s_touch[w][ln];
       }
-      ptr[j] = static_cast<T*>(p.amax_col) + band * p.ld_ac + c0 + cc;
-      v[j] = m;
-      // the block's first and last elements decide whether the piece holds it whole
-      const int64_t gf = r0 * p.cols + c0 + cc, gl = (r0 + nrows - 1) * p.cols + c0 + cc;
-      if (ok && c0 + cc < p.cols && ((t >> e) & 1u)) {
-        if (gf >= p.start && gl < p.end)
-          *ptr[j] = (T)m;
-        else
-          act |= 1u << j;
+      int mode[2] = {0, 0};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t cg = c0 + cc + h;
+        // the block's first and last elements decide whether the piece holds it whole
+        const int64_t gf = r0 * p.cols + cg, gl = (r0 + nrows - 1) * p.cols + cg;
+        if (ok && cg < p.cols && ((t >> (2 * q + h)) & 1u)) mode[h] = (gf >= p.start && gl < p.end) ? 1 : 2;
       }
+      if (mode[0] | mode[1])
+        update_entry_pair(reinterpret_cast<uint32_t*>(static_cast<T*>(p.amax_col) + band * p.ld_ac +
+                                                      c0 + cc),
+                          m, mode[0], mode[1]);
+    } else if (colw) {
+      constexpr int kPer = WC >= kT ? WC / kT : 1;  // columns per thread (2 or 1 with 256 threads)
+      T* ptr[kPer];
+      uint32_t v[kPer], act = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int cc0 = threadIdx.x + j * kT;  // column within the tile
+        const bool ok = cc0 < WC;              // threads past the tile's columns idle
+        const int cc = ok ? cc0 : 0;
+        const int ln = cc / E, e = cc % E;
+        uint32_t m = 0, t = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const uint4 o = s_col[w][ln];
+          const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+          m = umax(m, col_entry<T>(ov, e));
+          t |= s_touch[w][ln];
+        }
+        ptr[j] = static_cast<T*>(p.amax_col) + band * p.ld_ac + c0 + cc;
+        v[j] = m;
+        // the block's first and last elements decide whether the piece holds it whole
+        const int64_t gf = r0 * p.cols + c0 + cc, gl = (r0 + nrows - 1) * p.cols + c0 + cc;
+        if (ok && c0 + cc < p.cols && ((t >> e) & 1u)) {
+          if (gf >= p.start && gl < p.end)
+            *ptr[j] = (T)m;
+          else
+            act |= 1u << j;
+        }
+      }
+      atomic_max_entries<kPer>(ptr, v, act);
     }
-    atomic_max_entries<kPer>(ptr, v, act);
   }
 }
 
@@ -2397,13 +2714,28 @@ inline bool one_launch_for_both(const Buckets& bk, int bf16, int pre) {
   return tiles < kSmallLaunchTiles;
 }
 
+// The pieces of one amax launch (or of launches that may run in any order), each with its
+// amax_own flag: set where no other of them has the same row-wise or column-wise amax array
+// (pieces of one call share amax arrays only as the same pointer in the same role).
+inline std::vector<TileArgs> mark_amax_owners(std::vector<TileArgs> v) {
+  std::unordered_map<const void*, int> uses;
+  for (const TileArgs& t : v) {
+    if (t.amax_row) ++uses[t.amax_row];
+    if (t.amax_col) ++uses[t.amax_col];
+  }
+  for (TileArgs& t : v)
+    t.amax_own = (!t.amax_row || uses[t.amax_row] == 1) && (!t.amax_col || uses[t.amax_col] == 1);
+  return v;
+}
+
 template <typename T, bool kCol, bool kPre>
 hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vector<TileArgs>& elem,
                               hipStream_t s) {
   hipError_t e = hipSuccess;
   if (!vec.empty())
     e = launch_grouped(amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmax>,
-                       amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, vec, 1,
+                       amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>,
+                       mark_amax_owners(vec), 1,
                        Occupancy<T>::kAmaxCap, s,
                        {amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8>,
                         kAmax8Tiles, 1, kWaveSize * 8});
@@ -2511,7 +2843,7 @@ hipError_t launch_cast_pieces(const Piece* ps, int n, hipStream_t s) {
 template <typename T, bool kPre>
 hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
   const int bf16 = sizeof(T) == 2, pre = kPre;
-  const std::vector<TileArgs> v = both_directions(bk, bf16, pre);
+  const std::vector<TileArgs> v = mark_amax_owners(both_directions(bk, bf16, pre));
   hipError_t e = hipSuccess;
   if (!v.empty())
     e = launch_grouped(amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmax, true>,

@@ -74,19 +74,20 @@ def test_a_call_of_two_kernels_is_timed_from_first_start_to_last_end():
     n = m.rows * m.cols
     frags = [(0, n // 2), (n // 2, n // 2)]
     want, x, outs, pieces = _cast_pieces(m, frags, [True, False])
-    singles = []
-    for p in pieces:  # each launch alone, timed, after a warm-up call
-        B.mxfp8_partial_cast([p])
-        k0, k1 = TimingEvent(), TimingEvent()
-        B.mxfp8_time_next_call(k0.ev.value, k1.ev.value)
-        B.mxfp8_partial_cast([p])
-        torch.cuda.synchronize()
-        singles.append(k0.elapsed_time(k1))
-    k0, k1 = TimingEvent(), TimingEvent()
-    B.mxfp8_time_next_call(k0.ev.value, k1.ev.value)
-    B.mxfp8_partial_cast(pieces)
-    torch.cuda.synchronize()
-    both = k0.elapsed_time(k1)
+    def timed(ps):  # the fastest of three timed calls, after a warm-up call
+        B.mxfp8_partial_cast(ps)
+        best = None
+        for _ in range(3):
+            k0, k1 = TimingEvent(), TimingEvent()
+            B.mxfp8_time_next_call(k0.ev.value, k1.ev.value)
+            B.mxfp8_partial_cast(ps)
+            torch.cuda.synchronize()
+            ms = k0.elapsed_time(k1)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    singles = [timed([p]) for p in pieces]  # each launch alone
+    both = timed(pieces)
     assert both > max(singles) and both >= 0.8 * sum(singles), (both, singles)
     for (s, l, dr, dc) in outs:
         assert np.array_equal(to_np(dr), want["data_row"][s:s + l])

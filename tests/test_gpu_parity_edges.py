@@ -287,6 +287,43 @@ def test_amax_sets_whole_blocks_and_merges_cut_blocks(dtype, inputs, cols, frag)
     assert (bits(war) != bits(init)).any() and (bits(wac) != bits(initc)).any()
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("frags", [
+    [(1000, 6000)],                                   # one piece: it owns the amax arrays
+    [(1000, 3001), (4001, 2999)],                     # two pieces in one call sharing them
+    [(17, 128 * 96 // 4)],                            # a quarter at offset 17
+])
+def test_amax_merges_with_entries_on_any_alignment(dtype, offset, frags):
+    """Entries start at random values; the amax arrays start `offset` entries into their
+    allocations (BF16 at offset 1: rows of both arrays off 4-byte boundaries, so entries are
+    updated one by one rather than in aligned pairs).  Pieces alone in a call and pieces
+    sharing the arrays in one call must both give the oracle's entries."""
+    rows, cols = 96, 128
+    x = wl.random_matrix(rows, cols, dtype, seed=31, kind="normal")
+    nb = B.nblocks(cols)
+    g = np.random.Generator(np.random.PCG64(2))
+    init = np.abs(g.standard_normal(rows * nb + offset) * 1.5).astype(np.float32)
+    initc = np.abs(g.standard_normal(3 * cols + offset) * 1.5).astype(np.float32)
+    if dtype == "bf16":
+        init, initc = wl.to_dtype(init, "bf16"), wl.to_dtype(initc, "bf16")
+    ard, acd = to_dev(init), to_dev(initc)
+    ar = ard[offset:].view(rows, nb)
+    ac = acd[offset:].view(3, cols)
+    xd = to_dev(x)
+    pieces = [B.make_piece(rows, cols, s, xd[s:s + l], amax_row=ar, amax_col=ac) for s, l in frags]
+    B.mxfp8_partial_amax(pieces)
+    torch.cuda.synchronize()
+    war = init[offset:].reshape(rows, nb).copy()
+    wac = initc[offset:].reshape(3, cols).copy()
+    for s, l in frags:
+        oracle.partial_amax(x[s:s + l], rows, cols, s, war, wac)
+    assert not first_mismatch(bits(to_np(ar)), bits(war))
+    assert not first_mismatch(bits(to_np(ac)), bits(wac))
+    assert (bits(to_np(ard)[:offset]) == bits(init[:offset])).all()
+    assert (bits(war) != bits(init[offset:].reshape(rows, nb))).any()
+
+
 def test_scales_for_every_nonnegative_bf16_amax():
     codes = np.arange(0, 0x7F80, dtype=np.uint16)  # +0 .. largest finite, subnormals included
     codes = np.concatenate([codes, np.zeros((-codes.size) % 64, np.uint16)])
