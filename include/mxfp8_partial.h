@@ -102,7 +102,10 @@ typedef struct {
  *  - blocks the fragment does not touch keep their entry.
  * So pieces of one weight whose fragments do not overlap may share amax buffers within a
  * call or across calls, and a zero-filled buffer accumulates the amax of all pieces (on it
- * the result is max(entry, m) for every touched block).  The column-wise direction is
+ * the result is max(entry, m) for every touched block).  Calls that share an amax buffer must
+ * be ordered (one stream, or streams synchronized with each other): a piece that no other
+ * piece of its call shares amax buffers with may merge by a read and a write rather than an
+ * atomic.  The column-wise direction is
  * computed iff amax_col.ptr != NULL.  Reads: rows, cols, start, len, in_dtype,
  * preround_bf16, input, amax_row (required), amax_col. */
 int mxfp8_partial_amax(const mxfp8_piece* pieces, int n, void* hip_stream);
