@@ -1141,8 +1141,9 @@ def layer_batch(args, dev, L=None):
                             "frac_of_peak": round(stage_bytes[nm] / (stage_us[nm] * 1e-6) / 1e9
                                                   / HBM_PEAK_GBS, 4)}
                        for nm in names},
-            "launches": {"amax": plans[0].n_amax, "cast": plans[0].n_cast},
-            "note": "stage times from a pass with a marker before every stage"}
+            "pieces": {"amax": plans[0].n_amax, "cast": plans[0].n_cast},
+            "note": "stage times from a pass with a marker before every stage; launches per "
+                    "call: the kernel trace summary"}
         del plans
         torch.cuda.empty_cache()
 
@@ -1151,8 +1152,6 @@ def layer_batch(args, dev, L=None):
     fs, fl = frags[f]
     rank = {"fragment": [fs, fl], "pieces": [[i, st, n] for (i, st, n, _) in
                                               W.split_fragment(specs, fs, fl)]}
-    # one launch per kernel specialization: the bidirectional pieces and the row-only ones
-    n_launch = len({specs[i].colwise for (i, _, _, _) in W.split_fragment(specs, fs, fl)})
     per_set = fl * 2 * 2 + 2 * packed * 3
     n_sets = max(2, min(10, int(np.ceil(args.min_footprint_gb * 1e9 / per_set))))
     for name, fo in (("in_place", False), ("fragment_outputs", True)):
@@ -1178,7 +1177,7 @@ def layer_batch(args, dev, L=None):
                                        "GBps": round(nb / (us * 1e-6) / 1e9, 1),
                                        "frac_of_peak": round(nb / (us * 1e-6) / 1e9
                                                              / HBM_PEAK_GBS, 4),
-                                       "launches": n_launch, "buffer_sets": n_sets}
+                                       "pieces": len(rank["pieces"]), "buffer_sets": n_sets}
         del plans
         torch.cuda.empty_cache()
     res["rank_fragment"] = rank
