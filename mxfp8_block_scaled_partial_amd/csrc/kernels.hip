@@ -977,9 +977,10 @@ __device__ __forceinline__ void fold_col(uint32_t (&col)[4], const uint4& o) {
 // kGuard (with kCol = true; the ablation library, and small calls holding both directions):
 // one kernel for both kinds of piece, its column-wise work selected at run time by the
 // column-wise pointer.  kWaves: the workgroup's waves, each taking 32 / kWaves rows of the
-// band (8 waves of 4 rows for launches too small to fill the GPU).
+// band (8 waves of 4 rows for launches too small to fill the GPU).  kOne: a launch of a single
+// piece (Tier::one), whose piece index is 0.
 template <typename T, bool kCol, bool kPre, int kOcc, bool kGuard = false,
-          int kWaves = kWavesPerGroup>
+          int kWaves = kWavesPerGroup, bool kOne = false>
 __global__ __launch_bounds__(kWaveSize * kWaves)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -995,9 +996,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void amax_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  pin_header(ga);
+  if constexpr (!kOne) pin_header(ga);
   const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
-  const int k = piece_of(ga, lt);
+  const int k = kOne ? 0 : piece_of(ga, lt);  // a launch of one piece: piece 0
   const TileArgs& p = ga.piece[k];
   pin_tile_fields(ga, k);
   const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
@@ -1674,12 +1675,12 @@ __device__ __forceinline__ void cast_tile_general(
 // Same tiling as the amax: a workgroup per (band, 64*E columns), wave w casts rows 8w..8w+7
 // with all loads in flight.  kGuard as for the amax (not fused): the column-wise work
 // follows a run-time test of data_col.  kScaleFirst (not fused): the common tile loads its
-// scale bytes before its input rows (see there).  kSplit (not fused; launches too small to
-// fill the GPU): a workgroup takes 32 / kSplit rows of a band, wave w rows
-// (8 / kSplit) w ... , so each wave's serial work, an edge tile's above all, is kSplit times
-// shorter; tile t of a piece is then (sub-band t / ntc, column tile t % ntc).
+// scale bytes before its input rows (see there).  kSplit (launches too small to fill the
+// GPU): a workgroup takes 32 / kSplit rows of a band, wave w rows (8 / kSplit) w ... , so each
+// wave's serial work, an edge tile's above all, is kSplit times shorter; tile t of a piece is
+// then (sub-band t / ntc, column tile t % ntc).  kOne as for the amax.
 template <typename T, bool kCol, bool kPre, bool kFuse, int kOcc, bool kGuard = false,
-          bool kScaleFirst = false, int kSplit = 1>
+          bool kScaleFirst = false, int kSplit = 1, bool kOne = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -1690,9 +1691,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_vec_kernel(GroupArgs ga) {
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  pin_header(ga);
+  if constexpr (!kOne) pin_header(ga);
   const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
-  const int k = piece_of(ga, lt);
+  const int k = kOne ? 0 : piece_of(ga, lt);  // a launch of one piece: piece 0
   const TileArgs& p = ga.piece[k];
   pin_cast_fields(ga, k);
   const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
@@ -2017,8 +2018,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void cast_lines_kernel(GroupArgs ga) 
 // amax are final without any combine: one pass reads each tile once, keeps it in registers,
 // reduces the row-wise blocks with DPP and the column-wise blocks over the four waves in LDS,
 // and writes the amax (when requested), the E8M0 scales and the E4M3 data.  All loads are
-// issued before the first store.
-template <typename T, bool kCol, bool kPre, int kOcc, int kWaves = kWavesPerGroup>
+// issued before the first store.  kWaves and kOne as for the amax.
+template <typename T, bool kCol, bool kPre, int kOcc, int kWaves = kWavesPerGroup,
+          bool kOne = false>
 __global__ __launch_bounds__(kWaveSize * kWaves)
 __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga) {
   constexpr int E = Chunk<T>::E;
@@ -2029,9 +2031,9 @@ __attribute__((amdgpu_waves_per_eu(kOcc))) void quantize_vec_kernel(GroupArgs ga
 
   const int lane = threadIdx.x & (kWaveSize - 1);
   const int wave = threadIdx.x >> 6;
-  pin_header(ga);
+  if constexpr (!kOne) pin_header(ga);
   const uint32_t lt = xcd_remap(blockIdx.x, gridDim.x);  // tile of the launch
-  const int k = piece_of(ga, lt);
+  const int k = kOne ? 0 : piece_of(ga, lt);  // a launch of one piece: piece 0
   const TileArgs& p = ga.piece[k];
   pin_tile_fields(ga, k);
   const int64_t tile = (int64_t)(lt - ga.first[k]) + p.tile0;
@@ -2629,13 +2631,17 @@ hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t shm, hipStream_
 }
 
 // A kernel for launches of fewer than `below` tiles: it takes each tile as `split` workgroups
-// of `threads` threads (the cast's split tiles, the amax's wide workgroups).
+// of `threads` threads (the cast's split tiles, the amax's wide workgroups).  `one` is the same
+// kernel for a launch of a single piece (kOne): its piece index is known, so the workgroup
+// loads the launch header and the piece's fields in one batch of scalar loads, one round trip
+// where the piece lookup takes two (graph replays, 1024x1024 calls: 3-7% faster).
 template <typename K>
 struct Tier {
   K kernel = nullptr;
   int64_t below = 0;
   int split = 1;
   int threads = kThreads;
+  K one = nullptr;
 };
 
 template <typename K>
@@ -2664,7 +2670,8 @@ hipError_t launch_grouped(K kernel, K small_kernel, const std::vector<TileArgs>&
     }
     const int64_t groups = cdiv(total, tiles_per_wg);
     const bool small = total < kSmallLaunchTiles;
-    const K k = tier.kernel != nullptr ? tier.kernel : small ? small_kernel : kernel;
+    const K tk = g.n == 1 && tier.one != nullptr ? tier.one : tier.kernel;
+    const K k = tk != nullptr ? tk : small ? small_kernel : kernel;
     const size_t shm = small ? 0 : cap_lds(k, cap);
     for (int64_t g0 = 0; g0 < groups; g0 += kMaxLaunchGroups) {
       // the pieces' first tiles counted from this launch's first workgroup (see GroupArgs)
@@ -2738,7 +2745,8 @@ hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vecto
                        mark_amax_owners(vec), 1,
                        Occupancy<T>::kAmaxCap, s,
                        {amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8>,
-                        kAmax8Tiles, 1, kWaveSize * 8});
+                        kAmax8Tiles, 1, kWaveSize * 8,
+                        amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8, true>});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, amax_elem_kernel<T, kCol, kPre>, elem,
                        kWavesPerGroup, 0, s);
@@ -2758,9 +2766,13 @@ hipError_t launch_cast_bucket(const std::vector<TileArgs>& vec, const std::vecto
                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast>, vec, 1,
                        Occupancy<T>::cast_cap(kCol, kFuse), s,
                        {cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 8>,
-                        kSplit8Tiles, 8},
+                        kSplit8Tiles, 8, kThreads,
+                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 8,
+                                        true>},
                        {cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 4>,
-                        kSplit4Tiles, 4});
+                        kSplit4Tiles, 4, kThreads,
+                        cast_vec_kernel<T, kCol, kPre, kFuse, Occupancy<T>::kCast, false, false, 4,
+                                        true>});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(cast_elem_kernel<T, kCol, kPre, kFuse>, cast_elem_kernel<T, kCol, kPre, kFuse>,
                        elem, kWavesPerGroup, 0, s);
@@ -2785,8 +2797,10 @@ hipError_t launch_cast_guarded(const Buckets& bk, hipStream_t s) {
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, sizeof(T) == 2>,
         cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true>, v, 1,
         Occupancy<T>::cast_cap(true, false), s,
-        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8>, kSplit8Tiles, 8},
-        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4>, kSplit4Tiles, 4});
+        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8>, kSplit8Tiles, 8,
+         kThreads, cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 8, true>},
+        {cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4>, kSplit4Tiles, 4,
+         kThreads, cast_vec_kernel<T, true, kPre, false, Occupancy<T>::kCast, true, false, 4, true>});
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_cast_bucket<T, true, kPre, false>(none, bk.b[bf16][1][pre][0], s);
   if (e == hipSuccess) e = launch_cast_bucket<T, false, kPre, false>(none, bk.b[bf16][0][pre][0], s);
@@ -2850,7 +2864,8 @@ hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true>, v, 1,
                        Occupancy<T>::kAmaxCap, s,
                        {amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8>,
-                        kAmax8Tiles, 1, kWaveSize * 8});
+                        kAmax8Tiles, 1, kWaveSize * 8,
+                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8, true>});
   // the element-wise kernels keep their compile-time specializations
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_amax_bucket<T, true, kPre>(none, bk.b[bf16][1][pre][0], s);
@@ -2898,7 +2913,8 @@ hipError_t launch_quantize_bucket(const std::vector<TileArgs>& vec,
                        Occupancy<T>::kQuantCap, s,
                        // launches too small to fill the GPU: 8-wave workgroups, as the amax's
                        {quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, 8>,
-                        kAmax8Tiles, 1, kWaveSize * 8});
+                        kAmax8Tiles, 1, kWaveSize * 8,
+                        quantize_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, 8, true>});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(quantize_elem_kernel<T, kCol, kPre>, quantize_elem_kernel<T, kCol, kPre>,
                        elem, kWavesPerGroup, 0, s);
