@@ -2746,7 +2746,11 @@ hipError_t launch_amax_bucket(const std::vector<TileArgs>& vec, const std::vecto
                        Occupancy<T>::kAmaxCap, s,
                        {amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8>,
                         kAmax8Tiles, 1, kWaveSize * 8,
-                        amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8, true>});
+                        amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false, 8, true>},
+                       {amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall>, kSmallLaunchTiles,
+                        1, kThreads,
+                        amax_vec_kernel<T, kCol, kPre, Occupancy<T>::kAmaxSmall, false,
+                                        kWavesPerGroup, true>});
   if (e == hipSuccess && !elem.empty())
     e = launch_grouped(amax_elem_kernel<T, kCol, kPre>, amax_elem_kernel<T, kCol, kPre>, elem,
                        kWavesPerGroup, 0, s);
@@ -2865,7 +2869,11 @@ hipError_t launch_amax_guarded(const Buckets& bk, hipStream_t s) {
                        Occupancy<T>::kAmaxCap, s,
                        {amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8>,
                         kAmax8Tiles, 1, kWaveSize * 8,
-                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8, true>});
+                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true, 8, true>},
+                       {amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true>,
+                        kSmallLaunchTiles, 1, kThreads,
+                        amax_vec_kernel<T, true, kPre, Occupancy<T>::kAmaxSmall, true,
+                                        kWavesPerGroup, true>});
   // the element-wise kernels keep their compile-time specializations
   const std::vector<TileArgs> none;
   if (e == hipSuccess) e = launch_amax_bucket<T, true, kPre>(none, bk.b[bf16][1][pre][0], s);
